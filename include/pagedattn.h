@@ -1,0 +1,156 @@
+/*
+ * libpagedattn — paged decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Every pointer argument that names
+ * tensor data is DEVICE memory owned by the caller; the library allocates
+ * nothing, keeps no state between calls and holds no handle.  All work is
+ * enqueued asynchronously on the given stream (a hipStream_t passed as void*;
+ * NULL means the default stream).
+ *
+ * The method (sources cited by page title and section):
+ *   - the KV cache is cut into fixed-size blocks of 16 or 32 tokens that live
+ *     anywhere in a physical pool; a per-sequence block table maps logical
+ *     block j to its physical block (vLLM tutorial page "3. PagedAttention原理",
+ *     §3.2 and §3.3.1; page "PagedAttentionMetal：基于Metal 3的Apple Silicon原生
+ *     LLM推理加速方案", sections 分页KV缓存机制 and 块表管理);
+ *   - decode attention fetches K/V through the table and otherwise computes
+ *     ordinary softmax attention; sequences of different lengths share one
+ *     batch without padding (PagedAttentionMetal, section 注意力计算优化;
+ *     "PagedAttention MLX：为Apple Silicon打造的高吞吐量LLM推理引擎", architecture
+ *     list; PagedAttention原理, closing remarks of §3.4);
+ *   - a new token is written into the next row of its sequence's last block
+ *     (PagedAttention原理 §3.3.2);
+ *   - shared blocks are copied before a private write: copy-on-write
+ *     ("mlx-paged-attention: Bringing vLLM-level High Throughput Inference to
+ *     Apple Silicon", core feature 2; PagedAttention原理 §3.3.3).
+ *
+ * Layouts (row-major, dense, part of the ABI):
+ *   q, out            [num_seqs][num_heads][head_dim]
+ *   k_pool, v_pool    [num_blocks][num_heads][block_size][head_dim]  (two arrays)
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens      int32 [num_seqs]
+ *   slot_mapping      int32 [num_tokens]; slot = physical_block*block_size + row
+ *   block_mapping     int32 [num_pairs][2] = {src, dst}
+ * One element dtype covers q, k_pool, v_pool, out, k_new and v_new.  Keys and
+ * values have as many heads as queries.  head_dim is 64 or 128; block_size is
+ * 16 or 32.  Every tensor pointer must be 16-byte aligned.
+ *
+ * Errors: arguments are validated on the host before anything is launched; a
+ * failed check returns a status and enqueues nothing.  A launch failure returns
+ * PA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ * synchronisation.  Entries the host cannot check (table ids, slots, copy pairs)
+ * are bounds-checked in the kernels: see each call.
+ */
+#ifndef PAGEDATTN_H_
+#define PAGEDATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype {
+  PA_DTYPE_F32 = 0,
+  PA_DTYPE_F16 = 1,
+  PA_DTYPE_BF16 = 2
+} pa_dtype_t;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, misaligned pointer, bad size, bad scale */
+  PA_ERR_UNSUPPORTED = 2, /* head_dim, block_size or dtype outside what is built */
+  PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pa_decode_workspace_size() */
+  PA_ERR_HIP = 4          /* the HIP runtime refused the launch */
+} pa_status_t;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int32_t pa_abi_version(void);
+
+/* Human-readable name of a status (static storage; never NULL). */
+const char* pa_status_string(pa_status_t status);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes (0 when every
+ * sequence fits in one partition, i.e. max_blocks_per_seq*block_size <=
+ * partition tokens).  partition_size 0 selects the library default (512
+ * tokens).  Returns 0 for sizes pa_decode would reject.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, int32_t block_size,
+                                int32_t partition_size);
+
+/*
+ * Decode attention over a paged KV cache: for every sequence s and head h,
+ *   out[s][h][:] = sum_t softmax_t(scale * <q[s][h], K_t>) * V_t,  t < L_s,
+ * where K_t, V_t are row t % block_size of physical block
+ * block_tables[s][t / block_size] (head h) and L_s = context_lens[s].
+ * Sources: PagedAttentionMetal, section 注意力计算优化; PagedAttention原理 §3.2
+ * and the closing remarks of §3.4.
+ *
+ * Long contexts are split into partitions of partition_size tokens (0 = 512;
+ * otherwise a positive multiple of block_size); each partition's softmax
+ * partials (max, sum, weighted values) go to `workspace` and a log-sum-exp
+ * merge combines them (the split-context decode the "PagedAttention MLX" page
+ * names as its "Flash-Dec" roadmap milestone).  Within rounding the result
+ * does not depend on partition_size.
+ *
+ * Arithmetic: inputs are converted to fp32, dot products, softmax and the
+ * weighted sum accumulate in fp32, and out is rounded to nearest-even once.
+ *
+ * Semantics of edge cases:
+ *   - L_s == 0 writes a zero row; L_s is clamped to [0, max_blocks_per_seq*block_size];
+ *   - table entries at or past ceil(L_s/block_size) and rows at or past L_s in
+ *     the last block are never read (may hold anything, NaN included);
+ *   - a referenced table entry outside [0, num_blocks) is not dereferenced:
+ *     that (sequence, head) row of out becomes NaN.
+ * Preconditions: out aliases no input; workspace is not shared by concurrent
+ * calls.  num_seqs == 0 returns PA_OK and launches nothing.
+ * Limits: num_seqs <= 65535, num_heads <= 65535, partitions per sequence <= 65535.
+ */
+pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      float scale, int32_t block_size,
+                      int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                      int32_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t partition_size, pa_dtype_t dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Write each new token's K and V (all heads) into its cache slot:
+ *   k_pool[slot / block_size][h][slot % block_size][:] = k_new[i][h][:]
+ * and likewise for v, for i < num_tokens with slot = slot_mapping[i].
+ * Bit-exact byte copy.  Source: PagedAttention原理 §3.3.2 (append into the last
+ * block, or row 0 of a fresh one).
+ * k_new, v_new: [num_tokens][num_heads][head_dim].  A negative slot, or one
+ * >= num_blocks*block_size, writes nothing.  Slots must be distinct (two
+ * writes to one slot race).  num_tokens == 0 returns PA_OK.
+ */
+pa_status_t pa_reshape_and_cache(void* k_pool, void* v_pool,
+                                 const void* k_new, const void* v_new,
+                                 const int32_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, pa_dtype_t dtype, void* stream);
+
+/*
+ * Copy whole physical blocks (every head and row) in both pools:
+ *   k_pool[dst] = k_pool[src], v_pool[dst] = v_pool[src]
+ * for each {src, dst} pair of block_mapping.  Bit-exact.  This is the copy step
+ * of copy-on-write for shared, reference-counted blocks (mlx-paged-attention,
+ * core feature 2; PagedAttentionMetal, section 块表管理; PagedAttention原理
+ * §3.3.3).  Pairs with an id outside [0, num_blocks) are skipped.
+ * Preconditions: destinations are distinct and no destination is also a
+ * source (otherwise the result depends on scheduling).  num_pairs == 0
+ * returns PA_OK.
+ */
+pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping,
+                           int32_t num_pairs, int32_t num_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, pa_dtype_t dtype,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H_ */

@@ -1,0 +1,19 @@
+"""libpagedattn: paged decode attention for AMD MI355X (gfx950).
+
+The compute path is the C-ABI shared library ``libpagedattn.so`` (hand-written
+HIP kernels, declared in ``include/pagedattn.h``); ``binding`` wraps it for
+torch tensors.  ``block_manager`` holds the host-side allocator (free list,
+block tables, reference counts, copy-on-write plans) and ``workloads`` the
+seeded synthetic inputs.
+"""
+
+from .binding import (  # noqa: F401
+    PagedAttnError,
+    load_library,
+    pa_copy_blocks,
+    pa_decode,
+    pa_decode_workspace_size,
+    pa_reshape_and_cache,
+    status_string,
+)
+from .block_manager import BlockManager  # noqa: F401

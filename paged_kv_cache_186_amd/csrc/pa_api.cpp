@@ -1,0 +1,199 @@
+// C ABI of libpagedattn: argument validation, sizing and dispatch.
+//
+// Every check here runs on the host before anything is enqueued; a failed
+// check returns a status and launches nothing.  No allocation, no state.
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+int elem_bytes(pa_dtype_t dtype) {
+  switch (dtype) {
+    case PA_DTYPE_F32:
+      return 4;
+    case PA_DTYPE_F16:
+    case PA_DTYPE_BF16:
+      return 2;
+    default:
+      return 0;
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_shape(int head_dim, int block_size) {
+  return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
+}
+
+// Blocks per partition, or 0 when partition_size is not a positive multiple of
+// block_size (0 selects the default).
+int partition_blocks(int partition_size, int block_size) {
+  if (partition_size == 0) partition_size = pa::kDefaultPartitionTokens;
+  if (partition_size < 0 || partition_size % block_size != 0) return 0;
+  return partition_size / block_size;
+}
+
+struct DecodePlan {
+  pa_status_t status;
+  int part_blocks;
+  int max_parts;
+  pa::WorkspaceLayout ws;
+};
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                       int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
+  DecodePlan p{PA_OK, 0, 0, {0, 0, 0}};
+  if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  if (!supported_shape(head_dim, block_size)) {
+    p.status = PA_ERR_UNSUPPORTED;
+    return p;
+  }
+  if (num_seqs > pa::kMaxGridYZ || num_heads > pa::kMaxGridYZ ||
+      max_blocks_per_seq > INT_MAX / block_size) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  p.part_blocks = partition_blocks(partition_size, block_size);
+  if (p.part_blocks == 0) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  p.max_parts = (max_blocks_per_seq + p.part_blocks - 1) / p.part_blocks;
+  if (p.max_parts > pa::kMaxGridYZ) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  p.ws = pa::workspace_layout(num_seqs, num_heads, head_dim, p.max_parts);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return kAbiVersion; }
+
+const char* pa_status_string(pa_status_t status) {
+  switch (status) {
+    case PA_OK:
+      return "PA_OK";
+    case PA_ERR_INVALID_ARG:
+      return "PA_ERR_INVALID_ARG: null or misaligned pointer, or a size out of range";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: head_dim must be 64 or 128, block_size 16 or 32, dtype f32/f16/bf16";
+    case PA_ERR_WORKSPACE:
+      return "PA_ERR_WORKSPACE: workspace missing or smaller than pa_decode_workspace_size()";
+    case PA_ERR_HIP:
+      return "PA_ERR_HIP: the HIP runtime rejected a kernel launch";
+    default:
+      return "unknown pa_status_t";
+  }
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, int32_t block_size,
+                                int32_t partition_size) {
+  const DecodePlan p =
+      plan_decode(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size);
+  return p.status == PA_OK ? p.ws.total : 0;
+}
+
+pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t partition_size,
+                      pa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  const DecodePlan plan =
+      plan_decode(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size);
+  if (plan.status != PA_OK) return plan.status;
+  if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  if (plan.ws.total > 0) {
+    if (!workspace || workspace_bytes < plan.ws.total) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+  }
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.block_size = block_size;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.partition_blocks = plan.part_blocks;
+  a.max_partitions = plan.max_parts;
+  a.dtype = dtype;
+  if (plan.ws.total > 0) {
+    char* ws = static_cast<char*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
+    a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
+  }
+  const hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status_t pa_reshape_and_cache(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                                 const int32_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, pa_dtype_t dtype, void* stream) {
+  const int e = elem_bytes(dtype);
+  if (e == 0 || !supported_shape(head_dim, block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (num_heads > INT_MAX / (head_dim * e)) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(slot_mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  const hipError_t err =
+      pa::launch_reshape_and_cache(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
+                                   num_heads, head_dim * e, block_size, num_blocks,
+                                   static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping,
+                           int32_t num_pairs, int32_t num_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, pa_dtype_t dtype,
+                           void* stream) {
+  const int e = elem_bytes(dtype);
+  if (e == 0 || !supported_shape(head_dim, block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  const size_t block_bytes = static_cast<size_t>(num_heads) * block_size * head_dim * e;
+  const size_t chunks = (block_bytes + pa::kCopyChunkBytes - 1) / pa::kCopyChunkBytes;
+  if (chunks * static_cast<size_t>(num_pairs) > static_cast<size_t>(INT_MAX))
+    return PA_ERR_INVALID_ARG;
+  const hipError_t err = pa::launch_copy_blocks(k_pool, v_pool, block_mapping, num_pairs,
+                                                block_bytes, num_blocks,
+                                                static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

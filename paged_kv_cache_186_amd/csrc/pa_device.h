@@ -1,0 +1,119 @@
+// Device-side building blocks shared by the libpagedattn kernels (gfx950).
+//
+// Storage types are tag structs that know how to turn one 16-byte vector
+// (what one lane moves with a global_load_dwordx4) into fp32 values and how to
+// round an fp32 result back to storage with round-to-nearest-even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kVecBytes = 16;
+
+// Reinterpret one 32-bit word as fp32.  The word is taken by value on
+// purpose: this clang lowers __builtin_bit_cast applied directly to an
+// ext-vector element (v.y, v.z, ...) as a cast of the vector's FIRST word.
+__device__ __forceinline__ float word_as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
+
+struct F32 {
+  using storage = float;
+  static constexpr int kElems = 4;  // per 16-byte vector
+  static __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
+    const uint32_t w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
+    f[0] = word_as_float(w0);
+    f[1] = word_as_float(w1);
+    f[2] = word_as_float(w2);
+    f[3] = word_as_float(w3);
+  }
+  static __device__ __forceinline__ storage pack(float x) { return x; }
+};
+
+struct F16 {
+  using storage = _Float16;
+  static constexpr int kElems = 8;
+  static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    f[0] = static_cast<float>(h.x);
+    f[1] = static_cast<float>(h.y);
+  }
+  static __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
+    unpack_word(v.x, f + 0);
+    unpack_word(v.y, f + 2);
+    unpack_word(v.z, f + 4);
+    unpack_word(v.w, f + 6);
+  }
+  // v_cvt_f16_f32 rounds to nearest even in the default rounding mode.
+  static __device__ __forceinline__ storage pack(float x) { return static_cast<_Float16>(x); }
+};
+
+struct BF16 {
+  using storage = uint16_t;
+  static constexpr int kElems = 8;
+  static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
+    f[0] = __builtin_bit_cast(float, w << 16);
+    f[1] = __builtin_bit_cast(float, w & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
+    unpack_word(v.x, f + 0);
+    unpack_word(v.y, f + 2);
+    unpack_word(v.z, f + 4);
+    unpack_word(v.w, f + 6);
+  }
+  // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+  static __device__ __forceinline__ storage pack(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums over aligned groups of G consecutive lanes (G = 8, 16, 32),
+// leaving the group total in every lane of the group.  DPP quad permutes give
+// the xor-1 and xor-2 partners; row_half_mirror (lane i <- 7-i within 8) and
+// row_mirror (lane i <- 15-i within 16) then pair each lane with one in the
+// other half, which completes the 8- and 16-lane sums; ds_swizzle with xor
+// mask 16 crosses the two rows of a 32-lane half-wave.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dpp_quad_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_half_mirror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_mirror(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swizzle_xor16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 8 || G == 16 || G == 32, "group of 8, 16 or 32 lanes");
+  x += dpp_quad_xor1(x);
+  x += dpp_quad_xor2(x);
+  x += dpp_row_half_mirror(x);
+  if constexpr (G >= 16) x += dpp_row_mirror(x);
+  if constexpr (G >= 32) x += swizzle_xor16(x);
+  return x;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+}  // namespace pa
