@@ -203,7 +203,7 @@ def main() -> int:
     reps = [(w.k_pool, w.v_pool)] + [(w.k_pool.clone(), w.v_pool.clone()) for _ in range(R - 1)]
     out = torch.empty_like(q)
     ws_bytes = pa.pa_decode_workspace_size(S, H, D, w.table_width, bs, args.partition)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = pa.new_workspace(ws_bytes, dev)
 
     def make_step(n_rep):
         def step(i, ev_a, ev_b, ev_c):

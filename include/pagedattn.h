@@ -3,7 +3,9 @@
  *
  * A C ABI over hand-written HIP kernels.  Every pointer argument that names
  * tensor data is DEVICE memory owned by the caller; the library allocates
- * nothing, keeps no state between calls and holds no handle.  All work is
+ * nothing and holds no handle (the only thing carried from one call to the
+ * next is the all-zero state of the arrival counters in the caller's decode
+ * workspace, see pa_decode_workspace_size).  All work is
  * enqueued asynchronously on the given stream (a hipStream_t passed as void*;
  * NULL means the default stream).
  *
@@ -74,8 +76,16 @@ const char* pa_status_string(pa_status_t status);
 /*
  * Bytes of device workspace pa_decode needs for these sizes (0 when every
  * sequence fits in one partition, i.e. max_blocks_per_seq*block_size <=
- * partition tokens).  partition_size 0 selects the library default (512
- * tokens).  Returns 0 for sizes pa_decode would reject.
+ * partition tokens).  partition_size 0 lets the library choose the partition
+ * from the shape, exactly as pa_decode does.  Returns 0 for sizes pa_decode
+ * would reject.
+ *
+ * Workspace contract: the workspace begins with one 32-bit arrival counter per
+ * (sequence, head), 4*num_seqs*num_heads bytes rounded up to 256.  Those bytes
+ * must be zero when pa_decode starts; every pa_decode call leaves them zero
+ * when it completes.  So zero-fill a workspace once after allocating it, and
+ * again if it was used for anything else or with a different
+ * num_seqs*num_heads.  The rest of the workspace is scratch.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t max_blocks_per_seq, int32_t block_size,
@@ -89,12 +99,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  * Sources: PagedAttentionMetal, section 注意力计算优化; PagedAttention原理 §3.2
  * and the closing remarks of §3.4.
  *
- * Long contexts are split into partitions of partition_size tokens (0 = 512;
- * otherwise a positive multiple of block_size); each partition's softmax
- * partials (max, sum, weighted values) go to `workspace` and a log-sum-exp
- * merge combines them (the split-context decode the "PagedAttention MLX" page
- * names as its "Flash-Dec" roadmap milestone).  Within rounding the result
- * does not depend on partition_size.
+ * Long contexts are split into partitions of partition_size tokens (a positive
+ * multiple of block_size; 0 lets the library choose: 512 tokens, halved while
+ * the grid would be too small to fill the GPU, never below 8 blocks).  Each
+ * partition's softmax partials (max, sum, weighted values) go to `workspace`,
+ * and the last partition of a (sequence, head) to finish merges them with the
+ * log-sum-exp identity (the split-context decode the "PagedAttention MLX" page
+ * names as its "Flash-Dec" roadmap milestone) — one kernel launch in all.
+ * Within rounding the result does not depend on partition_size.
  *
  * Arithmetic: inputs are converted to fp32, dot products, softmax and the
  * weighted sum accumulate in fp32, and out is rounded to nearest-even once.
@@ -105,8 +117,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  *     the last block are never read (may hold anything, NaN included);
  *   - a referenced table entry outside [0, num_blocks) is not dereferenced:
  *     that (sequence, head) row of out becomes NaN.
- * Preconditions: out aliases no input; workspace is not shared by concurrent
- * calls.  num_seqs == 0 returns PA_OK and launches nothing.
+ * Preconditions: out aliases no input; the workspace follows the contract of
+ * pa_decode_workspace_size() and is not shared by calls that may overlap in
+ * time.  num_seqs == 0 returns PA_OK and launches nothing.
  * Limits: num_seqs <= 65535, num_heads <= 65535, partitions per sequence <= 65535.
  */
 pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,

@@ -10,6 +10,7 @@ seeded synthetic inputs.
 from .binding import (  # noqa: F401
     PagedAttnError,
     load_library,
+    new_workspace,
     pa_copy_blocks,
     pa_decode,
     pa_decode_workspace_size,

@@ -39,6 +39,12 @@ _SIGNATURES = {
 
 _lib: Optional[ctypes.CDLL] = None
 
+# Zero-filled pa_decode workspaces kept between calls, keyed by (device, stream,
+# num_seqs*num_heads): the library leaves the arrival counters at the start of a
+# workspace at zero after every call, so a cached workspace stays valid for the
+# next call with the same number of rows on the same stream.
+_WORKSPACES: dict = {}
+
 
 class PagedAttnError(RuntimeError):
     def __init__(self, fn: str, status: int):
@@ -105,11 +111,29 @@ def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int,
                                                        partition_size))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace that satisfies pa_decode's contract (zero-filled)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _cached_workspace(device, stream_handle: int, rows: int, need: int) -> torch.Tensor:
+    key = (torch.device(device).index, stream_handle, rows)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = new_workspace(need, device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def pa_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
               block_size: int, *, partition_size: int = 0,
               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Paged decode attention; writes and returns ``out`` ([S, H, D], q's dtype)."""
+    """Paged decode attention; writes and returns ``out`` ([S, H, D], q's dtype).
+
+    ``workspace`` (optional) must follow the C contract: zero-filled when first
+    used (``new_workspace``); by default a cached zero-filled one is used.
+    """
     lib = load_library()
     for t, n in ((out, "out"), (q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"),
                  (block_tables, "block_tables"), (context_lens, "context_lens")):
@@ -128,18 +152,18 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
              "context_lens must be int32 [num_seqs]")
     W = block_tables.shape[1]
     need = pa_decode_workspace_size(S, H, D, W, block_size, partition_size)
+    handle = _stream_handle(q.device, stream)
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _cached_workspace(q.device, handle, S * H, need)
         _dev(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         st = lib.pa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                            block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
                            block_size, S, H, D, k_pool.shape[0], W, partition_size,
-                           DTYPE_CODES[q.dtype], ws_ptr, ws_bytes,
-                           _stream_handle(q.device, stream))
+                           DTYPE_CODES[q.dtype], ws_ptr, ws_bytes, handle)
     _check("pa_decode", st)
     return out
 

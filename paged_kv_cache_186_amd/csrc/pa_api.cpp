@@ -33,9 +33,11 @@ bool supported_shape(int head_dim, int block_size) {
 }
 
 // Blocks per partition, or 0 when partition_size is not a positive multiple of
-// block_size (0 selects the default).
-int partition_blocks(int partition_size, int block_size) {
-  if (partition_size == 0) partition_size = pa::kDefaultPartitionTokens;
+// block_size.  0 lets the library choose from the shape.
+int partition_blocks(int partition_size, int num_seqs, int num_heads, int max_blocks,
+                     int block_size) {
+  if (partition_size == 0)
+    return pa::default_partition_blocks(num_seqs, num_heads, max_blocks, block_size);
   if (partition_size < 0 || partition_size % block_size != 0) return 0;
   return partition_size / block_size;
 }
@@ -63,7 +65,8 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
     p.status = PA_ERR_INVALID_ARG;
     return p;
   }
-  p.part_blocks = partition_blocks(partition_size, block_size);
+  p.part_blocks =
+      partition_blocks(partition_size, num_seqs, num_heads, max_blocks_per_seq, block_size);
   if (p.part_blocks == 0) {
     p.status = PA_ERR_INVALID_ARG;
     return p;
@@ -148,6 +151,7 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
   a.dtype = dtype;
   if (plan.ws.total > 0) {
     char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(ws + plan.ws.counter_offset);
     a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
     a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
   }

@@ -1,4 +1,4 @@
-// Paged decode attention kernels for gfx950.
+// Paged decode attention kernel for gfx950.
 //
 // What is computed: for each sequence s and head h, single-query softmax
 // attention over the first L_s cached tokens, whose K/V rows are found through
@@ -13,10 +13,10 @@
 // milestone 4) without describing.
 //
 // How (our design, not the pages'): decode is a matrix-vector product per
-// (sequence, head), so it is HBM-bound and MFMA would idle; the kernels are
-// built around streaming each (block, head) tile — BS*D contiguous elements,
-// 4 KiB for fp16 D=128 BS=16 — with every lane moving 16 bytes per load, so one
-// wave instruction covers 1 KiB of contiguous memory.
+// (sequence, head), so it is HBM-bound and MFMA would idle; everything is built
+// around streaming each (block, head) tile — BS*D contiguous elements, 4 KiB
+// for fp16 D=128 BS=16 — with every lane moving 16 bytes per load, so one wave
+// instruction covers 1 KiB of contiguous memory.
 //
 // Lane layout inside one wave for one tile: a cache row of D elements is spread
 // over LPR = D*elem/16 consecutive lanes, so one load instruction covers
@@ -27,6 +27,18 @@
 // cross-wave traffic; the RPL*NW group states of a workgroup are merged once,
 // through LDS, at the end.  Scores are kept in base-2 units (q is pre-scaled by
 // scale*log2(e)) so every exponential is a single v_exp_f32.
+//
+// Memory-level parallelism: each wave walks its tiles in groups of G and keeps
+// the NEXT group's K/V loads in flight while it computes the current group
+// (two register buffers), so up to 2*G tiles per wave are outstanding.
+//
+// Split-context merge without a second launch: a workgroup that covers one
+// partition of a multi-partition context writes its partial (max, sum,
+// unnormalised weighted V sum) to the workspace with L2-bypassing agent-scope
+// stores and takes a ticket from the (sequence, head) counter; the workgroup
+// that draws the last ticket merges all partials and resets the counter to
+// zero for the next call.  (A device-scope fence would have to write back and
+// invalidate the whole L2 of every XCD; the atomics avoid that.)
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -36,7 +48,8 @@ namespace pa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWavesPerGroup = 4;  // waves per workgroup of the partition kernel
+constexpr int kWavesPerGroup = 4;  // waves per workgroup
+constexpr int kTilesPerStage = 1;  // G: tiles per pipeline stage (2*G in flight per wave)
 
 template <typename T, int D, int BS>
 struct Tile {
@@ -51,24 +64,26 @@ struct Tile {
   static_assert(kLoads * kLoadBytes == kTileBytes, "a tile is a whole number of wave loads");
 };
 
+// G tiles' worth of K/V registers plus which logical block each one is.
+template <typename T, int D, int BS, int G>
+struct Stage {
+  u32x4 k[G][Tile<T, D, BS>::kLoads];
+  u32x4 v[G][Tile<T, D, BS>::kLoads];
+  int block[G];  // logical block index, or -1 when this slot holds no tile
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// One (block, head) tile: scores for this lane-group's rows, online-softmax
-// update, weighted V accumulation.  kMasked handles the last, partly filled
-// block: rows at or past L get weight exactly 0 and their V is never touched
-// (they may hold NaN).  All 64 lanes must be active (the DPP sums read every lane).
+// Online-softmax update of one lane group with one loaded tile.  kMasked
+// handles the last, partly filled block: rows at or past L get weight exactly
+// 0 and their V values are replaced by 0 (they may hold NaN).  All 64 lanes
+// must be active (the DPP sums read every lane).
 template <typename T, int D, int BS, bool kMasked>
-__device__ __forceinline__ void attend_tile(const char* __restrict__ kb, const char* __restrict__ vb,
+__device__ __forceinline__ void attend_tile(const u32x4 (&kv)[Tile<T, D, BS>::kLoads],
+                                            const u32x4 (&vv)[Tile<T, D, BS>::kLoads],
                                             const float (&qf)[T::kElems], float& m, float& l,
-                                            float (&acc)[T::kElems], int lane, int tok0, int L) {
+                                            float (&acc)[T::kElems], int tok0, int L) {
   using C = Tile<T, D, BS>;
-  u32x4 kv[C::kLoads];
-  u32x4 vv[C::kLoads];
-#pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) kv[i] = load16(kb + i * C::kLoadBytes + lane * kVecBytes);
-#pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) vv[i] = load16(vb + i * C::kLoadBytes + lane * kVecBytes);
-
   float sc[C::kLoads];
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
@@ -93,38 +108,39 @@ __device__ __forceinline__ void attend_tile(const char* __restrict__ kb, const c
   l *= alpha;
 #pragma unroll
   for (int e = 0; e < T::kElems; ++e) acc[e] *= alpha;
+  // Branch-free on purpose: rows past L are selected to weight 0 and value 0
+  // (never 0 * NaN), and every loaded register is read on every path, which
+  // lets the compiler keep the next tile's loads in flight across this call.
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
-    if (ok[i]) {
-      const float p = fast_exp2(sc[i] - mn);
-      float vf[T::kElems];
-      T::unpack(vv[i], vf);
-      l += p;
+    const float p = ok[i] ? fast_exp2(sc[i] - mn) : 0.f;
+    float vf[T::kElems];
+    T::unpack(vv[i], vf);
+    l += p;
 #pragma unroll
-      for (int e = 0; e < T::kElems; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
-    }
+    for (int e = 0; e < T::kElems; ++e) acc[e] = fmaf(p, ok[i] ? vf[e] : 0.f, acc[e]);
   }
   m = mn;
 }
 
 // Grid: (head, partition, sequence); NW waves per workgroup.  Workgroup
 // (h, p, s) covers blocks [p*PB, min((p+1)*PB, nblk)) of sequence s; wave w
-// takes blocks w, w+NW, ... of that range.  A sequence whose context fits one
-// partition writes `out` directly; otherwise the partition's (max, sum) and
-// unnormalised weighted V sum go to the workspace for decode_merge_kernel.
-template <typename T, int D, int BS, int NW>
-__global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
-    typename T::storage* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-    const typename T::storage* __restrict__ q, const char* __restrict__ k_pool,
-    const char* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, float q_scale, int num_heads, int num_blocks,
-    int max_blocks, int part_blocks, int max_parts) {
+// takes blocks w, w+NW, ... of that range.
+template <typename T, int D, int BS, int NW, int G>
+__global__ __launch_bounds__(NW* kWave) void decode_kernel(
+    typename T::storage* __restrict__ out, uint32_t* __restrict__ counters,
+    float* __restrict__ ws_ml, float* __restrict__ ws_acc, const typename T::storage* __restrict__ q,
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    float q_scale, int num_heads, int num_blocks, int max_blocks, int part_blocks, int max_parts) {
   using C = Tile<T, D, BS>;
+  using St = Stage<T, D, BS, G>;
   constexpr int kGroups = NW * C::kRowsPerLoad;
   __shared__ float s_m[kGroups];
   __shared__ float s_l[kGroups];
   __shared__ float s_acc[kGroups][D];
   __shared__ int s_bad[NW];
+  __shared__ int s_last;
 
   const int h = blockIdx.x;
   const int p = blockIdx.y;
@@ -161,109 +177,180 @@ __global__ __launch_bounds__(NW* kWave) void decode_partition_kernel(
   bool bad = false;
 
   const int32_t* tbl = block_tables + static_cast<size_t>(s) * max_blocks;
-  for (int j = b_begin + wave; j < b_end; j += NW) {
+  const int first = b_begin + wave;
+  const int nt = first < b_end ? (b_end - first + NW - 1) / NW : 0;  // tiles of this wave
+
+  // Issue the K/V loads of tile k of this wave (k < nt).
+  auto load_tile = [&](St& st, int g, int k) {
+    const int j = first + k * NW;
     int phys = tbl[j];
     if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
       bad = true;  // never dereference an id outside the pool
       phys = 0;
     }
     const size_t tile = (static_cast<size_t>(phys) * num_heads + h) * C::kTileBytes;
+    const char* kb = k_pool + tile + lane * kVecBytes;
+    const char* vb = v_pool + tile + lane * kVecBytes;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) st.k[g][i] = load16(kb + i * C::kLoadBytes);
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) st.v[g][i] = load16(vb + i * C::kLoadBytes);
+    st.block[g] = j;
+  };
+  auto attend_slot = [&](const St& st, int g) {
+    const int j = st.block[g];
     const int tok0 = j * BS + grp;
     if ((j + 1) * BS <= L)
-      attend_tile<T, D, BS, false>(k_pool + tile, v_pool + tile, qf, m, l, acc, lane, tok0, L);
+      attend_tile<T, D, BS, false>(st.k[g], st.v[g], qf, m, l, acc, tok0, L);
     else
-      attend_tile<T, D, BS, true>(k_pool + tile, v_pool + tile, qf, m, l, acc, lane, tok0, L);
+      attend_tile<T, D, BS, true>(st.k[g], st.v[g], qf, m, l, acc, tok0, L);
+  };
+  // A full stage holds G existing tiles: no per-slot guards, so every load it
+  // issues is consumed on every path (the compiler then knows which loads are
+  // outstanding and never waits on the prefetched stage early).
+  auto load_full = [&](St& st, int k0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) load_tile(st, g, k0 + g);
+    // keep the scheduler from sinking these loads below the compute that
+    // follows: they must be in flight while the previous stage is consumed
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto attend_full = [&](const St& st) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) attend_slot(st, g);
+  };
+
+  // Steady state over the full stages: load b, compute a, load the next a,
+  // compute b — no conditional load inside the loop, so at every point the
+  // compiler knows exactly one prefetched stage is outstanding.  The epilogue
+  // finishes the last one or two full stages, then the partial stage (fewer
+  // than G tiles), if any.
+  const int nfs = nt / G;
+  St a, b;
+  if (nfs > 0) load_full(a, 0);
+  int st = 0;
+  for (; st + 2 < nfs; st += 2) {
+    load_full(b, (st + 1) * G);
+    attend_full(a);
+    load_full(a, (st + 2) * G);
+    attend_full(b);
+  }
+  if (st + 1 < nfs) {
+    load_full(b, (st + 1) * G);
+    attend_full(a);
+    attend_full(b);
+  } else if (st < nfs) {
+    attend_full(a);
+  }
+  if constexpr (G > 1) {
+    const int rem = nt - nfs * G;
+#pragma unroll
+    for (int g = 0; g < G - 1; ++g)
+      if (g < rem) load_tile(b, g, nfs * G + g);
+#pragma unroll
+    for (int g = 0; g < G - 1; ++g)
+      if (g < rem) attend_slot(b, g);
   }
 
   // Merge the kGroups lane-group states of this workgroup through LDS.
-  const int g = wave * C::kRowsPerLoad + grp;
+  const int gidx = wave * C::kRowsPerLoad + grp;
   if (col == 0) {
-    s_m[g] = m;
-    s_l[g] = l;
+    s_m[gidx] = m;
+    s_l[gidx] = l;
   }
 #pragma unroll
-  for (int e = 0; e < T::kElems; ++e) s_acc[g][col * T::kElems + e] = acc[e];
+  for (int e = 0; e < T::kElems; ++e) s_acc[gidx][col * T::kElems + e] = acc[e];
   if (lane == 0) s_bad[wave] = bad ? 1 : 0;
   __syncthreads();
 
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+  const int d = threadIdx.x;  // blockDim.x >= D
+  float M = -INFINITY;
+  float lsum = 0.f;
+  float o = 0.f;
+  if (d < D) {
     int any_bad = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) any_bad |= s_bad[w];
-    float M = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) M = fmaxf(M, s_m[k]);
-    float lsum = 0.f;
-    float o = 0.f;
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
-      const float a = fast_exp2(s_m[k] - M);  // groups that met no token: exp2(-inf) = 0
-      lsum = fmaf(a, s_l[k], lsum);
-      o = fmaf(a, s_acc[k][d], o);
+      const float a_k = fast_exp2(s_m[k] - M);  // groups that met no token: exp2(-inf) = 0
+      lsum = fmaf(a_k, s_l[k], lsum);
+      o = fmaf(a_k, s_acc[k][d], o);
     }
     if (any_bad) {
       o = __builtin_nanf("");
       lsum = __builtin_nanf("");
     }
-    if (nparts == 1) {
-      out[row * D + d] = T::pack(o / lsum);
-    } else {
-      const size_t prow = row * max_parts + p;
-      ws_acc[prow * D + d] = o;
-      if (d == 0) {
-        ws_ml[prow * 2 + 0] = M;
-        ws_ml[prow * 2 + 1] = lsum;
-      }
+  }
+  if (nparts == 1) {
+    if (d < D) out[row * D + d] = T::pack(o / lsum);
+    return;
+  }
+
+  // Publish this partition's partial, then take a ticket.  Partials are
+  // written and read with agent-scope atomic accesses: on gfx950 these bypass
+  // the per-XCD L2 (which is not coherent across XCDs), so no L2 write-back or
+  // invalidate is needed — a device-scope fence would flush the whole L2 of
+  // every XCD once per workgroup.  Ordering comes from completion: the barrier
+  // waits until this workgroup's partial stores are performed (s_waitcnt)
+  // before thread 0 takes the ticket, and the last workgroup issues its partial
+  // loads only after its ticket has returned.
+  const size_t base = row * max_parts;
+  if (d < D) {
+    __hip_atomic_store(&ws_acc[(base + p) * D + d], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(&ws_ml[(base + p) * 2 + 0], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ws_ml[(base + p) * 2 + 1], lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-}
-
-// Log-sum-exp merge of the partitions of one (sequence, head): with M the
-// largest partition max, out = sum_i 2^(m_i-M) acc_i / sum_i 2^(m_i-M) l_i.
-// Grid (head, sequence), D threads; sequences with one partition are skipped
-// (the partition kernel already wrote them).
-template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(
-    typename T::storage* __restrict__ out, const float* __restrict__ ws_ml,
-    const float* __restrict__ ws_acc, const int32_t* __restrict__ context_lens, int num_heads,
-    int block_size, int max_blocks, int part_blocks, int max_parts) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int d = threadIdx.x;
-  const int L = min(max(context_lens[s], 0), max_blocks * block_size);
-  const int nblk = (L + block_size - 1) / block_size;
-  const int nparts = (nblk + part_blocks - 1) / part_blocks;
-  if (nparts <= 1) return;
-  const size_t row = static_cast<size_t>(s) * num_heads + h;
-  const size_t base = row * max_parts;
-  float M = -INFINITY;
-  for (int i = 0; i < nparts; ++i) M = fmaxf(M, ws_ml[(base + i) * 2]);
-  float num = 0.f;
-  float den = 0.f;
-  for (int i = 0; i < nparts; ++i) {
-    const float a = fast_exp2(ws_ml[(base + i) * 2] - M);
-    den = fmaf(a, ws_ml[(base + i) * 2 + 1], den);
-    num = fmaf(a, ws_acc[(base + i) * D + d], num);
+  // Wait until this wave's partial stores are performed (a workgroup barrier
+  // alone does not wait for global stores); the clobber keeps the compiler
+  // from moving memory accesses across the wait.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t ticket =
+        __hip_atomic_fetch_add(&counters[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (ticket == static_cast<uint32_t>(nparts - 1));
   }
-  out[row * D + d] = T::pack(num / den);
+  __syncthreads();
+  if (!s_last) return;
+
+  // Last arrival: log-sum-exp merge over the partitions of this (s, h),
+  // out = sum_i 2^(m_i-M) acc_i / sum_i 2^(m_i-M) l_i.
+  if (d < D) {
+    float Mx = -INFINITY;
+    for (int i = 0; i < nparts; ++i)
+      Mx = fmaxf(Mx, __hip_atomic_load(&ws_ml[(base + i) * 2], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT));
+    float num = 0.f;
+    float den = 0.f;
+    for (int i = 0; i < nparts; ++i) {
+      const float mi = __hip_atomic_load(&ws_ml[(base + i) * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float li = __hip_atomic_load(&ws_ml[(base + i) * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float ai = __hip_atomic_load(&ws_acc[(base + i) * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float wi = fast_exp2(mi - Mx);
+      den = fmaf(wi, li, den);
+      num = fmaf(wi, ai, num);
+    }
+    out[row * D + d] = T::pack(num / den);
+  }
+  if (threadIdx.x == 0)  // ready for the next call
+    __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int D, int BS>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t stream) {
   using S = typename T::storage;
   const dim3 grid(a.num_heads, a.max_partitions, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, BS, kWavesPerGroup>), grid,
-                     dim3(kWavesPerGroup * kWave), 0, stream, static_cast<S*>(a.out), a.ws_ml,
-                     a.ws_acc, static_cast<const S*>(a.q), static_cast<const char*>(a.k_pool),
-                     static_cast<const char*>(a.v_pool), a.block_tables, a.context_lens,
-                     a.scale * kLog2e, a.num_heads, a.num_blocks, a.max_blocks_per_seq,
-                     a.partition_blocks, a.max_partitions);
-  if (a.max_partitions > 1) {
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.num_heads, a.num_seqs), dim3(D), 0,
-                       stream, static_cast<S*>(a.out), a.ws_ml, a.ws_acc, a.context_lens,
-                       a.num_heads, BS, a.max_blocks_per_seq, a.partition_blocks,
-                       a.max_partitions);
-  }
+  hipLaunchKernelGGL((decode_kernel<T, D, BS, kWavesPerGroup, kTilesPerStage>), grid,
+                     dim3(kWavesPerGroup * kWave), 0, stream, static_cast<S*>(a.out), a.counters,
+                     a.ws_ml, a.ws_acc, static_cast<const S*>(a.q),
+                     static_cast<const char*>(a.k_pool), static_cast<const char*>(a.v_pool),
+                     a.block_tables, a.context_lens, a.scale * kLog2e, a.num_heads, a.num_blocks,
+                     a.max_blocks_per_seq, a.partition_blocks, a.max_partitions);
   return hipGetLastError();
 }
 

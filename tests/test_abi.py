@@ -82,16 +82,27 @@ def test_decode_workspace_rules(lib):
     # 3 blocks of 16 fit one 512-token partition: no workspace needed, none given:
     # the call would launch, so only the size is checked here
     assert lib.pa_decode_workspace_size(4, 4, 64, 3, 16, 0) == 0
-    need = lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 0)      # 4 partitions
-    assert need >= 8 * 32 * 4 * (128 + 2) * 4 and need % 256 == 0
-    assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 512) == need
+    need = lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 512)    # 4 partitions
+    rows = 8 * 32
+    assert need >= 4 * rows + rows * 4 * (128 + 2) * 4 and need % 256 == 0
     assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 256) > need
     assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 2048) == 0
+    # partition 0: the library halves 512 while the grid would have fewer than
+    # 2048 workgroups: 256 rows x 4 partitions -> 256 tokens (8 partitions)
+    assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 0) == \
+        lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 256)
+    # plenty of rows: 512 tokens stays
+    assert lib.pa_decode_workspace_size(64, 32, 128, 130, 32, 0) == \
+        lib.pa_decode_workspace_size(64, 32, 128, 130, 32, 512)
+    # never below 8 blocks per partition
+    assert lib.pa_decode_workspace_size(1, 1, 64, 64, 16, 0) == \
+        lib.pa_decode_workspace_size(1, 1, 64, 64, 16, 128)
     assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 24) == 0        # invalid -> 0
     assert lib.pa_decode_workspace_size(8, 32, 96, 128, 16, 0) == 0          # invalid -> 0
+    need0 = lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 0)
     assert _decode(lib, S=8, H=32, D=128, W=128, ws=None, wsb=0) == WORKSPACE
-    assert _decode(lib, S=8, H=32, D=128, W=128, ws=FAKE, wsb=need - 1) == WORKSPACE
-    assert _decode(lib, S=8, H=32, D=128, W=128, ws=FAKE + 16, wsb=need) == INVALID  # misaligned
+    assert _decode(lib, S=8, H=32, D=128, W=128, ws=FAKE, wsb=need0 - 1) == WORKSPACE
+    assert _decode(lib, S=8, H=32, D=128, W=128, ws=FAKE + 16, wsb=need0) == INVALID  # misaligned
     # num_seqs == 0 is a no-op: OK without pointers, nothing launched
     assert _decode(lib, S=0, out=None, q=None, k=None, v=None, bt=None, cl=None) == OK
 

@@ -258,3 +258,29 @@ def test_workspace_too_small_is_refused():
     with pytest.raises(pa.PagedAttnError):
         pa.pa_decode(torch.empty_like(w.q), w.q, w.k_pool, w.v_pool, w.block_tables().to(DEV),
                      w.context_lens().to(DEV), w.scale, w.block_size, workspace=ws)
+
+
+def test_split_merge_counters_return_to_zero_and_results_repeat():
+    """The last-arriving partition merges; every call must leave the arrival
+    counters at the start of the workspace at zero, and the merge (done in
+    partition order whatever the arrival order) must repeat bit for bit."""
+    announce("decode ticket merge: counters and repeatability")
+    w = _on_device(W.layer_shape(2))
+    S, H = w.num_seqs, w.num_heads
+    need = pa.pa_decode_workspace_size(S, H, w.head_dim, w.table_width, w.block_size, 16)
+    ws = pa.new_workspace(need, DEV)
+    ref = oracle_decode(w)
+    bt, cl = w.block_tables().to(DEV), w.context_lens().to(DEV)
+    first = None
+    for it in range(20):
+        out = torch.empty_like(w.q)
+        pa.pa_decode(out, w.q, w.k_pool, w.v_pool, bt, cl, w.scale, w.block_size,
+                     partition_size=16, workspace=ws)
+        torch.cuda.synchronize()
+        counters = ws[: 4 * S * H].view(torch.int32)
+        assert int(counters.abs().sum()) == 0, f"counters not reset after call {it}"
+        if first is None:
+            first = out.clone()
+            assert_close(out, ref, torch.float16, "128 partitions")
+        else:
+            assert torch.equal(bits(out), bits(first)), f"call {it} differs"
