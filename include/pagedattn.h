@@ -74,11 +74,10 @@ int32_t pa_abi_version(void);
 const char* pa_status_string(pa_status_t status);
 
 /*
- * Bytes of device workspace pa_decode needs for these sizes (0 when every
- * sequence fits in one partition, i.e. max_blocks_per_seq*block_size <=
- * partition tokens).  partition_size 0 lets the library choose the partition
- * from the shape, exactly as pa_decode does.  Returns 0 for sizes pa_decode
- * would reject.
+ * Bytes of device workspace pa_decode needs for these sizes and this
+ * partition_size (the same rule as pa_decode; with an explicit partition_size
+ * it is 0 when every sequence fits in one partition).  Returns 0 for sizes
+ * pa_decode would reject.
  *
  * Workspace contract: the workspace begins with one 32-bit arrival counter per
  * (sequence, head), 4*num_seqs*num_heads bytes rounded up to 256.  Those bytes
@@ -99,14 +98,20 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t hea
  * Sources: PagedAttentionMetal, section 注意力计算优化; PagedAttention原理 §3.2
  * and the closing remarks of §3.4.
  *
- * Long contexts are split into partitions of partition_size tokens (a positive
- * multiple of block_size; 0 lets the library choose: 512 tokens, halved while
- * the grid would be too small to fill the GPU, never below 8 blocks).  Each
- * partition's softmax partials (max, sum, weighted values) go to `workspace`,
- * and the last partition of a (sequence, head) to finish merges them with the
- * log-sum-exp identity (the split-context decode the "PagedAttention MLX" page
- * names as its "Flash-Dec" roadmap milestone) — one kernel launch in all.
- * Within rounding the result does not depend on partition_size.
+ * Long contexts are split and the pieces' softmax partials (max, sum,
+ * weighted values) are merged with the log-sum-exp identity — the
+ * split-context decode the "PagedAttention MLX" page names as its "Flash-Dec"
+ * roadmap milestone — inside the one kernel launch: the last piece of a
+ * (sequence, head) to finish merges them.  How contexts are split:
+ *   - partition_size 0 with num_seqs <= 2048 (the default): every wave of a
+ *     fixed grid takes an equal share of all (sequence, head, block) work, so
+ *     the load is balanced whatever the mix of lengths; a (sequence, head)
+ *     lying inside one share is finished without any partial;
+ *   - partition_size > 0 (a multiple of block_size), or num_seqs > 2048: one
+ *     workgroup per partition of partition_size tokens (0 then picks 512,
+ *     halved while the grid would be too small to fill the GPU, never below 8
+ *     blocks).
+ * Within rounding the result does not depend on how contexts are split.
  *
  * Arithmetic: inputs are converted to fp32, dot products, softmax and the
  * weighted sum accumulate in fp32, and out is rounded to nearest-even once.

@@ -18,7 +18,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+# PAGEDATTN_LIBRARY may name another build of the same library (e.g. one
+# compiled with different launch-shape constants); default: the in-tree build.
+LIB_PATH = os.environ.get("PAGEDATTN_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            "include", "pagedattn.h")
 

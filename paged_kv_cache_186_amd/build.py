@@ -23,7 +23,7 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
-SOURCES = ["pa_decode.hip", "pa_cache_ops.hip", "pa_api.cpp"]
+SOURCES = ["pa_decode.hip", "pa_decode_balanced.hip", "pa_cache_ops.hip", "pa_api.cpp"]
 
 # Packed-FP32 VALU forms are disabled: plain fp32 code only.
 COMMON_FLAGS = [
@@ -40,28 +40,32 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm install required to build libpagedattn)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out_path: str = LIB_PATH, defines=()) -> str:
+    """Compile every source and link ``out_path``.  ``defines`` (NAME=VALUE
+    strings) override the launch-shape constants of the kernels, for tuning."""
+    build_dir = BUILD_DIR if out_path == LIB_PATH else out_path + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    tmp = out_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link of {LIB_NAME} failed:\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out_path}")
+    return out_path
 
 
 if __name__ == "__main__":

@@ -44,14 +44,19 @@ int partition_blocks(int partition_size, int num_seqs, int num_heads, int max_bl
 
 struct DecodePlan {
   pa_status_t status;
+  pa::DecodeMode mode;
   int part_blocks;
   int max_parts;
+  int workgroups;
   pa::WorkspaceLayout ws;
 };
 
+// partition_size 0 selects the balanced split whenever it applies (at most
+// kBalancedMaxSeqs sequences); otherwise, or with an explicit partition size,
+// the partitioned kernel runs.
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                        int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
-  DecodePlan p{PA_OK, 0, 0, {0, 0, 0}};
+  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, {0, 0, 0, 0}};
   if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0) {
     p.status = PA_ERR_INVALID_ARG;
     return p;
@@ -65,6 +70,15 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
     p.status = PA_ERR_INVALID_ARG;
     return p;
   }
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads;
+  const long long tiles = static_cast<long long>(rows) * max_blocks_per_seq;
+  if (partition_size == 0 && num_seqs <= pa::kBalancedMaxSeqs && tiles < (1LL << 40)) {
+    p.mode = pa::DecodeMode::kBalanced;
+    p.workgroups = pa::balanced_workgroups(num_seqs, num_heads, max_blocks_per_seq);
+    const size_t slots = static_cast<size_t>(p.workgroups) * pa::kBalancedWaves + rows;
+    p.ws = pa::workspace_layout(rows, slots, head_dim);
+    return p;
+  }
   p.part_blocks =
       partition_blocks(partition_size, num_seqs, num_heads, max_blocks_per_seq, block_size);
   if (p.part_blocks == 0) {
@@ -76,7 +90,8 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
     p.status = PA_ERR_INVALID_ARG;
     return p;
   }
-  p.ws = pa::workspace_layout(num_seqs, num_heads, head_dim, p.max_parts);
+  const size_t slots = p.max_parts > 1 ? rows * p.max_parts : 0;
+  p.ws = pa::workspace_layout(rows, slots, head_dim);
   return p;
 }
 
@@ -146,16 +161,20 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
+  a.dtype = dtype;
+  a.mode = plan.mode;
   a.partition_blocks = plan.part_blocks;
   a.max_partitions = plan.max_parts;
-  a.dtype = dtype;
+  a.workgroups = plan.workgroups;
   if (plan.ws.total > 0) {
     char* ws = static_cast<char*>(workspace);
     a.counters = reinterpret_cast<uint32_t*>(ws + plan.ws.counter_offset);
     a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
     a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
   }
-  const hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = plan.mode == pa::DecodeMode::kBalanced
+                           ? pa::launch_decode_balanced(a, static_cast<hipStream_t>(stream))
+                           : pa::launch_decode_partitioned(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -1,0 +1,106 @@
+// Shared pieces of the decode kernels (gfx950): tile geometry, the per-tile
+// online-softmax update, log-sum-exp combination and coherent accesses to the
+// workspace.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int D, int BS>
+struct Tile {
+  static constexpr int kElems = T::kElems;                       // per 16-byte vector
+  static constexpr int kLanesPerRow = D / kElems;                // 8, 16 or 32
+  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;      // 8, 4 or 2
+  static constexpr int kLoads = BS / kRowsPerLoad;               // per tensor per tile
+  static constexpr int kRowBytes = D * static_cast<int>(sizeof(typename T::storage));
+  static constexpr int kTileBytes = BS * kRowBytes;
+  static constexpr int kLoadBytes = kWave * kVecBytes;           // 1 KiB per wave instruction
+  static_assert(kLanesPerRow * kVecBytes == kRowBytes, "a row is a whole number of lane vectors");
+  static_assert(kLoads * kLoadBytes == kTileBytes, "a tile is a whole number of wave loads");
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax update of one lane group with one loaded tile.  kMasked
+// handles the last, partly filled block: rows at or past L get weight exactly
+// 0 and their V values are replaced by 0 (they may hold NaN).  All 64 lanes
+// must be active (the DPP sums read every lane).
+template <typename T, int D, int BS, bool kMasked>
+__device__ __forceinline__ void attend_tile(const u32x4 (&kv)[Tile<T, D, BS>::kLoads],
+                                            const u32x4 (&vv)[Tile<T, D, BS>::kLoads],
+                                            const float (&qf)[T::kElems], float& m, float& l,
+                                            float (&acc)[T::kElems], int tok0, int L) {
+  using C = Tile<T, D, BS>;
+  float sc[C::kLoads];
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    float kf[T::kElems];
+    T::unpack(kv[i], kf);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < T::kElems; ++e) d = fmaf(qf[e], kf[e], d);
+    sc[i] = group_sum<C::kLanesPerRow>(d);
+  }
+
+  bool ok[C::kLoads];
+  float bm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    ok[i] = !kMasked || (tok0 + i * C::kRowsPerLoad < L);
+    if (ok[i]) bm = fmaxf(bm, sc[i]);
+  }
+  const float mn = fmaxf(m, bm);
+  // mn is -inf only while this group has met no token: nothing to rescale then.
+  const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+  l *= alpha;
+#pragma unroll
+  for (int e = 0; e < T::kElems; ++e) acc[e] *= alpha;
+  // Branch-free on purpose: rows past L are selected to weight 0 and value 0
+  // (never 0 * NaN), and every loaded register is read on every path, which
+  // lets the compiler keep the next tile's loads in flight across this call.
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    const float p = ok[i] ? fast_exp2(sc[i] - mn) : 0.f;
+    float vf[T::kElems];
+    T::unpack(vv[i], vf);
+    l += p;
+#pragma unroll
+    for (int e = 0; e < T::kElems; ++e) acc[e] = fmaf(p, ok[i] ? vf[e] : 0.f, acc[e]);
+  }
+  m = mn;
+}
+
+// Workspace accesses shared between workgroups on different XCDs use
+// agent-scope relaxed atomics: on gfx950 these are L2-bypassing (sc1) loads
+// and stores, coherent across XCDs without any cache write-back or invalidate.
+__device__ __forceinline__ uint64_t load_coherent_u64(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// (m, d) <- lse-combine of (m, d) and (m2, d2); empty states have m = -inf.
+__device__ __forceinline__ void lse_combine(float& m, float& d, float m2, float d2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    d = d2;
+    return;
+  }
+  const float mn = fmaxf(m, m2);
+  d = d * fast_exp2(m - mn) + d2 * fast_exp2(m2 - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void store_coherent_u64(float* p, float lo, float hi) {
+  const uint64_t v = static_cast<uint64_t>(__builtin_bit_cast(uint32_t, lo)) |
+                     (static_cast<uint64_t>(__builtin_bit_cast(uint32_t, hi)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float lo_float(uint64_t v) { return __builtin_bit_cast(float, static_cast<uint32_t>(v)); }
+__device__ __forceinline__ float hi_float(uint64_t v) { return __builtin_bit_cast(float, static_cast<uint32_t>(v >> 32)); }
+
+}  // namespace pa

@@ -40,6 +40,7 @@
 // zero for the next call.  (A device-scope fence would have to write back and
 // invalidate the whole L2 of every XCD; the atomics avoid that.)
 
+#include "pa_attend.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pagedattn.h"
@@ -47,22 +48,16 @@
 namespace pa {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWavesPerGroup = 4;  // waves per workgroup
-constexpr int kTilesPerStage = 1;  // G: tiles per pipeline stage (2*G in flight per wave)
-
-template <typename T, int D, int BS>
-struct Tile {
-  static constexpr int kElems = T::kElems;                       // per 16-byte vector
-  static constexpr int kLanesPerRow = D / kElems;                // 8, 16 or 32
-  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;      // 8, 4 or 2
-  static constexpr int kLoads = BS / kRowsPerLoad;               // per tensor per tile
-  static constexpr int kRowBytes = D * static_cast<int>(sizeof(typename T::storage));
-  static constexpr int kTileBytes = BS * kRowBytes;
-  static constexpr int kLoadBytes = kWave * kVecBytes;           // 1 KiB per wave instruction
-  static_assert(kLanesPerRow * kVecBytes == kRowBytes, "a row is a whole number of lane vectors");
-  static_assert(kLoads * kLoadBytes == kTileBytes, "a tile is a whole number of wave loads");
-};
+// Launch shape; the defaults were chosen by measurement on MI355X and can be
+// overridden at build time for tuning sweeps.
+#ifndef PA_WAVES_PER_WG
+#define PA_WAVES_PER_WG 4
+#endif
+#ifndef PA_TILES_PER_STAGE
+#define PA_TILES_PER_STAGE 1
+#endif
+constexpr int kWavesPerGroup = PA_WAVES_PER_WG;  // waves per workgroup
+constexpr int kTilesPerStage = PA_TILES_PER_STAGE;  // G: tiles per stage (2*G in flight per wave)
 
 // G tiles' worth of K/V registers plus which logical block each one is.
 template <typename T, int D, int BS, int G>
@@ -72,55 +67,93 @@ struct Stage {
   int block[G];  // logical block index, or -1 when this slot holds no tile
 };
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of one (sequence, head)'s partition partials, run by the
+// workgroup that finished last.  With M = max_i m_i (base-2 units):
+//   out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
+// All loads are agent-scope (coherent across XCDs) and independent, so they
+// are issued in large batches: pass 1 streams (m_i, l_i) pairs and keeps an
+// online (max, sum) per thread; pass 2 has every thread read a 16-byte slice
+// of kMergeBatch partials before using any of them.
+// ---------------------------------------------------------------------------
+constexpr int kMergeCache = 1024;  // partitions whose weights are kept in LDS
+constexpr int kMergeBatch = 16;    // partial slices in flight per thread
 
-// Online-softmax update of one lane group with one loaded tile.  kMasked
-// handles the last, partly filled block: rows at or past L get weight exactly
-// 0 and their V values are replaced by 0 (they may hold NaN).  All 64 lanes
-// must be active (the DPP sums read every lane).
-template <typename T, int D, int BS, bool kMasked>
-__device__ __forceinline__ void attend_tile(const u32x4 (&kv)[Tile<T, D, BS>::kLoads],
-                                            const u32x4 (&vv)[Tile<T, D, BS>::kLoads],
-                                            const float (&qf)[T::kElems], float& m, float& l,
-                                            float (&acc)[T::kElems], int tok0, int L) {
-  using C = Tile<T, D, BS>;
-  float sc[C::kLoads];
-#pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    float kf[T::kElems];
-    T::unpack(kv[i], kf);
-    float d = 0.f;
-#pragma unroll
-    for (int e = 0; e < T::kElems; ++e) d = fmaf(qf[e], kf[e], d);
-    sc[i] = group_sum<C::kLanesPerRow>(d);
+template <typename T, int D, int kThreads>
+__device__ __forceinline__ void merge_partials(typename T::storage* __restrict__ out_row,
+                               const float* __restrict__ ml,   // [nparts][2]
+                               const float* __restrict__ acc,  // [nparts][D]
+                               int nparts, float* s_w, float* s_red, float* s_pair) {
+  const int t = threadIdx.x;
+  // pass 1: global max and denominator; cache each partition's max
+  float m = -INFINITY;
+  float den = 0.f;
+  for (int i = t; i < nparts; i += kThreads) {
+    const uint64_t pr = load_coherent_u64(ml + 2 * i);
+    const float mi = __builtin_bit_cast(float, static_cast<uint32_t>(pr));
+    const float li = __builtin_bit_cast(float, static_cast<uint32_t>(pr >> 32));
+    if (i < kMergeCache) s_w[i] = mi;
+    lse_combine(m, den, mi, li);
   }
+  // reduce (m, den) over the wave, then over the waves through LDS
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float d2 = __shfl_xor(den, off);
+    lse_combine(m, den, m2, d2);
+  }
+  constexpr int kWaves = kThreads / kWave;
+  if (t % kWave == 0) {
+    s_pair[2 * (t / kWave)] = m;
+    s_pair[2 * (t / kWave) + 1] = den;
+  }
+  __syncthreads();
+  m = -INFINITY;
+  den = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) lse_combine(m, den, s_pair[2 * w], s_pair[2 * w + 1]);
+  const float M = m;
+  for (int i = t; i < min(nparts, kMergeCache); i += kThreads) s_w[i] = fast_exp2(s_w[i] - M);
+  __syncthreads();
 
-  bool ok[C::kLoads];
-  float bm = -INFINITY;
+  // pass 2: weighted sum of the partial vectors, 4 floats per thread per partial
+  constexpr int kChunks = D / 4;             // 16-byte slices per partial row
+  constexpr int kG = kThreads / kChunks;      // partials read side by side
+  const int c = t % kChunks;
+  const int g = t / kChunks;
+  float num[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = g; i0 < nparts; i0 += kG * kMergeBatch) {
+    uint64_t lo[kMergeBatch], hi[kMergeBatch];
 #pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    ok[i] = !kMasked || (tok0 + i * C::kRowsPerLoad < L);
-    if (ok[i]) bm = fmaxf(bm, sc[i]);
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int i = min(i0 + u * kG, nparts - 1);  // clamped: always issue the load
+      lo[u] = load_coherent_u64(acc + static_cast<size_t>(i) * D + 4 * c);
+      hi[u] = load_coherent_u64(acc + static_cast<size_t>(i) * D + 4 * c + 2);
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int i = i0 + u * kG;
+      float wi = 0.f;
+      if (i < nparts) {
+        wi = i < kMergeCache ? s_w[i]
+                             : fast_exp2(__builtin_bit_cast(float, static_cast<uint32_t>(
+                                             load_coherent_u64(ml + 2 * i))) - M);
+      }
+      num[0] = fmaf(wi, __builtin_bit_cast(float, static_cast<uint32_t>(lo[u])), num[0]);
+      num[1] = fmaf(wi, __builtin_bit_cast(float, static_cast<uint32_t>(lo[u] >> 32)), num[1]);
+      num[2] = fmaf(wi, __builtin_bit_cast(float, static_cast<uint32_t>(hi[u])), num[2]);
+      num[3] = fmaf(wi, __builtin_bit_cast(float, static_cast<uint32_t>(hi[u] >> 32)), num[3]);
+    }
   }
-  const float mn = fmaxf(m, bm);
-  // mn is -inf only while this group has met no token: nothing to rescale then.
-  const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
-  l *= alpha;
 #pragma unroll
-  for (int e = 0; e < T::kElems; ++e) acc[e] *= alpha;
-  // Branch-free on purpose: rows past L are selected to weight 0 and value 0
-  // (never 0 * NaN), and every loaded register is read on every path, which
-  // lets the compiler keep the next tile's loads in flight across this call.
+  for (int e = 0; e < 4; ++e) s_red[g * D + 4 * c + e] = num[e];
+  __syncthreads();
+  for (int d = t; d < D; d += kThreads) {
+    float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    const float p = ok[i] ? fast_exp2(sc[i] - mn) : 0.f;
-    float vf[T::kElems];
-    T::unpack(vv[i], vf);
-    l += p;
-#pragma unroll
-    for (int e = 0; e < T::kElems; ++e) acc[e] = fmaf(p, ok[i] ? vf[e] : 0.f, acc[e]);
+    for (int k = 0; k < kG; ++k) sum += s_red[k * D + d];
+    out_row[d] = T::pack(sum / den);
   }
-  m = mn;
 }
 
 // Grid: (head, partition, sequence); NW waves per workgroup.  Workgroup
@@ -141,6 +174,9 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
   __shared__ float s_acc[kGroups][D];
   __shared__ int s_bad[NW];
   __shared__ int s_last;
+  __shared__ float s_w[kMergeCache];
+  __shared__ float s_pair[2 * NW];
+  static_assert(kGroups * D >= (NW * kWave / (D / 4)) * D, "merge reduction fits in s_acc");
 
   const int h = blockIdx.x;
   const int p = blockIdx.y;
@@ -318,25 +354,10 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
   __syncthreads();
   if (!s_last) return;
 
-  // Last arrival: log-sum-exp merge over the partitions of this (s, h),
-  // out = sum_i 2^(m_i-M) acc_i / sum_i 2^(m_i-M) l_i.
-  if (d < D) {
-    float Mx = -INFINITY;
-    for (int i = 0; i < nparts; ++i)
-      Mx = fmaxf(Mx, __hip_atomic_load(&ws_ml[(base + i) * 2], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT));
-    float num = 0.f;
-    float den = 0.f;
-    for (int i = 0; i < nparts; ++i) {
-      const float mi = __hip_atomic_load(&ws_ml[(base + i) * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float li = __hip_atomic_load(&ws_ml[(base + i) * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float ai = __hip_atomic_load(&ws_acc[(base + i) * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float wi = fast_exp2(mi - Mx);
-      den = fmaf(wi, li, den);
-      num = fmaf(wi, ai, num);
-    }
-    out[row * D + d] = T::pack(num / den);
-  }
+  // Last arrival: merge every partition of this (s, h).  s_acc is free again
+  // and serves as the reduction buffer.
+  merge_partials<T, D, NW * kWave>(out + row * D, ws_ml + base * 2, ws_acc + base * D, nparts,
+                                   s_w, &s_acc[0][0], s_pair);
   if (threadIdx.x == 0)  // ready for the next call
     __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -366,7 +387,7 @@ hipError_t run_decode_d(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_partitioned(const DecodeArgs& a, hipStream_t stream) {
   switch (a.dtype) {
     case PA_DTYPE_F32:
       return run_decode_d<F32>(a, stream);

@@ -7,9 +7,38 @@
 
 namespace pa {
 
-constexpr int kDefaultPartitionTokens = 512;
+#ifndef PA_DEFAULT_PARTITION_TOKENS
+#define PA_DEFAULT_PARTITION_TOKENS 512
+#endif
+#ifndef PA_TARGET_WORKGROUPS
+#define PA_TARGET_WORKGROUPS 2048
+#endif
+#ifndef PA_MIN_PARTITION_BLOCKS
+#define PA_MIN_PARTITION_BLOCKS 8
+#endif
+#ifndef PA_BALANCED_WAVES
+#define PA_BALANCED_WAVES 4
+#endif
+#ifndef PA_BALANCED_WORKGROUPS
+#define PA_BALANCED_WORKGROUPS 256
+#endif
+#ifndef PA_BALANCED_MIN_TILES
+#define PA_BALANCED_MIN_TILES 2
+#endif
+
+constexpr int kDefaultPartitionTokens = PA_DEFAULT_PARTITION_TOKENS;
 constexpr int kMaxGridYZ = 65535;
 constexpr int kCopyChunkBytes = 16384;  // bytes one copy_blocks workgroup moves
+
+// Two work decompositions of one decode call:
+//  * kBalanced (partition_size 0, at most kBalancedMaxSeqs sequences): a fixed
+//    grid whose waves each take an equal contiguous share of all (sequence,
+//    head, block) tiles; only rows that straddle a share boundary produce
+//    partials.
+//  * kPartitioned (partition_size > 0, or more sequences): one workgroup per
+//    (head, partition, sequence); every multi-partition row produces one
+//    partial per partition.
+enum class DecodeMode { kBalanced, kPartitioned };
 
 struct DecodeArgs {
   void* out;
@@ -25,40 +54,41 @@ struct DecodeArgs {
   int head_dim;
   int num_blocks;
   int max_blocks_per_seq;
-  int partition_blocks;  // blocks per partition
-  int max_partitions;    // ceil(max_blocks_per_seq / partition_blocks)
   int dtype;             // pa_dtype_t
-  uint32_t* counters;    // [S][H] arrival tickets — null when max_partitions == 1
-  float* ws_ml;          // [S][H][max_partitions][2]  (max, sum)
-  float* ws_acc;         // [S][H][max_partitions][D]  unnormalised weighted V sums
+  DecodeMode mode;
+  int partition_blocks;  // kPartitioned: blocks per partition
+  int max_partitions;    // kPartitioned: ceil(max_blocks_per_seq / partition_blocks)
+  int workgroups;        // kBalanced: grid size
+  uint32_t* counters;    // [S][H] arrival tickets (null when no row can be split)
+  float* ws_ml;          // [slots][2]  (max, sum) of each partial
+  float* ws_acc;         // [slots][D]  unnormalised weighted V sum of each partial
 };
 
 // Workspace of pa_decode: the ticket counters come first (they must be zero
 // when a call starts; every call leaves the ones it used at zero), then the
-// per-partition softmax partials.
+// partial slots.
 struct WorkspaceLayout {
   size_t counter_offset, ml_offset, acc_offset, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline WorkspaceLayout workspace_layout(int num_seqs, int num_heads, int head_dim, int max_partitions) {
+inline WorkspaceLayout workspace_layout(size_t rows, size_t slots, int head_dim) {
   WorkspaceLayout w{0, 0, 0, 0};
-  if (max_partitions <= 1) return w;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads;
+  if (slots == 0) return w;
   w.counter_offset = 0;
   w.ml_offset = align_up(rows * sizeof(uint32_t), 256);
-  w.acc_offset = align_up(w.ml_offset + rows * max_partitions * 2 * sizeof(float), 256);
-  w.total = align_up(w.acc_offset + rows * max_partitions * head_dim * sizeof(float), 256);
+  w.acc_offset = align_up(w.ml_offset + slots * 2 * sizeof(float), 256);
+  w.total = align_up(w.acc_offset + slots * head_dim * sizeof(float), 256);
   return w;
 }
 
-// Partition size when the caller passes 0: start at kDefaultPartitionTokens and
-// halve while the grid would hold fewer than kTargetWorkgroups workgroups (an
-// upper bound: sequences shorter than the table width use fewer), but keep at
-// least kMinPartitionBlocks blocks so every wave pipelines two tile groups.
-constexpr long long kTargetWorkgroups = 2048;
-constexpr int kMinPartitionBlocks = 8;
+// Partition size when the caller passes 0 but the balanced split does not
+// apply: start at kDefaultPartitionTokens and halve while the grid would hold
+// fewer than kTargetWorkgroups workgroups (an upper bound: sequences shorter
+// than the table width use fewer), but keep at least kMinPartitionBlocks.
+constexpr long long kTargetWorkgroups = PA_TARGET_WORKGROUPS;
+constexpr int kMinPartitionBlocks = PA_MIN_PARTITION_BLOCKS;
 
 inline int default_partition_blocks(int num_seqs, int num_heads, int max_blocks, int block_size) {
   int pb = kDefaultPartitionTokens / block_size;
@@ -67,7 +97,29 @@ inline int default_partition_blocks(int num_seqs, int num_heads, int max_blocks,
   return pb;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Balanced split: at most kBalancedWorkgroups workgroups of kBalancedWaves
+// waves — one workgroup per CU of a 256-CU MI355X.  Measured: several
+// workgroups per CU finish at very different times (the older workgroup on a
+// CU is served first), so an equal static split only balances when each CU
+// runs one; it also keeps just enough bytes in flight.  Fewer workgroups are
+// used when the upper bound on tiles
+// (num_seqs * num_heads * max_blocks) would leave waves with under
+// kBalancedMinTiles tiles each.  The per-sequence prefix sums live in LDS,
+// hence the sequence limit.
+constexpr int kBalancedMaxSeqs = 2048;
+constexpr int kBalancedWaves = PA_BALANCED_WAVES;
+constexpr int kBalancedWorkgroups = PA_BALANCED_WORKGROUPS;
+constexpr int kBalancedMinTiles = PA_BALANCED_MIN_TILES;
+
+inline int balanced_workgroups(int num_seqs, int num_heads, int max_blocks) {
+  const long long tiles = static_cast<long long>(num_seqs) * num_heads * max_blocks;
+  const long long per_wg = static_cast<long long>(kBalancedWaves) * kBalancedMinTiles;
+  const long long g = (tiles + per_wg - 1) / per_wg;
+  return static_cast<int>(g < 1 ? 1 : (g > kBalancedWorkgroups ? kBalancedWorkgroups : g));
+}
+
+hipError_t launch_decode_partitioned(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_balanced(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                                     const int32_t* slot_mapping, int num_tokens, int num_heads,

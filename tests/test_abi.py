@@ -79,24 +79,25 @@ def test_decode_rejects_before_launch(lib, kw, status):
 
 
 def test_decode_workspace_rules(lib):
-    # 3 blocks of 16 fit one 512-token partition: no workspace needed, none given:
-    # the call would launch, so only the size is checked here
-    assert lib.pa_decode_workspace_size(4, 4, 64, 3, 16, 0) == 0
+    # 3 blocks of 16 fit one 512-token partition: no workspace needed (only the
+    # size is checked here: the call itself would launch)
+    assert lib.pa_decode_workspace_size(4, 4, 64, 3, 16, 512) == 0
     need = lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 512)    # 4 partitions
     rows = 8 * 32
     assert need >= 4 * rows + rows * 4 * (128 + 2) * 4 and need % 256 == 0
     assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 256) > need
     assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 2048) == 0
-    # partition 0: the library halves 512 while the grid would have fewer than
-    # 2048 workgroups: 256 rows x 4 partitions -> 256 tokens (8 partitions)
-    assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 0) == \
-        lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 256)
-    # plenty of rows: 512 tokens stays
-    assert lib.pa_decode_workspace_size(64, 32, 128, 130, 32, 0) == \
-        lib.pa_decode_workspace_size(64, 32, 128, 130, 32, 512)
-    # never below 8 blocks per partition
-    assert lib.pa_decode_workspace_size(1, 1, 64, 64, 16, 0) == \
-        lib.pa_decode_workspace_size(1, 1, 64, 64, 16, 128)
+    # partition 0 with <= 2048 sequences: balanced split; its workspace holds a
+    # counter per row and a partial slot per wave plus one per row
+    bal = lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 0)
+    assert bal > 0 and bal % 256 == 0
+    assert bal >= 4 * rows + (4 * 1024 + rows) * (128 + 2) * 4
+    assert lib.pa_decode_workspace_size(1, 1, 64, 1, 16, 0) > 0       # needed even if tiny
+    # more than 2048 sequences: partitioned, 512 tokens halved while the grid
+    # would have fewer than 2048 workgroups, never below 8 blocks
+    assert lib.pa_decode_workspace_size(4000, 2, 64, 64, 16, 0) == \
+        lib.pa_decode_workspace_size(4000, 2, 64, 64, 16, 512)
+    assert lib.pa_decode_workspace_size(4000, 2, 64, 3, 16, 0) == 0
     assert lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 24) == 0        # invalid -> 0
     assert lib.pa_decode_workspace_size(8, 32, 96, 128, 16, 0) == 0          # invalid -> 0
     need0 = lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 0)

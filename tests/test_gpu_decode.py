@@ -284,3 +284,59 @@ def test_split_merge_counters_return_to_zero_and_results_repeat():
             assert_close(out, ref, torch.float16, "128 partitions")
         else:
             assert torch.equal(bits(out), bits(first)), f"call {it} differs"
+
+
+def _ragged_workload(lens, H, D, bs, dtype, seed, poison=True):
+    rng = np.random.default_rng(seed)
+    nb = sum(-(-L // bs) for L in lens) + len(lens) + 4
+    m = W.BlockManager(nb, bs, free_order=rng.permutation(nb).tolist())
+    for s, L in enumerate(lens):
+        m.allocate(s)
+        m.append_slots(s, L)
+    width = max(1, max(-(-L // bs) for L in lens))
+    w = W.PagedWorkload("ragged", dtype, H, D, bs, nb, 0.9 / np.sqrt(D), m, list(range(len(lens))),
+                        width, seed, DEV)
+    return W.fill_values(w, poison=poison)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_balanced_split_with_empty_and_tiny_rows(dtype, bs):
+    """Default (balanced) split: empty contexts, 1-token contexts and long rows
+    that straddle many wave shares, all in one batch."""
+    announce(f"decode balanced ragged dtype={dtype} bs={bs}")
+    lens = [0, 1, 0, 5000, 2, 0, 333, bs, bs + 1, 0, 1]
+    w = _ragged_workload(lens, 5, 128, bs, dtype, 11)
+    ref = oracle_decode(w)
+    out = gpu_decode(w)
+    assert_close(out, ref, dtype, "balanced ragged")
+    for s in (0, 2, 5, 9):
+        assert torch.equal(out[s].cpu(), torch.zeros_like(out[s].cpu()))
+
+
+def test_more_sequences_than_the_balanced_limit_use_partitions():
+    announce("decode 2100 sequences (partitioned default)")
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 70, size=2100).tolist()
+    w = _ragged_workload(lens, 2, 64, 16, torch.float16, 12)
+    assert_close(gpu_decode(w), oracle_decode(w), torch.float16, "2100 sequences")
+
+
+def test_balanced_counters_return_to_zero_and_results_repeat():
+    announce("decode balanced: counters and repeatability")
+    w = _on_device(W.long_context(1, batch=1, device="cpu", context=40000))
+    S, H = w.num_seqs, w.num_heads
+    need = pa.pa_decode_workspace_size(S, H, w.head_dim, w.table_width, w.block_size, 0)
+    ws = pa.new_workspace(need, DEV)
+    bt, cl = w.block_tables().to(DEV), w.context_lens().to(DEV)
+    first = None
+    for it in range(10):
+        out = torch.empty_like(w.q)
+        pa.pa_decode(out, w.q, w.k_pool, w.v_pool, bt, cl, w.scale, w.block_size, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[: 4 * S * H].view(torch.int32).abs().sum()) == 0, f"counters after call {it}"
+        if first is None:
+            first = out.clone()
+            assert_close(out, oracle_decode(w), torch.float16, "40000-token rows")
+        else:
+            assert torch.equal(bits(out), bits(first)), f"call {it} differs"
