@@ -39,7 +39,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published peak
 COLD_BYTES = 2 << 30           # replica footprint that defeats the 256 MB last-level cache
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "pa_decode_layer_shape_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
-                  for f in ("pa_decode.hip", "pa_device.h")]
+                  for f in ("pa_decode.hip", "pa_decode_balanced.hip", "pa_attend.h",
+                            "pa_device.h", "pa_internal.h", "pa_api.cpp")]
 
 
 def log(msg: str) -> None:
@@ -111,24 +112,73 @@ def describe(w) -> str:
             f"block {w.block_size}, {str(w.dtype).replace('torch.', '')}, pool {w.num_blocks} blocks")
 
 
-def time_steps(step, n_steps: int, stream) -> dict:
-    """Run n_steps of `step(i, ev_a, ev_b, ev_c)`; events bracket each kernel call."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+def capture(enqueue) -> "torch.cuda.CUDAGraph":
+    """Capture the kernels `enqueue` launches on the current stream into a graph."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        enqueue()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, n: int, stream) -> float:
+    """Milliseconds per replay of g over n back-to-back replays."""
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    g.replay()
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(n_steps):
-        step(i, *ev[i])
+    for _ in range(n):
+        g.replay()
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    return start.elapsed_time(end) / n
+
+
+def time_eager(reshape, decode, n: int, stream) -> dict:
+    """Per-call HIP events around eager calls (includes host launch overhead)."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        ev[i][0].record(stream)
+        reshape(i)
+        ev[i][1].record(stream)
+        decode(i)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
     res = np.array([e[0].elapsed_time(e[1]) for e in ev])
     dec = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    return {"step_ms": total_ms / n_steps, "reshape_ms": float(res.mean()),
-            "decode_ms": float(dec.mean()), "decode_ms_p10": float(np.percentile(dec, 10)),
-            "decode_ms_p50": float(np.percentile(dec, 50)),
-            "decode_ms_p90": float(np.percentile(dec, 90))}
+    return {"pa_reshape_and_cache": float(np.median(res)), "pa_decode": float(np.median(dec)),
+            "pa_decode_p10": float(np.percentile(dec, 10)), "pa_decode_p90": float(np.percentile(dec, 90))}
+
+
+def check_graph_replays(g, decode, R: int, out) -> None:
+    """Replays of the decode graph must equal the eager call bit for bit, with
+    eager work in between (the graph ends with replica R-1)."""
+    decode(R - 1)
+    torch.cuda.synchronize()
+    want = out.clone()
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out.view(torch.int16), want.view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager decode")
+        decode(0)
+    torch.cuda.synchronize()
+
+
+def calibration_copy(pa, dev) -> None:
+    """pa_copy_blocks over a known byte count (3 calls of 256 blocks of 128 KiB
+    per pool: 64 MiB read and 64 MiB written each), so that counter runs carry
+    their own scale for FETCH_SIZE / WRITE_SIZE."""
+    k = torch.zeros((512, 32, 16, 128), dtype=torch.float16, device=dev)
+    v = torch.zeros_like(k)
+    pairs = torch.stack([torch.arange(256), torch.arange(256, 512)], 1).to(torch.int32).to(dev)
+    for _ in range(3):
+        pa.pa_copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    del k, v
 
 
 def cpu_baseline(w_host, k_new, v_new, slots, step_bytes: int, seconds: float) -> dict:
@@ -205,29 +255,44 @@ def main() -> int:
     ws_bytes = pa.pa_decode_workspace_size(S, H, D, w.table_width, bs, args.partition)
     ws = pa.new_workspace(ws_bytes, dev)
 
-    def make_step(n_rep):
-        def step(i, ev_a, ev_b, ev_c):
-            kp, vp = reps[i % n_rep]
-            ev_a.record(stream)
-            pa.pa_reshape_and_cache(kp, vp, k_new, v_new, slot_t)
-            ev_b.record(stream)
-            pa.pa_decode(out, q, kp, vp, tables, clens, w.scale, bs,
-                         partition_size=args.partition, workspace=ws)
-            ev_c.record(stream)
-        return step
+    calibration_copy(pa, dev)
 
-    log(f"warmup {args.warmup} steps")
-    time_steps(make_step(R), max(1, args.warmup), stream)
-    log(f"timing {args.steps} cold steps")
-    cold = time_steps(make_step(R), args.steps, stream)
-    log(f"timing {args.steps} warm steps")
-    warm = time_steps(make_step(1), args.steps, stream)
+    def reshape(i):
+        kp, vp = reps[i % R]
+        pa.pa_reshape_and_cache(kp, vp, k_new, v_new, slot_t)
+
+    def decode(i):
+        kp, vp = reps[i % R]
+        pa.pa_decode(out, q, kp, vp, tables, clens, w.scale, bs,
+                     partition_size=args.partition, workspace=ws)
+
+    # eager warmup, then HIP graphs: R steps (one per replica) captured once and
+    # replayed, so no host-side launch cost sits inside the timed region
+    log(f"warmup {args.warmup} steps (eager)")
+    for i in range(max(1, args.warmup)):
+        reshape(i)
+        decode(i)
+    torch.cuda.synchronize()
+    eager = time_eager(reshape, decode, min(args.steps, 200), stream)
+
+    step_graph = capture(lambda: [f(i) for i in range(R) for f in (reshape, decode)])
+    decode_graph = capture(lambda: [decode(i) for i in range(R)])
+    warm_graph = capture(lambda: [f(0) for _ in range(R) for f in (reshape, decode)])
+    check_graph_replays(decode_graph, decode, R, out)
+
+    n_rep = max(1, math.ceil(args.steps / R))
+    log(f"timing {n_rep * R} cold steps ({n_rep} replays of a {R}-step graph)")
+    step_ms = time_graph(step_graph, n_rep, stream) / R
+    dec_ms = time_graph(decode_graph, n_rep, stream) / R
+    log(f"timing {n_rep * R} warm steps")
+    warm_ms = time_graph(warm_graph, n_rep, stream) / R
+    n_steps = n_rep * R
 
     b_dec = decode_bytes(lens, H, D, e, bs)
     b_res = reshape_bytes(S, H, D, e)
-    step_s = cold["step_ms"] * 1e-3
+    step_s = step_ms * 1e-3
     value = (b_dec + b_res) / step_s / 1e9
-    dec_gbs = b_dec / (cold["decode_ms"] * 1e-3) / 1e9
+    dec_gbs = b_dec / (dec_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
     traffic = traffic_from_profile(digest)
 
@@ -236,9 +301,9 @@ def main() -> int:
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": n_steps,
         "warmup": args.warmup,
-        "ms_per_step": round(cold["step_ms"], 5),
+        "ms_per_step": round(step_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -249,24 +314,24 @@ def main() -> int:
             "seed": args.seed,
             "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": bs,
             "context_tokens": int(lens.sum()),
-            "partition_tokens": args.partition or 512,
+            "split": ("balanced (partition_size 0)" if args.partition == 0
+                      else f"partitions of {args.partition} tokens"),
             "accumulate": "f32",
             "cache": f"cold: rotates {R} pool replicas ({R * pool_bytes / 2**30:.2f} GiB)",
+            "timing": "HIP graph replays of R steps, HIP events around the replays",
             "parallelism": "none (1 GPU)",
         },
-        "us_per_step": round(cold["step_ms"] * 1e3, 3),
+        "us_per_step": round(step_ms * 1e3, 3),
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "sequence_heads_per_s": round(S * H / step_s, 1),
         "bytes_per_step": {"pa_decode": b_dec, "pa_reshape_and_cache": b_res},
-        "kernels_us": {"pa_reshape_and_cache": round(cold["reshape_ms"] * 1e3, 3),
-                       "pa_decode": round(cold["decode_ms"] * 1e3, 3),
-                       "pa_decode_p10": round(cold["decode_ms_p10"] * 1e3, 3),
-                       "pa_decode_p90": round(cold["decode_ms_p90"] * 1e3, 3)},
-        "warm": {"value": round((b_dec + b_res) / (warm["step_ms"] * 1e-3) / 1e9, 2),
-                 "us_per_step": round(warm["step_ms"] * 1e3, 3),
-                 "pa_decode_us": round(warm["decode_ms"] * 1e3, 3),
+        "kernels_us": {"pa_decode": round(dec_ms * 1e3, 3),
+                       "pa_reshape_and_cache_and_gaps": round((step_ms - dec_ms) * 1e3, 3)},
+        "eager_us": {k: round(v * 1e3, 3) for k, v in eager.items()},
+        "warm": {"value": round((b_dec + b_res) / (warm_ms * 1e-3) / 1e9, 2),
+                 "us_per_step": round(warm_ms * 1e3, 3),
                  "note": "no replica rotation: the working set can sit in the last-level cache"},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode",
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (one kernel launch per call)",
                      "achieved": round(dec_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel_source_sha": digest},
