@@ -395,14 +395,17 @@ __global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
   if (pend == 0) return;
   // tickets: this wave's partial stores must be performed first
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // lane p (< pend) takes pending row p's ticket: both in one round trip
+  uint32_t ticket = 0;
+  const size_t my_row = lane == 1 ? pend_row[1] : pend_row[0];
+  if (lane < pend)
+    ticket = __hip_atomic_fetch_add(&counters[my_row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t tk[2] = {static_cast<uint32_t>(__builtin_amdgcn_readlane(ticket, 0)),
+                          static_cast<uint32_t>(__builtin_amdgcn_readlane(ticket, 1))};
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     if (p >= pend) break;
-    uint32_t ticket = 0;
-    if (lane == 0)
-      ticket = __hip_atomic_fetch_add(&counters[pend_row[p]], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ticket = __builtin_amdgcn_readfirstlane(ticket);
-    if (ticket == static_cast<uint32_t>(pend_n[p] - 1)) {
+    if (tk[p] == static_cast<uint32_t>(pend_n[p] - 1)) {
       merge_row_wave<T, D>(out + pend_row[p] * D, ws_ml + pend_slot0[p] * 2, ws_acc + pend_slot0[p] * D,
                            pend_n[p], lane);
       if (lane == 0)  // ready for the next call

@@ -340,3 +340,57 @@ def test_balanced_counters_return_to_zero_and_results_repeat():
             assert_close(out, oracle_decode(w), torch.float16, "40000-token rows")
         else:
             assert torch.equal(bits(out), bits(first)), f"call {it} differs"
+
+
+def test_table_width_and_alignment_do_not_change_the_bits():
+    """Padding the block table with unused columns, or placing it at an
+    address that is only 4-byte aligned, changes neither the split (same grid,
+    same shares here) nor any arithmetic: every layout gives the same bits and
+    matches the oracle."""
+    announce("decode balanced: table width and alignment")
+    lens = [250, 7, 170]
+    S, H = len(lens), 48
+    w = _ragged_workload(lens, H, 128, 16, torch.float16, 21)
+    base = torch.from_numpy(w.block_tables_np())
+    ref = oracle_decode(w)
+
+    def table(width, offset=0):
+        buf = torch.full((offset + S * width,), -1, dtype=torch.int32)
+        buf[offset:].view(S, width)[:, : base.shape[1]] = base
+        dev = buf.to(DEV)
+        return dev[offset:].view(S, width)
+
+    outs = {}
+    for name, width, offset in (("w16", 16, 0), ("w17", 17, 0), ("w17+4B", 17, 1), ("w4200", 4200, 0)):
+        bt = table(width, offset)
+        assert (bt.data_ptr() % 16 == 0) == (offset == 0)
+        outs[name] = gpu_decode(w, tables=bt)
+        assert_close(outs[name], ref, torch.float16, name)
+    for name, out in outs.items():
+        assert torch.equal(bits(out), bits(outs["w16"])), f"{name} differs from w16"
+
+
+def test_one_workspace_serves_balanced_and_partitioned_calls_in_turn():
+    """The counter region (a ticket per row and the chunk-claim counter) is
+    the same in both layouts, and each kind of call leaves all of it zero, so
+    one zero-filled workspace can serve both kinds of call in any order."""
+    announce("decode: balanced and partitioned calls sharing one workspace")
+    w = _on_device(W.layer_shape(0, device="cpu"))
+    S, H = w.num_seqs, w.num_heads
+    need = max(pa.pa_decode_workspace_size(S, H, w.head_dim, w.table_width, w.block_size, p)
+               for p in (0, 16, 64))
+    ws = pa.new_workspace(need, DEV)
+    bt, cl = w.block_tables().to(DEV), w.context_lens().to(DEV)
+    ref = oracle_decode(w)
+    outs = []
+    for it, part in enumerate((0, 16, 0, 64, 0, 0)):
+        out = torch.empty_like(w.q)
+        pa.pa_decode(out, w.q, w.k_pool, w.v_pool, bt, cl, w.scale, w.block_size,
+                     partition_size=part, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[: 4 * S * H].view(torch.int32).abs().sum()) == 0, f"counters after call {it}"
+        assert_close(out, ref, torch.float16, f"call {it} (partition {part})")
+        if part == 0:
+            outs.append(out)
+    for o in outs[1:]:
+        assert torch.equal(bits(o), bits(outs[0]))
