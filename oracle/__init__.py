@@ -44,3 +44,11 @@ from .paged_attention import (  # noqa: F401
     reshape_and_cache_ref,
     copy_blocks_ref,
 )
+from .fp8 import (  # noqa: F401
+    fp8_values,
+    quantize_fp8_ref,
+    dequant_ref,
+    decode_fp8_ref,
+    reshape_and_cache_fp8_ref,
+    copy_blocks_fp8_ref,
+)
