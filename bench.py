@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and µs/step, 1 MI355X"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published peak
 COLD_BYTES = 2 << 30           # replica footprint that defeats the 256 MB last-level cache
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "pa_decode_layer_shape_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_decode_balanced.hip", "pa_attend.h",
                             "pa_device.h", "pa_internal.h", "pa_api.cpp")]
@@ -55,27 +55,40 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def decode_bytes(lens: np.ndarray, H: int, D: int, e: int, bs: int) -> int:
-    """Algorithmic bytes of one decode: K+V rows read, q read, out written,
-    the used block-table entries and the lengths."""
+def decode_bytes(lens: np.ndarray, H: int, D: int, e: int, bs: int, e_kv: int = 0) -> int:
+    """Algorithmic bytes of one decode: K+V rows read (e_kv bytes per element,
+    default e), q read, out written (e bytes), the used block-table entries and
+    the lengths; an 8-bit cache (e_kv == 1) also reads the K and V scale of
+    every (block, head) it visits."""
+    e_kv = e_kv or e
     lens = lens.astype(np.int64)
     S = len(lens)
     nb = -(-lens // bs)
-    return int(lens.sum() * H * D * 2 * e + 2 * S * H * D * e + 4 * nb.sum() + 4 * S)
+    scales = 2 * 4 * int(nb.sum()) * H if e_kv == 1 else 0
+    return int(lens.sum() * H * D * 2 * e_kv + 2 * S * H * D * e + 4 * nb.sum() + 4 * S + scales)
 
 
-def reshape_bytes(T: int, H: int, D: int, e: int) -> int:
-    """New K and V rows read and written, plus the slot numbers."""
-    return 4 * T * H * D * e + 4 * T
+def reshape_bytes(T: int, H: int, D: int, e: int, e_kv: int = 0) -> int:
+    """New K and V rows read (e bytes) and written (e_kv bytes), the slot
+    numbers, and for an 8-bit cache the scales of the written blocks."""
+    e_kv = e_kv or e
+    scales = 2 * 4 * T * H if e_kv == 1 else 0
+    return 2 * T * H * D * e + 2 * T * H * D * e_kv + 4 * T + scales
 
 
-def traffic_from_profile(digest: str):
-    """Counter-measured HBM bytes per pa_decode launch, if the committed
-    rocprofv3 record was taken on this exact kernel source; else None."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def profile_path(workload: str, kv: str) -> str:
+    tag = workload if kv == "native" else f"{workload}_fp8_{kv}"
+    return os.path.join(PROFILES, f"pa_decode_{tag}_traffic.txt")
+
+
+def traffic_from_profile(digest: str, path: str):
+    """Counter-measured HBM bytes per pa_decode launch, if a committed
+    rocprofv3 record exists for this workload and was taken on this exact
+    kernel source; else None."""
+    if not os.path.exists(path):
         return None
     rec = {}
-    with open(PROFILE_TRAFFIC) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -184,16 +197,23 @@ def calibration_copy(pa, dev) -> None:
 def cpu_baseline(w_host, k_new, v_new, slots, step_bytes: int, seconds: float) -> dict:
     """The float64 oracle, as it stands, on the host: one thread, same step."""
     from threadpoolctl import threadpool_limits
-    from oracle import decode_ref, reshape_and_cache_ref
+    from oracle import decode_fp8_ref, decode_ref, reshape_and_cache_fp8_ref, reshape_and_cache_ref
     torch.set_num_threads(1)
     lens = w_host["lens"]
+    fmt = w_host["fmt"]
     times = []
     t_end = time.perf_counter() + seconds
     with threadpool_limits(limits=1):
         while True:
             t0 = time.perf_counter()
-            kp, vp = reshape_and_cache_ref(w_host["k"], w_host["v"], k_new, v_new, slots, w_host["bs"])
-            decode_ref(w_host["q"], kp, vp, w_host["tables"], lens, w_host["scale"], w_host["bs"])
+            if fmt is None:
+                kp, vp = reshape_and_cache_ref(w_host["k"], w_host["v"], k_new, v_new, slots, w_host["bs"])
+                decode_ref(w_host["q"], kp, vp, w_host["tables"], lens, w_host["scale"], w_host["bs"])
+            else:
+                kp, vp = reshape_and_cache_fp8_ref(w_host["k"], w_host["v"], w_host["ks"], w_host["vs"],
+                                                   k_new, v_new, slots, w_host["bs"], fmt)
+                decode_fp8_ref(w_host["q"], kp, vp, w_host["ks"], w_host["vs"], w_host["tables"], lens,
+                               w_host["scale"], w_host["bs"], fmt)
             times.append(time.perf_counter() - t0)
             if time.perf_counter() >= t_end and len(times) >= 1:
                 break
@@ -213,6 +233,9 @@ def main() -> int:
                     choices=["layer_shape", "continuous_batching", "shared_prefix",
                              "long_context_b1", "long_context_b4", "tiny"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kv", default="native", choices=["native", "e4m3", "e5m2"],
+                    help="KV cache element format: the workload's own dtype, or an 8-bit cache "
+                         "(OCP E4M3 / E5M2 with per-block, per-head scales; q and out keep their dtype)")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--replicas", type=int, default=0, help="KV pool replicas (0 = enough for 2 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -230,10 +253,23 @@ def main() -> int:
     pa.load_library()
     stream = torch.cuda.current_stream(dev)
 
+    from paged_kv_cache_186_amd import workloads as W
     log(f"building workload {args.workload} (seed {args.seed})")
     w = build_workload(args.workload, args.seed, dev)
-    log(describe(w))
-    e = w.k_pool.element_size()
+    fp8 = args.kv != "native"
+    host = None
+    if fp8:
+        # the 8-bit cache holds the same values, quantized (input generation)
+        kc, vc, ks, vs = W.fp8_pools(w, args.kv)
+        if not args.no_cpu_baseline:
+            host = {"k": kc.cpu(), "v": vc.cpu(), "ks": ks.cpu(), "vs": vs.cpu()}
+        w.k_pool = w.v_pool = None
+        torch.cuda.empty_cache()
+    elif not args.no_cpu_baseline:
+        host = {"k": w.k_pool.cpu(), "v": w.v_pool.cpu()}
+    log(describe(w) + (f", KV cache fp8 {args.kv}" if fp8 else ""))
+    e = w.q.element_size()
+    e_kv = 1 if fp8 else e
     S, H, D, bs = w.num_seqs, w.num_heads, w.head_dim, w.block_size
     lens = w.context_lens_np()
     tables = w.block_tables().to(dev)
@@ -242,15 +278,15 @@ def main() -> int:
     # the token decoded this step is the last one of each context: its K/V are
     # (re)written into its slot, then attention runs over the whole context
     slots = [w.manager.slot_of(s, int(lens[i]) - 1) for i, s in enumerate(w.seq_ids)]
-    q, k_new, v_new = w.q, None, None
-    from paged_kv_cache_186_amd import workloads as W
+    q = w.q
     _, k_new, v_new = W.new_token_values(w, 0)
     slot_t = torch.tensor(slots, dtype=torch.int32, device=dev)
 
-    pool_bytes = 2 * w.k_pool.numel() * e
+    base = (kc, vc, ks, vs) if fp8 else (w.k_pool, w.v_pool)
+    pool_bytes = sum(t.numel() * t.element_size() for t in base)
     R = args.replicas or max(1, math.ceil(COLD_BYTES / pool_bytes))
     log(f"pool K+V {pool_bytes / 2**20:.0f} MiB; {R} replica(s) for cold-cache timing")
-    reps = [(w.k_pool, w.v_pool)] + [(w.k_pool.clone(), w.v_pool.clone()) for _ in range(R - 1)]
+    reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
     out = torch.empty_like(q)
     ws_bytes = pa.pa_decode_workspace_size(S, H, D, w.table_width, bs, args.partition)
     ws = pa.new_workspace(ws_bytes, dev)
@@ -258,13 +294,20 @@ def main() -> int:
     calibration_copy(pa, dev)
 
     def reshape(i):
-        kp, vp = reps[i % R]
-        pa.pa_reshape_and_cache(kp, vp, k_new, v_new, slot_t)
+        if fp8:
+            pa.pa_reshape_and_cache_fp8(*reps[i % R], k_new, v_new, slot_t)
+        else:
+            pa.pa_reshape_and_cache(*reps[i % R], k_new, v_new, slot_t)
 
     def decode(i):
-        kp, vp = reps[i % R]
-        pa.pa_decode(out, q, kp, vp, tables, clens, w.scale, bs,
-                     partition_size=args.partition, workspace=ws)
+        if fp8:
+            kp, vp, kss, vss = reps[i % R]
+            pa.pa_decode_fp8(out, q, kp, vp, kss, vss, tables, clens, w.scale, bs,
+                             partition_size=args.partition, workspace=ws)
+        else:
+            kp, vp = reps[i % R]
+            pa.pa_decode(out, q, kp, vp, tables, clens, w.scale, bs,
+                         partition_size=args.partition, workspace=ws)
 
     # eager warmup, then HIP graphs: R steps (one per replica) captured once and
     # replayed, so no host-side launch cost sits inside the timed region
@@ -288,13 +331,13 @@ def main() -> int:
     warm_ms = time_graph(warm_graph, n_rep, stream) / R
     n_steps = n_rep * R
 
-    b_dec = decode_bytes(lens, H, D, e, bs)
-    b_res = reshape_bytes(S, H, D, e)
+    b_dec = decode_bytes(lens, H, D, e, bs, e_kv)
+    b_res = reshape_bytes(S, H, D, e, e_kv)
     step_s = step_ms * 1e-3
     value = (b_dec + b_res) / step_s / 1e9
     dec_gbs = b_dec / (dec_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
-    traffic = traffic_from_profile(digest)
+    traffic = traffic_from_profile(digest, profile_path(args.workload, args.kv))
 
     result = {
         "metric": METRIC,
@@ -307,13 +350,15 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {2: "f16" if w.dtype == torch.float16 else "bf16", 4: "f32"}[e],
+        "dtype": {2: "f16" if w.dtype == torch.float16 else "bf16", 4: "f32"}[e]
+                 + (f" (KV cache fp8 {args.kv}, per-block scales)" if fp8 else ""),
         "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block layout)",
         "config": {
             "workload": describe(w),
             "seed": args.seed,
             "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": bs,
             "context_tokens": int(lens.sum()),
+            "kv_cache": "native" if not fp8 else f"fp8 {args.kv} + fp32 scale per (block, head)",
             "split": ("balanced (partition_size 0)" if args.partition == 0
                       else f"partitions of {args.partition} tokens"),
             "accumulate": "f32",
@@ -338,8 +383,8 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s on one host thread")
-        host = {"q": q.cpu(), "k": w.k_pool.cpu(), "v": w.v_pool.cpu(),
-                "tables": w.block_tables_np(), "lens": lens, "scale": w.scale, "bs": bs}
+        host.update({"q": q.cpu(), "tables": w.block_tables_np(), "lens": lens, "scale": w.scale,
+                     "bs": bs, "fmt": args.kv if fp8 else None})
         result["cpu_baseline"] = cpu_baseline(host, k_new.cpu(), v_new.cpu(), slots,
                                               b_dec + b_res, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -33,8 +33,9 @@
  *   context_lens      int32 [num_seqs]
  *   slot_mapping      int32 [num_tokens]; slot = physical_block*block_size + row
  *   block_mapping     int32 [num_pairs][2] = {src, dst}
- * One element dtype covers q, k_pool, v_pool, out, k_new and v_new.  Keys and
- * values have as many heads as queries.  head_dim is 64 or 128; block_size is
+ * One element dtype covers q, k_pool, v_pool, out, k_new and v_new (the *_fp8
+ * calls below: an 8-bit pool with per-block scales).  Keys and values have as
+ * many heads as queries.  head_dim is 64 or 128; block_size is
  * 16 or 32.  Every tensor pointer must be 16-byte aligned.
  *
  * Errors: arguments are validated on the host before anything is launched; a
@@ -56,7 +57,14 @@ extern "C" {
 typedef enum pa_dtype {
   PA_DTYPE_F32 = 0,
   PA_DTYPE_F16 = 1,
-  PA_DTYPE_BF16 = 2
+  PA_DTYPE_BF16 = 2,
+  /* 8-bit KV-cache element formats (the *_fp8 calls only), OCP 8-bit floats:
+   * E4M3 = sign, 4 exponent bits (bias 7), 3 mantissa bits, no infinities,
+   * S.1111.111 = NaN, largest finite 448; E5M2 = sign, 5 exponent bits
+   * (bias 15), 2 mantissa bits, IEEE infinities and NaNs, largest finite
+   * 57344.  Both have subnormals. */
+  PA_DTYPE_FP8_E4M3 = 3,
+  PA_DTYPE_FP8_E5M2 = 4
 } pa_dtype_t;
 
 typedef enum pa_status {
@@ -166,6 +174,72 @@ pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapp
                            int32_t num_pairs, int32_t num_heads, int32_t head_dim,
                            int32_t block_size, int32_t num_blocks, pa_dtype_t dtype,
                            void* stream);
+
+/*
+ * ---- 8-bit KV cache --------------------------------------------------------
+ * The pages name quantization only as future work (page "mlx-paged-attention:
+ * Bringing vLLM-level High Throughput Inference to Apple Silicon", future
+ * plans); the scheme below is this library's reading.  The pools hold one
+ * byte per element in kv_dtype (PA_DTYPE_FP8_E4M3 or PA_DTYPE_FP8_E5M2); each
+ * (physical block, head) has one fp32 scale for K and one for V:
+ *   k_scales, v_scales  float [num_blocks][num_heads], caller-owned device
+ *   memory, 4-byte aligned; a cached code c of block b, head h stands for
+ *   scale[b][h] * value(c).  Scales are chosen by the caller (for instance
+ *   when it takes a fresh block) and must be finite and positive for every
+ *   block in use; these calls never change them (pa_copy_blocks_fp8 copies
+ *   them along with the blocks).
+ * q, out, k_new, v_new keep a 16-bit or 32-bit dtype; the pool layout is the
+ * one above with 1-byte elements.
+ */
+
+/*
+ * pa_decode over an 8-bit cache: as pa_decode, with each K element read as
+ * k_scales[b][h] * value(code) and each V element as v_scales[b][h] *
+ * value(code).  q_dtype (PA_DTYPE_F16 or PA_DTYPE_BF16) is the dtype of q and
+ * out; arithmetic is fp32 as in pa_decode (scores sk*<q, k_code>, V weights
+ * p*sv).  Workspace: pa_decode_workspace_size() with the same sizes and
+ * partition_size, same contract.  Tensor pointers 16-byte aligned, except
+ * block_tables, context_lens and the scales (4 bytes).  Returns
+ * PA_ERR_UNSUPPORTED for other dtype pairs.
+ */
+pa_status_t pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          float scale, int32_t block_size,
+                          int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                          int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t partition_size, pa_dtype_t q_dtype, pa_dtype_t kv_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_reshape_and_cache into an 8-bit cache: for i < num_tokens with
+ * slot = slot_mapping[i], b = slot / block_size, r = slot % block_size and
+ * every head h and element d,
+ *   k_pool[b][h][r][d] = Q(k_new[i][h][d] / k_scales[b][h])   (likewise v)
+ * where the division is fp32 (correctly rounded) and Q rounds to the nearest
+ * kv_dtype value, ties to the even code, saturating beyond the largest finite
+ * value (infinities included) and mapping NaN to the code 0x7F; the sign of
+ * the quotient is kept (-0 gives 0x80).  new_dtype (F32, F16 or BF16) is the
+ * dtype of k_new / v_new.  Slots as in pa_reshape_and_cache (negative or past
+ * the pool: no write).
+ */
+pa_status_t pa_reshape_and_cache_fp8(void* k_pool, void* v_pool,
+                                     const float* k_scales, const float* v_scales,
+                                     const void* k_new, const void* v_new,
+                                     const int32_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, pa_dtype_t new_dtype,
+                                     pa_dtype_t kv_dtype, void* stream);
+
+/*
+ * pa_copy_blocks for an 8-bit cache: copies the blocks' codes and their
+ * per-head K and V scales (k_scales[dst][:] = k_scales[src][:], likewise v).
+ * Same pair rules and preconditions as pa_copy_blocks.
+ */
+pa_status_t pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                               const int32_t* block_mapping, int32_t num_pairs,
+                               int32_t num_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, pa_dtype_t kv_dtype, void* stream);
 
 #ifdef __cplusplus
 }

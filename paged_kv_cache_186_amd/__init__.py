@@ -12,9 +12,12 @@ from .binding import (  # noqa: F401
     load_library,
     new_workspace,
     pa_copy_blocks,
+    pa_copy_blocks_fp8,
     pa_decode,
+    pa_decode_fp8,
     pa_decode_workspace_size,
     pa_reshape_and_cache,
+    pa_reshape_and_cache_fp8,
     status_string,
 )
 from .block_manager import BlockManager  # noqa: F401

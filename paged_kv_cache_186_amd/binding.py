@@ -27,6 +27,8 @@ HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__fil
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+# 8-bit KV-cache element formats (OCP E4M3 / E5M2), held in torch's float8 dtypes
+FP8_CODES = {torch.float8_e4m3fn: 3, torch.float8_e5m2: 4}
 
 _c_int, _c_size, _c_float, _c_void = ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
 
@@ -38,6 +40,10 @@ _SIGNATURES = {
                   + [_c_void, _c_size, _c_void]),
     "pa_reshape_and_cache": (_c_int, [_c_void] * 5 + [_c_int] * 5 + [_c_int, _c_void]),
     "pa_copy_blocks": (_c_int, [_c_void] * 3 + [_c_int] * 5 + [_c_int, _c_void]),
+    "pa_decode_fp8": (_c_int, [_c_void] * 8 + [_c_float] + [_c_int] * 6 + [_c_int] * 3
+                      + [_c_void, _c_size, _c_void]),
+    "pa_reshape_and_cache_fp8": (_c_int, [_c_void] * 7 + [_c_int] * 5 + [_c_int, _c_int, _c_void]),
+    "pa_copy_blocks_fp8": (_c_int, [_c_void] * 5 + [_c_int] * 5 + [_c_int, _c_void]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -128,16 +134,9 @@ def _cached_workspace(device, stream_handle: int, rows: int, need: int) -> torch
     return ws
 
 
-def pa_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
-              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-              block_size: int, *, partition_size: int = 0,
-              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Paged decode attention; writes and returns ``out`` ([S, H, D], q's dtype).
-
-    ``workspace`` (optional) must follow the C contract: zero-filled when first
-    used (``new_workspace``); by default a cached zero-filled one is used.
-    """
-    lib = load_library()
+def _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, block_size, partition_size,
+                 workspace, stream):
+    """Shared checks of pa_decode / pa_decode_fp8; returns (S, H, D, W, ws_ptr, ws_bytes, stream)."""
     for t, n in ((out, "out"), (q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"),
                  (block_tables, "block_tables"), (context_lens, "context_lens")):
         _dev(t, n)
@@ -147,8 +146,7 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
     _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     _require(k_pool.dim() == 4 and k_pool.shape[1:] == (H, block_size, D),
              "k_pool must be [num_blocks, num_heads, block_size, head_dim]")
-    _require(v_pool.shape == k_pool.shape, "v_pool must match k_pool")
-    _require(k_pool.dtype == q.dtype and v_pool.dtype == q.dtype, "q, k_pool, v_pool share one dtype")
+    _require(v_pool.shape == k_pool.shape and v_pool.dtype == k_pool.dtype, "v_pool must match k_pool")
     _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
              and block_tables.shape[0] == S, "block_tables must be int32 [num_seqs, max_blocks]")
     _require(context_lens.dtype == torch.int32 and context_lens.shape == (S,),
@@ -162,12 +160,59 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
             workspace = _cached_workspace(q.device, handle, S * H, need)
         _dev(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return S, H, D, W, ws_ptr, ws_bytes, handle
+
+
+def pa_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+              block_size: int, *, partition_size: int = 0,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Paged decode attention; writes and returns ``out`` ([S, H, D], q's dtype).
+
+    ``workspace`` (optional) must follow the C contract: zero-filled when first
+    used (``new_workspace``); by default a cached zero-filled one is used.
+    """
+    lib = load_library()
+    S, H, D, W, ws_ptr, ws_bytes, handle = _decode_args(
+        out, q, k_pool, v_pool, block_tables, context_lens, block_size, partition_size,
+        workspace, stream)
+    _require(k_pool.dtype == q.dtype, "q, k_pool, v_pool share one dtype")
     with torch.cuda.device(q.device):
         st = lib.pa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                            block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
                            block_size, S, H, D, k_pool.shape[0], W, partition_size,
                            DTYPE_CODES[q.dtype], ws_ptr, ws_bytes, handle)
     _check("pa_decode", st)
+    return out
+
+
+def _scales(k_scales, v_scales, N, H):
+    for t, n in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        _dev(t, n)
+        _require(t.dtype == torch.float32 and t.shape == (N, H),
+                 f"{n} must be float32 [num_blocks, num_heads]")
+
+
+def pa_decode_fp8(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                  k_scales: torch.Tensor, v_scales: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, scale: float, block_size: int, *,
+                  partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Paged decode over an 8-bit cache (pools in torch.float8_e4m3fn or
+    torch.float8_e5m2, per-(block, head) float32 scales); q / out fp16 or bf16."""
+    lib = load_library()
+    S, H, D, W, ws_ptr, ws_bytes, handle = _decode_args(
+        out, q, k_pool, v_pool, block_tables, context_lens, block_size, partition_size,
+        workspace, stream)
+    _require(k_pool.dtype in FP8_CODES, "k_pool / v_pool must be float8_e4m3fn or float8_e5m2")
+    _scales(k_scales, v_scales, k_pool.shape[0], H)
+    with torch.cuda.device(q.device):
+        st = lib.pa_decode_fp8(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                               k_scales.data_ptr(), v_scales.data_ptr(), block_tables.data_ptr(),
+                               context_lens.data_ptr(), float(scale), block_size, S, H, D,
+                               k_pool.shape[0], W, partition_size, DTYPE_CODES[q.dtype],
+                               FP8_CODES[k_pool.dtype], ws_ptr, ws_bytes, handle)
+    _check("pa_decode_fp8", st)
     return out
 
 
@@ -210,3 +255,49 @@ def pa_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, block_mapping: to
                                 block_mapping.shape[0], H, D, BS, N, DTYPE_CODES[k_pool.dtype],
                                 _stream_handle(k_pool.device, stream))
     _check("pa_copy_blocks", st)
+
+
+def pa_reshape_and_cache_fp8(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scales: torch.Tensor,
+                             v_scales: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                             slot_mapping: torch.Tensor, *, stream=None) -> None:
+    """Quantize new tokens' K/V ([T, H, D], fp32/fp16/bf16) with their blocks'
+    scales and write the codes into the 8-bit pools."""
+    lib = load_library()
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (k_new, "k_new"), (v_new, "v_new"),
+                 (slot_mapping, "slot_mapping")):
+        _dev(t, n)
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape and v_pool.dtype == k_pool.dtype
+             and k_pool.dtype in FP8_CODES, "pools must be 8-bit [N, H, BS, D] of one format")
+    N, H, BS, D = k_pool.shape
+    _scales(k_scales, v_scales, N, H)
+    _require(k_new.dim() == 3 and k_new.shape[1:] == (H, D) and v_new.shape == k_new.shape
+             and v_new.dtype == k_new.dtype and k_new.dtype in DTYPE_CODES,
+             "k_new/v_new must be [num_tokens, num_heads, head_dim] of one 16/32-bit dtype")
+    _require(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (k_new.shape[0],),
+             "slot_mapping must be int32 [num_tokens]")
+    with torch.cuda.device(k_pool.device):
+        st = lib.pa_reshape_and_cache_fp8(
+            k_pool.data_ptr(), v_pool.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(),
+            k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), k_new.shape[0], H, D, BS,
+            N, DTYPE_CODES[k_new.dtype], FP8_CODES[k_pool.dtype], _stream_handle(k_pool.device, stream))
+    _check("pa_reshape_and_cache_fp8", st)
+
+
+def pa_copy_blocks_fp8(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scales: torch.Tensor,
+                       v_scales: torch.Tensor, block_mapping: torch.Tensor, *, stream=None) -> None:
+    """Copy whole 8-bit blocks and their scales src -> dst; ``block_mapping`` int32 [n, 2]."""
+    lib = load_library()
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (block_mapping, "block_mapping")):
+        _dev(t, n)
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape and v_pool.dtype == k_pool.dtype
+             and k_pool.dtype in FP8_CODES, "pools must be 8-bit [N, H, BS, D] of one format")
+    N, H, BS, D = k_pool.shape
+    _scales(k_scales, v_scales, N, H)
+    _require(block_mapping.dtype == torch.int32 and block_mapping.dim() == 2
+             and block_mapping.shape[1] == 2, "block_mapping must be int32 [n, 2]")
+    with torch.cuda.device(k_pool.device):
+        st = lib.pa_copy_blocks_fp8(k_pool.data_ptr(), v_pool.data_ptr(), k_scales.data_ptr(),
+                                    v_scales.data_ptr(), block_mapping.data_ptr(),
+                                    block_mapping.shape[0], H, D, BS, N, FP8_CODES[k_pool.dtype],
+                                    _stream_handle(k_pool.device, stream))
+    _check("pa_copy_blocks_fp8", st)

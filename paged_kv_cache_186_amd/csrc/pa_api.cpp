@@ -12,8 +12,9 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
+// Bytes of one element of a 16/32-bit dtype (0 for anything else).
 int elem_bytes(pa_dtype_t dtype) {
   switch (dtype) {
     case PA_DTYPE_F32:
@@ -25,6 +26,8 @@ int elem_bytes(pa_dtype_t dtype) {
       return 0;
   }
 }
+
+bool is_fp8(pa_dtype_t dtype) { return dtype == PA_DTYPE_FP8_E4M3 || dtype == PA_DTYPE_FP8_E5M2; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -95,6 +98,86 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
   return p;
 }
 
+// Shared by pa_decode (kv_dtype == dtype, no scales) and pa_decode_fp8; the
+// caller has checked the dtype pair.
+pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                        const float* k_scales, const float* v_scales,
+                        const int32_t* block_tables, const int32_t* context_lens, float scale,
+                        int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t partition_size,
+                        pa_dtype_t dtype, pa_dtype_t kv_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const DecodePlan plan =
+      plan_decode(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size);
+  if (plan.status != PA_OK) return plan.status;
+  if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (is_fp8(kv_dtype) && (!k_scales || !v_scales || !aligned(k_scales, 4) || !aligned(v_scales, 4)))
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  if (plan.ws.total > 0) {
+    if (!workspace || workspace_bytes < plan.ws.total) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+  }
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.block_size = block_size;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.dtype = dtype;
+  a.kv_dtype = kv_dtype;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.mode = plan.mode;
+  a.partition_blocks = plan.part_blocks;
+  a.max_partitions = plan.max_parts;
+  a.workgroups = plan.workgroups;
+  if (plan.ws.total > 0) {
+    char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(ws + plan.ws.counter_offset);
+    a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
+    a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
+  }
+  const hipError_t e = plan.mode == pa::DecodeMode::kBalanced
+                           ? pa::launch_decode_balanced(a, static_cast<hipStream_t>(stream))
+                           : pa::launch_decode_partitioned(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// Shared by pa_copy_blocks (no scales) and pa_copy_blocks_fp8; e = element bytes.
+pa_status_t copy_impl(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                      const int32_t* block_mapping, int32_t num_pairs, int32_t num_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, int e,
+                      void* stream) {
+  if (num_pairs < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  const size_t block_bytes = static_cast<size_t>(num_heads) * block_size * head_dim * e;
+  const size_t chunks = (block_bytes + pa::kCopyChunkBytes - 1) / pa::kCopyChunkBytes;
+  if (chunks * static_cast<size_t>(num_pairs) > static_cast<size_t>(INT_MAX))
+    return PA_ERR_INVALID_ARG;
+  const hipError_t err =
+      pa::launch_copy_blocks(k_pool, v_pool, k_scales, v_scales, block_mapping, num_pairs,
+                             block_bytes, num_blocks, num_heads, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,50 +215,24 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
                       int32_t num_blocks, int32_t max_blocks_per_seq, int32_t partition_size,
                       pa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
-  const DecodePlan plan =
-      plan_decode(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size);
-  if (plan.status != PA_OK) return plan.status;
-  if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
-    return PA_ERR_INVALID_ARG;
-  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4))
-    return PA_ERR_INVALID_ARG;
-  if (plan.ws.total > 0) {
-    if (!workspace || workspace_bytes < plan.ws.total) return PA_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
-  }
+  return decode_impl(out, q, k_pool, v_pool, nullptr, nullptr, block_tables, context_lens, scale,
+                     block_size, num_seqs, num_heads, head_dim, num_blocks, max_blocks_per_seq,
+                     partition_size, dtype, dtype, workspace, workspace_bytes, stream);
+}
 
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.scale = scale;
-  a.block_size = block_size;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.head_dim = head_dim;
-  a.num_blocks = num_blocks;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.dtype = dtype;
-  a.mode = plan.mode;
-  a.partition_blocks = plan.part_blocks;
-  a.max_partitions = plan.max_parts;
-  a.workgroups = plan.workgroups;
-  if (plan.ws.total > 0) {
-    char* ws = static_cast<char*>(workspace);
-    a.counters = reinterpret_cast<uint32_t*>(ws + plan.ws.counter_offset);
-    a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
-    a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
-  }
-  const hipError_t e = plan.mode == pa::DecodeMode::kBalanced
-                           ? pa::launch_decode_balanced(a, static_cast<hipStream_t>(stream))
-                           : pa::launch_decode_partitioned(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+pa_status_t pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale,
+                          int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                          int32_t head_dim, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t partition_size, pa_dtype_t q_dtype, pa_dtype_t kv_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if ((q_dtype != PA_DTYPE_F16 && q_dtype != PA_DTYPE_BF16) || !is_fp8(kv_dtype))
+    return PA_ERR_UNSUPPORTED;
+  return decode_impl(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens,
+                     scale, block_size, num_seqs, num_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, partition_size, q_dtype, kv_dtype, workspace,
+                     workspace_bytes, stream);
 }
 
 pa_status_t pa_reshape_and_cache(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
@@ -204,19 +261,43 @@ pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapp
                            void* stream) {
   const int e = elem_bytes(dtype);
   if (e == 0 || !supported_shape(head_dim, block_size)) return PA_ERR_UNSUPPORTED;
-  if (num_pairs < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
-  if (num_pairs == 0) return PA_OK;
-  if (!k_pool || !v_pool || !block_mapping) return PA_ERR_INVALID_ARG;
-  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_mapping, 4))
+  return copy_impl(k_pool, v_pool, nullptr, nullptr, block_mapping, num_pairs, num_heads,
+                   head_dim, block_size, num_blocks, e, stream);
+}
+
+pa_status_t pa_reshape_and_cache_fp8(void* k_pool, void* v_pool, const float* k_scales,
+                                     const float* v_scales, const void* k_new, const void* v_new,
+                                     const int32_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, pa_dtype_t new_dtype,
+                                     pa_dtype_t kv_dtype, void* stream) {
+  const int e = elem_bytes(new_dtype);
+  if (e == 0 || !is_fp8(kv_dtype) || !supported_shape(head_dim, block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (num_heads > INT_MAX / (head_dim * e)) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_scales || !v_scales || !k_new || !v_new || !slot_mapping)
     return PA_ERR_INVALID_ARG;
-  const size_t block_bytes = static_cast<size_t>(num_heads) * block_size * head_dim * e;
-  const size_t chunks = (block_bytes + pa::kCopyChunkBytes - 1) / pa::kCopyChunkBytes;
-  if (chunks * static_cast<size_t>(num_pairs) > static_cast<size_t>(INT_MAX))
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(slot_mapping, 4))
     return PA_ERR_INVALID_ARG;
-  const hipError_t err = pa::launch_copy_blocks(k_pool, v_pool, block_mapping, num_pairs,
-                                                block_bytes, num_blocks,
-                                                static_cast<hipStream_t>(stream));
+  pa::ReshapeFp8Args a{k_pool,    v_pool,     k_scales,   v_scales,   k_new,
+                       v_new,     slot_mapping, num_tokens, num_heads, head_dim,
+                       block_size, num_blocks, new_dtype,  kv_dtype};
+  const hipError_t err = pa::launch_reshape_and_cache_fp8(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status_t pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                               const int32_t* block_mapping, int32_t num_pairs, int32_t num_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               pa_dtype_t kv_dtype, void* stream) {
+  if (!is_fp8(kv_dtype) || !supported_shape(head_dim, block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_pairs > 0 && (!k_scales || !v_scales || !aligned(k_scales, 4) || !aligned(v_scales, 4)))
+    return PA_ERR_INVALID_ARG;
+  return copy_impl(k_pool, v_pool, k_scales, v_scales, block_mapping, num_pairs, num_heads,
+                   head_dim, block_size, num_blocks, 1, stream);
 }
 
 }  // extern "C"

@@ -26,13 +26,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Online-softmax update of one lane group with one loaded tile.  kMasked
 // handles the last, partly filled block: rows at or past L get weight exactly
-// 0 and their V values are replaced by 0 (they may hold NaN).  All 64 lanes
-// must be active (the DPP sums read every lane).
+// 0 and their V values are replaced by 0 (they may hold NaN).  For a scaled
+// (8-bit) KV type, sk and sv are the tile's K and V scales: scores are
+// sk * <q, k_code> and V rows enter as sv * v_code (sv is folded into the
+// weight of the V sum, not into l).  All 64 lanes must be active (the DPP
+// sums read every lane).
 template <typename T, int D, int BS, bool kMasked>
 __device__ __forceinline__ void attend_tile(const u32x4 (&kv)[Tile<T, D, BS>::kLoads],
                                             const u32x4 (&vv)[Tile<T, D, BS>::kLoads],
                                             const float (&qf)[T::kElems], float& m, float& l,
-                                            float (&acc)[T::kElems], int tok0, int L) {
+                                            float (&acc)[T::kElems], int tok0, int L,
+                                            float sk = 1.f, float sv = 1.f) {
   using C = Tile<T, D, BS>;
   float sc[C::kLoads];
 #pragma unroll
@@ -43,6 +47,7 @@ __device__ __forceinline__ void attend_tile(const u32x4 (&kv)[Tile<T, D, BS>::kL
 #pragma unroll
     for (int e = 0; e < T::kElems; ++e) d = fmaf(qf[e], kf[e], d);
     sc[i] = group_sum<C::kLanesPerRow>(d);
+    if constexpr (T::kScaled) sc[i] *= sk;
   }
 
   bool ok[C::kLoads];
@@ -67,11 +72,45 @@ __device__ __forceinline__ void attend_tile(const u32x4 (&kv)[Tile<T, D, BS>::kL
     float vf[T::kElems];
     T::unpack(vv[i], vf);
     l += p;
+    float pv = p;
+    if constexpr (T::kScaled) pv *= sv;
 #pragma unroll
-    for (int e = 0; e < T::kElems; ++e) acc[e] = fmaf(p, ok[i] ? vf[e] : 0.f, acc[e]);
+    for (int e = 0; e < T::kElems; ++e) acc[e] = fmaf(pv, ok[i] ? vf[e] : 0.f, acc[e]);
   }
   m = mn;
 }
+
+// The query / output side of a lane: E = KT::kElems consecutive elements of a
+// row, stored as QT — one 16-byte vector when QT and KT have the same width,
+// two for an 8-bit KV cache read with a 16-bit query.
+template <typename QT, typename KT>
+struct QSlice {
+  static constexpr int kElems = KT::kElems;
+  static constexpr int kBytes = kElems * static_cast<int>(sizeof(typename QT::storage));
+  static constexpr int kVecs = kBytes / kVecBytes;
+  static_assert(kVecs * kVecBytes == kBytes && kVecs * QT::kElems == kElems, "whole vectors");
+
+  // fp32 values of the lane's slice of one row (row points at element 0)
+  static __device__ __forceinline__ void load(const typename QT::storage* row, int col, float* f) {
+    const char* p = reinterpret_cast<const char*>(row) + col * kBytes;
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) QT::unpack(load16(p + i * kVecBytes), f + i * QT::kElems);
+  }
+  // round the lane's slice to QT and store it
+  static __device__ __forceinline__ void store(typename QT::storage* row, int col, const float* f) {
+    char* p = reinterpret_cast<char*>(row) + col * kBytes;
+#pragma unroll
+    for (int i = 0; i < kVecs; ++i) {
+      typename QT::storage s[QT::kElems];
+#pragma unroll
+      for (int e = 0; e < QT::kElems; ++e) s[e] = QT::pack(f[i * QT::kElems + e]);
+      u32x4 w;
+      static_assert(sizeof(s) == sizeof(w), "16-byte slice");
+      __builtin_memcpy(&w, s, sizeof(w));
+      store16(p + i * kVecBytes, w);
+    }
+  }
+};
 
 // Workspace accesses shared between workgroups on different XCDs use
 // agent-scope relaxed atomics: on gfx950 these are L2-bypassing (sc1) loads

@@ -5,6 +5,7 @@
 
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pagedattn.h"
 
 namespace pa {
 namespace {
@@ -43,14 +44,66 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
   }
 }
 
+// The same slot write for an 8-bit cache: every element of the new token's
+// K/V row (storage IT) becomes the code of x / scale[blk][head] (an fp32
+// division, correctly rounded), rounded to the nearest value with ties to
+// even and saturated to the largest finite value (QFn).  One thread makes 16
+// codes — one 16-byte store — from 16 input elements.  The quantization is
+// this library's reading: the pages name quantization only as future work
+// (page "mlx-paged-attention: Bringing vLLM-level High Throughput Inference
+// to Apple Silicon", future plans).
+template <typename IT, uint32_t (*QFn)(float)>
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, const float* __restrict__ k_scales,
+    const float* __restrict__ v_scales, const typename IT::storage* __restrict__ k_new,
+    const typename IT::storage* __restrict__ v_new, const int32_t* __restrict__ slot_mapping,
+    int num_heads, int head_dim, int block_size, long long num_slots) {
+  constexpr int kCodes = 16;                        // codes per thread step
+  constexpr int kInVecs = kCodes / IT::kElems;      // 16-byte input vectors per step
+  const int t = blockIdx.x;
+  const int slot = slot_mapping[t];
+  if (slot < 0 || static_cast<long long>(slot) >= num_slots) return;
+  const int blk = slot / block_size;
+  const int r = slot % block_size;
+  const int vecs_per_row = head_dim / kCodes;
+  const int total = num_heads * vecs_per_row;
+  for (int i = threadIdx.x; i < total; i += kThreads) {
+    const int hh = i / vecs_per_row;
+    const int c = i % vecs_per_row;
+    const size_t src = (static_cast<size_t>(t) * num_heads + hh) * head_dim + c * kCodes;
+    const size_t dst = ((static_cast<size_t>(blk) * num_heads + hh) * block_size + r) * head_dim + c * kCodes;
+    const float sk = k_scales[static_cast<size_t>(blk) * num_heads + hh];
+    const float sv = v_scales[static_cast<size_t>(blk) * num_heads + hh];
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const typename IT::storage* in = (kv ? v_new : k_new) + src;
+      const float sc = kv ? sv : sk;
+      float x[kCodes];
+#pragma unroll
+      for (int u = 0; u < kInVecs; ++u) IT::unpack(load16(in + u * IT::kElems), x + u * IT::kElems);
+      u32x4 w;
+      uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) word |= QFn(x[4 * q + b] / sc) << (8 * b);
+        wp[q] = word;
+      }
+      store16((kv ? v_pool : k_pool) + dst, w);
+    }
+  }
+}
+
 // Copy-on-write copy: pool[dst] = pool[src] for every {src, dst} pair, for both
-// pools (blockIdx.y selects K or V).  Grid x enumerates (pair, 16 KiB chunk).
-// Source: page "mlx-paged-attention: Bringing vLLM-level High Throughput
-// Inference to Apple Silicon", core feature 2.  Pairs naming an id outside the
-// pool are skipped.
+// pools (blockIdx.y selects K or V), and for an 8-bit cache the block's
+// per-head scales too.  Grid x enumerates (pair, 16 KiB chunk).  Source: page
+// "mlx-paged-attention: Bringing vLLM-level High Throughput Inference to Apple
+// Silicon", core feature 2.  Pairs naming an id outside the pool are skipped.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
-    char* __restrict__ k_pool, char* __restrict__ v_pool, const int32_t* __restrict__ block_mapping,
-    size_t block_bytes, int chunks_per_block, int num_blocks) {
+    char* __restrict__ k_pool, char* __restrict__ v_pool, float* __restrict__ k_scales,
+    float* __restrict__ v_scales, const int32_t* __restrict__ block_mapping, size_t block_bytes,
+    int chunks_per_block, int num_blocks, int num_heads) {
   const int pair = blockIdx.x / chunks_per_block;
   const int chunk = blockIdx.x % chunks_per_block;
   char* pool = blockIdx.y ? v_pool : k_pool;
@@ -59,6 +112,10 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   if (static_cast<unsigned>(src) >= static_cast<unsigned>(num_blocks) ||
       static_cast<unsigned>(dst) >= static_cast<unsigned>(num_blocks))
     return;
+  float* scales = blockIdx.y ? v_scales : k_scales;
+  if (scales != nullptr && chunk == 0)
+    for (int i = threadIdx.x; i < num_heads; i += kThreads)
+      scales[static_cast<size_t>(dst) * num_heads + i] = scales[static_cast<size_t>(src) * num_heads + i];
   const char* from = pool + static_cast<size_t>(src) * block_bytes;
   char* to = pool + static_cast<size_t>(dst) * block_bytes;
   const size_t base = static_cast<size_t>(chunk) * kCopyChunk + threadIdx.x * kVecBytes;
@@ -89,13 +146,46 @@ hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_ne
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, int num_pairs,
-                              size_t block_bytes, int num_blocks, hipStream_t stream) {
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                              const int32_t* block_mapping, int num_pairs, size_t block_bytes,
+                              int num_blocks, int num_heads, hipStream_t stream) {
   const int chunks = static_cast<int>((block_bytes + kCopyChunk - 1) / kCopyChunk);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs * chunks, 2), dim3(kThreads), 0, stream,
-                     static_cast<char*>(k_pool), static_cast<char*>(v_pool), block_mapping,
-                     block_bytes, chunks, num_blocks);
+                     static_cast<char*>(k_pool), static_cast<char*>(v_pool), k_scales, v_scales,
+                     block_mapping, block_bytes, chunks, num_blocks, num_heads);
   return hipGetLastError();
+}
+
+namespace {
+template <typename IT>
+hipError_t run_reshape_fp8(const ReshapeFp8Args& a, hipStream_t stream) {
+  using S = typename IT::storage;
+  const long long slots = static_cast<long long>(a.num_blocks) * a.block_size;
+  if (a.kv_dtype == PA_DTYPE_FP8_E4M3)
+    hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<IT, quantize_e4m3>), dim3(a.num_tokens),
+                       dim3(kThreads), 0, stream, static_cast<uint8_t*>(a.k_pool),
+                       static_cast<uint8_t*>(a.v_pool), a.k_scales, a.v_scales,
+                       static_cast<const S*>(a.k_new), static_cast<const S*>(a.v_new), a.slot_mapping,
+                       a.num_heads, a.head_dim, a.block_size, slots);
+  else
+    hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<IT, quantize_e5m2>), dim3(a.num_tokens),
+                       dim3(kThreads), 0, stream, static_cast<uint8_t*>(a.k_pool),
+                       static_cast<uint8_t*>(a.v_pool), a.k_scales, a.v_scales,
+                       static_cast<const S*>(a.k_new), static_cast<const S*>(a.v_new), a.slot_mapping,
+                       a.num_heads, a.head_dim, a.block_size, slots);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_reshape_and_cache_fp8(const ReshapeFp8Args& a, hipStream_t stream) {
+  switch (a.in_dtype) {
+    case PA_DTYPE_F32:
+      return run_reshape_fp8<F32>(a, stream);
+    case PA_DTYPE_F16:
+      return run_reshape_fp8<F16>(a, stream);
+    default:
+      return run_reshape_fp8<BF16>(a, stream);
+  }
 }
 
 }  // namespace pa

@@ -59,11 +59,13 @@ namespace {
 constexpr int kWavesPerGroup = PA_WAVES_PER_WG;  // waves per workgroup
 constexpr int kTilesPerStage = PA_TILES_PER_STAGE;  // G: tiles per stage (2*G in flight per wave)
 
-// G tiles' worth of K/V registers plus which logical block each one is.
+// G tiles' worth of K/V registers plus which logical block each one is (and,
+// for an 8-bit cache, the tile's K and V scales).
 template <typename T, int D, int BS, int G>
 struct Stage {
   u32x4 k[G][Tile<T, D, BS>::kLoads];
   u32x4 v[G][Tile<T, D, BS>::kLoads];
+  float sk[G], sv[G];
   int block[G];  // logical block index, or -1 when this slot holds no tile
 };
 
@@ -158,16 +160,19 @@ __device__ __forceinline__ void merge_partials(typename T::storage* __restrict__
 
 // Grid: (head, partition, sequence); NW waves per workgroup.  Workgroup
 // (h, p, s) covers blocks [p*PB, min((p+1)*PB, nblk)) of sequence s; wave w
-// takes blocks w, w+NW, ... of that range.
-template <typename T, int D, int BS, int NW, int G>
+// takes blocks w, w+NW, ... of that range.  QT: query / output storage; KT:
+// K/V cache storage (QT itself, or an 8-bit type scaled per (block, head)).
+template <typename QT, typename KT, int D, int BS, int NW, int G>
 __global__ __launch_bounds__(NW* kWave) void decode_kernel(
-    typename T::storage* __restrict__ out, uint32_t* __restrict__ counters,
-    float* __restrict__ ws_ml, float* __restrict__ ws_acc, const typename T::storage* __restrict__ q,
+    typename QT::storage* __restrict__ out, uint32_t* __restrict__ counters,
+    float* __restrict__ ws_ml, float* __restrict__ ws_acc, const typename QT::storage* __restrict__ q,
     const char* __restrict__ k_pool, const char* __restrict__ v_pool,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     float q_scale, int num_heads, int num_blocks, int max_blocks, int part_blocks, int max_parts) {
-  using C = Tile<T, D, BS>;
-  using St = Stage<T, D, BS, G>;
+  using C = Tile<KT, D, BS>;
+  using St = Stage<KT, D, BS, G>;
+  constexpr int E = KT::kElems;
   constexpr int kGroups = NW * C::kRowsPerLoad;
   __shared__ float s_m[kGroups];
   __shared__ float s_l[kGroups];
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
 
   if (L == 0) {  // empty context: zero row (written once, by partition 0)
     if (p == 0)
-      for (int d = threadIdx.x; d < D; d += blockDim.x) out[row * D + d] = T::pack(0.f);
+      for (int d = threadIdx.x; d < D; d += blockDim.x) out[row * D + d] = QT::pack(0.f);
     return;
   }
   if (p >= nparts) return;
@@ -200,16 +205,16 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
   const int grp = lane / C::kLanesPerRow;
   const int col = lane % C::kLanesPerRow;
 
-  float qf[T::kElems];
-  T::unpack(load16(reinterpret_cast<const char*>(q + row * D) + col * kVecBytes), qf);
+  float qf[E];
+  QSlice<QT, KT>::load(q + row * D, col, qf);
 #pragma unroll
-  for (int e = 0; e < T::kElems; ++e) qf[e] *= q_scale;
+  for (int e = 0; e < E; ++e) qf[e] *= q_scale;
 
   float m = -INFINITY;
   float l = 0.f;
-  float acc[T::kElems];
+  float acc[E];
 #pragma unroll
-  for (int e = 0; e < T::kElems; ++e) acc[e] = 0.f;
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
   bool bad = false;
 
   const int32_t* tbl = block_tables + static_cast<size_t>(s) * max_blocks;
@@ -231,15 +236,21 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
     for (int i = 0; i < C::kLoads; ++i) st.k[g][i] = load16(kb + i * C::kLoadBytes);
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) st.v[g][i] = load16(vb + i * C::kLoadBytes);
+    if constexpr (KT::kScaled) {
+      st.sk[g] = load_uniform_f32(k_scales + static_cast<size_t>(phys) * num_heads + h);
+      st.sv[g] = load_uniform_f32(v_scales + static_cast<size_t>(phys) * num_heads + h);
+    } else {
+      st.sk[g] = st.sv[g] = 1.f;
+    }
     st.block[g] = j;
   };
   auto attend_slot = [&](const St& st, int g) {
     const int j = st.block[g];
     const int tok0 = j * BS + grp;
     if ((j + 1) * BS <= L)
-      attend_tile<T, D, BS, false>(st.k[g], st.v[g], qf, m, l, acc, tok0, L);
+      attend_tile<KT, D, BS, false>(st.k[g], st.v[g], qf, m, l, acc, tok0, L, st.sk[g], st.sv[g]);
     else
-      attend_tile<T, D, BS, true>(st.k[g], st.v[g], qf, m, l, acc, tok0, L);
+      attend_tile<KT, D, BS, true>(st.k[g], st.v[g], qf, m, l, acc, tok0, L, st.sk[g], st.sv[g]);
   };
   // A full stage holds G existing tiles: no per-slot guards, so every load it
   // issues is consumed on every path (the compiler then knows which loads are
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
     s_l[gidx] = l;
   }
 #pragma unroll
-  for (int e = 0; e < T::kElems; ++e) s_acc[gidx][col * T::kElems + e] = acc[e];
+  for (int e = 0; e < E; ++e) s_acc[gidx][col * E + e] = acc[e];
   if (lane == 0) s_bad[wave] = bad ? 1 : 0;
   __syncthreads();
 
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
     }
   }
   if (nparts == 1) {
-    if (d < D) out[row * D + d] = T::pack(o / lsum);
+    if (d < D) out[row * D + d] = QT::pack(o / lsum);
     return;
   }
 
@@ -356,33 +367,46 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
 
   // Last arrival: merge every partition of this (s, h).  s_acc is free again
   // and serves as the reduction buffer.
-  merge_partials<T, D, NW * kWave>(out + row * D, ws_ml + base * 2, ws_acc + base * D, nparts,
+  merge_partials<QT, D, NW * kWave>(out + row * D, ws_ml + base * 2, ws_acc + base * D, nparts,
                                    s_w, &s_acc[0][0], s_pair);
   if (threadIdx.x == 0)  // ready for the next call
     __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename T, int D, int BS>
+template <typename QT, typename KT, int D, int BS>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t stream) {
-  using S = typename T::storage;
+  using S = typename QT::storage;
   const dim3 grid(a.num_heads, a.max_partitions, a.num_seqs);
-  hipLaunchKernelGGL((decode_kernel<T, D, BS, kWavesPerGroup, kTilesPerStage>), grid,
+  hipLaunchKernelGGL((decode_kernel<QT, KT, D, BS, kWavesPerGroup, kTilesPerStage>), grid,
                      dim3(kWavesPerGroup * kWave), 0, stream, static_cast<S*>(a.out), a.counters,
                      a.ws_ml, a.ws_acc, static_cast<const S*>(a.q),
                      static_cast<const char*>(a.k_pool), static_cast<const char*>(a.v_pool),
-                     a.block_tables, a.context_lens, a.scale * kLog2e, a.num_heads, a.num_blocks,
-                     a.max_blocks_per_seq, a.partition_blocks, a.max_partitions);
+                     a.k_scales, a.v_scales, a.block_tables, a.context_lens, a.scale * kLog2e,
+                     a.num_heads, a.num_blocks, a.max_blocks_per_seq, a.partition_blocks,
+                     a.max_partitions);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename QT, typename KT, int D>
 hipError_t run_decode_bs(const DecodeArgs& a, hipStream_t stream) {
-  return a.block_size == 16 ? run_decode<T, D, 16>(a, stream) : run_decode<T, D, 32>(a, stream);
+  return a.block_size == 16 ? run_decode<QT, KT, D, 16>(a, stream) : run_decode<QT, KT, D, 32>(a, stream);
 }
 
-template <typename T>
+template <typename QT, typename KT>
 hipError_t run_decode_d(const DecodeArgs& a, hipStream_t stream) {
-  return a.head_dim == 64 ? run_decode_bs<T, 64>(a, stream) : run_decode_bs<T, 128>(a, stream);
+  return a.head_dim == 64 ? run_decode_bs<QT, KT, 64>(a, stream) : run_decode_bs<QT, KT, 128>(a, stream);
+}
+
+template <typename QT>
+hipError_t run_decode_kv(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.kv_dtype) {
+    case PA_DTYPE_FP8_E4M3:
+      return run_decode_d<QT, FP8E4M3>(a, stream);
+    case PA_DTYPE_FP8_E5M2:
+      return run_decode_d<QT, FP8E5M2>(a, stream);
+    default:
+      return run_decode_d<QT, QT>(a, stream);
+  }
 }
 
 }  // namespace
@@ -390,11 +414,11 @@ hipError_t run_decode_d(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_partitioned(const DecodeArgs& a, hipStream_t stream) {
   switch (a.dtype) {
     case PA_DTYPE_F32:
-      return run_decode_d<F32>(a, stream);
+      return run_decode_d<F32, F32>(a, stream);
     case PA_DTYPE_F16:
-      return run_decode_d<F16>(a, stream);
+      return run_decode_kv<F16>(a, stream);
     default:
-      return run_decode_d<BF16>(a, stream);
+      return run_decode_kv<BF16>(a, stream);
   }
 }
 

@@ -61,29 +61,18 @@ struct Unit {
   static_assert(BS % kRows == 0, "units tile a block");
 };
 
-template <typename T, int D, int BS>
+template <typename QT, typename KT, int D, int BS>
 struct BStage {
-  u32x4 k[Tile<T, D, Unit<T, D, BS>::kRows>::kLoads];
-  u32x4 v[Tile<T, D, Unit<T, D, BS>::kRows>::kLoads];
-  u32x4 q;
+  u32x4 k[Tile<KT, D, Unit<KT, D, BS>::kRows>::kLoads];
+  u32x4 v[Tile<KT, D, Unit<KT, D, BS>::kRows>::kLoads];
+  u32x4 q[QSlice<QT, KT>::kVecs];
+  float sk, sv;         // K and V scales of the unit's (block, head) (8-bit KV only)
   int s, h, u, L, bad;  // u: unit index within the row
 };
 
 // The wave whose share holds tile x: the largest k with floor(k*T/W) <= x.
 __device__ __forceinline__ long long wave_of_tile(long long x, long long T, long long W) {
   return ((x + 1) * W - 1) / T;
-}
-
-// Write E (4 or 8) values to 16 contiguous bytes of out, rounded to storage.
-template <typename T, int E>
-__device__ __forceinline__ void store_row_slice(typename T::storage* dst, const float* v) {
-  typename T::storage s[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) s[e] = T::pack(v[e]);
-  u32x4 w;
-  static_assert(sizeof(s) == sizeof(w), "16-byte slice");
-  __builtin_memcpy(&w, s, sizeof(w));
-  store16(dst, w);
 }
 
 // Log-sum-exp merge of one row's partials by a single wave (64 lanes).
@@ -147,18 +136,22 @@ __device__ __forceinline__ void merge_row_wave(typename T::storage* __restrict__
 
 // Launch bounds ask for 16 waves per CU (4 per SIMD, <= 128 VGPRs) so that a
 // grid of 16/NW workgroups per CU is resident at once.
-template <typename T, int D, int BS, int NW>
-__global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
-    typename T::storage* __restrict__ out, uint32_t* __restrict__ counters,
-    float* __restrict__ ws_ml, float* __restrict__ ws_acc, const typename T::storage* __restrict__ q,
+// QT: query / output storage; KT: K/V cache storage (QT itself, or an 8-bit
+// type whose (block, head) scales come from k_scales / v_scales).
+template <typename QT, typename KT, int D, int BS, int NW>
+__global__ __launch_bounds__(NW* kWave, KT::kScaled ? 2 : 16 / NW) void decode_balanced_kernel(
+    typename QT::storage* __restrict__ out, uint32_t* __restrict__ counters,
+    float* __restrict__ ws_ml, float* __restrict__ ws_acc, const typename QT::storage* __restrict__ q,
     const char* __restrict__ k_pool, const char* __restrict__ v_pool,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     float q_scale, int num_seqs, int num_heads, int num_blocks, int max_blocks) {
-  constexpr int R = Unit<T, D, BS>::kRows;
-  constexpr int kUnitsPerBlock = Unit<T, D, BS>::kPerBlock;
-  using C = Tile<T, D, R>;
-  using St = BStage<T, D, BS>;
-  constexpr int E = T::kElems;
+  constexpr int R = Unit<KT, D, BS>::kRows;
+  constexpr int kUnitsPerBlock = Unit<KT, D, BS>::kPerBlock;
+  using C = Tile<KT, D, R>;
+  using St = BStage<QT, KT, D, BS>;
+  using QS = QSlice<QT, KT>;
+  constexpr int E = KT::kElems;
   constexpr int kThreads = NW * kWave;
   constexpr int kPer = (kBalancedMaxSeqs + kThreads - 1) / kThreads;  // sequences per thread
   __shared__ int s_off[kBalancedMaxSeqs + 1];  // units of all sequences before s
@@ -214,7 +207,7 @@ __global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
   // 2. empty contexts give zero rows (spread over the workgroups)
   for (int s = blockIdx.x; s < S; s += gridDim.x)
     if (s_len[s] == 0)
-      for (int i = tid; i < H * D; i += kThreads) out[static_cast<size_t>(s) * H * D + i] = T::pack(0.f);
+      for (int i = tid; i < H * D; i += kThreads) out[static_cast<size_t>(s) * H * D + i] = QT::pack(0.f);
 
   // 3. this wave's share of the T units (no workgroup barrier after this point)
   // Wn = min(waves in the grid, T): with at most one wave per unit no share is
@@ -272,8 +265,15 @@ __global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
     for (int i = 0; i < C::kLoads; ++i) st.k[i] = load16(kb + i * C::kLoadBytes);
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) st.v[i] = load16(vb + i * C::kLoadBytes);
-    st.q = load16(reinterpret_cast<const char*>(q + (static_cast<size_t>(w_s) * H + w_h) * D) +
-                  col * kVecBytes);
+    const char* qrow = reinterpret_cast<const char*>(q + (static_cast<size_t>(w_s) * H + w_h) * D);
+#pragma unroll
+    for (int i = 0; i < QS::kVecs; ++i) st.q[i] = load16(qrow + col * QS::kBytes + i * kVecBytes);
+    if constexpr (KT::kScaled) {
+      st.sk = load_uniform_f32(k_scales + static_cast<size_t>(phys) * H + w_h);
+      st.sv = load_uniform_f32(v_scales + static_cast<size_t>(phys) * H + w_h);
+    } else {
+      st.sk = st.sv = 1.f;
+    }
     st.s = w_s;
     st.h = w_h;
     st.u = w_j;
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
         const float inv = 1.f / lt;
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = seg_bad ? __builtin_nanf("") : a[e] * inv;
-        store_row_slice<T, E>(out + row * D + col * E, o);
+        QS::store(out + row * D, col, o);
       }
     } else {
       const size_t slot = static_cast<size_t>(k) + row;
@@ -357,7 +357,8 @@ __global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
       seg_bad = 0;
       m = -INFINITY;
       l = 0.f;
-      T::unpack(st.q, qf);
+#pragma unroll
+      for (int i = 0; i < QS::kVecs; ++i) QT::unpack(st.q[i], qf + i * QT::kElems);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         acc[e] = 0.f;
@@ -367,9 +368,9 @@ __global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
     seg_bad |= st.bad;
     const int tok0 = st.u * R + grp;  // unit u holds tokens [u*R, (u+1)*R)
     if ((st.u + 1) * R <= st.L)
-      attend_tile<T, D, R, false>(st.k, st.v, qf, m, l, acc, tok0, st.L);
+      attend_tile<KT, D, R, false>(st.k, st.v, qf, m, l, acc, tok0, st.L, st.sk, st.sv);
     else
-      attend_tile<T, D, R, true>(st.k, st.v, qf, m, l, acc, tok0, st.L);
+      attend_tile<KT, D, R, true>(st.k, st.v, qf, m, l, acc, tok0, st.L, st.sk, st.sv);
   };
 
   // two-stage pipeline over the share (steady state without conditional
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
   for (int p = 0; p < 2; ++p) {
     if (p >= pend) break;
     if (tk[p] == static_cast<uint32_t>(pend_n[p] - 1)) {
-      merge_row_wave<T, D>(out + pend_row[p] * D, ws_ml + pend_slot0[p] * 2, ws_acc + pend_slot0[p] * D,
+      merge_row_wave<QT, D>(out + pend_row[p] * D, ws_ml + pend_slot0[p] * 2, ws_acc + pend_slot0[p] * D,
                            pend_n[p], lane);
       if (lane == 0)  // ready for the next call
         __hip_atomic_store(&counters[pend_row[p]], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -414,26 +415,38 @@ __global__ __launch_bounds__(NW* kWave, 16 / NW) void decode_balanced_kernel(
   }
 }
 
-template <typename T, int D, int BS>
+template <typename QT, typename KT, int D, int BS>
 hipError_t run_balanced(const DecodeArgs& a, hipStream_t stream) {
-  using S = typename T::storage;
-  hipLaunchKernelGGL((decode_balanced_kernel<T, D, BS, kBalancedWaves>), dim3(a.workgroups),
+  using S = typename QT::storage;
+  hipLaunchKernelGGL((decode_balanced_kernel<QT, KT, D, BS, kBalancedWaves>), dim3(a.workgroups),
                      dim3(kBalancedWaves * kWave), 0, stream, static_cast<S*>(a.out), a.counters,
                      a.ws_ml, a.ws_acc, static_cast<const S*>(a.q),
                      static_cast<const char*>(a.k_pool), static_cast<const char*>(a.v_pool),
-                     a.block_tables, a.context_lens, a.scale * kLog2e, a.num_seqs, a.num_heads,
-                     a.num_blocks, a.max_blocks_per_seq);
+                     a.k_scales, a.v_scales, a.block_tables, a.context_lens, a.scale * kLog2e,
+                     a.num_seqs, a.num_heads, a.num_blocks, a.max_blocks_per_seq);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename QT, typename KT, int D>
 hipError_t run_balanced_bs(const DecodeArgs& a, hipStream_t stream) {
-  return a.block_size == 16 ? run_balanced<T, D, 16>(a, stream) : run_balanced<T, D, 32>(a, stream);
+  return a.block_size == 16 ? run_balanced<QT, KT, D, 16>(a, stream) : run_balanced<QT, KT, D, 32>(a, stream);
 }
 
-template <typename T>
+template <typename QT, typename KT>
 hipError_t run_balanced_d(const DecodeArgs& a, hipStream_t stream) {
-  return a.head_dim == 64 ? run_balanced_bs<T, 64>(a, stream) : run_balanced_bs<T, 128>(a, stream);
+  return a.head_dim == 64 ? run_balanced_bs<QT, KT, 64>(a, stream) : run_balanced_bs<QT, KT, 128>(a, stream);
+}
+
+template <typename QT>
+hipError_t run_balanced_kv(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.kv_dtype) {
+    case PA_DTYPE_FP8_E4M3:
+      return run_balanced_d<QT, FP8E4M3>(a, stream);
+    case PA_DTYPE_FP8_E5M2:
+      return run_balanced_d<QT, FP8E5M2>(a, stream);
+    default:
+      return run_balanced_d<QT, QT>(a, stream);
+  }
 }
 
 }  // namespace
@@ -441,11 +454,11 @@ hipError_t run_balanced_d(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode_balanced(const DecodeArgs& a, hipStream_t stream) {
   switch (a.dtype) {
     case PA_DTYPE_F32:
-      return run_balanced_d<F32>(a, stream);
+      return run_balanced_d<F32, F32>(a, stream);
     case PA_DTYPE_F16:
-      return run_balanced_d<F16>(a, stream);
+      return run_balanced_kv<F16>(a, stream);
     default:
-      return run_balanced_d<BF16>(a, stream);
+      return run_balanced_kv<BF16>(a, stream);
   }
 }
 

@@ -2,7 +2,9 @@
 //
 // Storage types are tag structs that know how to turn one 16-byte vector
 // (what one lane moves with a global_load_dwordx4) into fp32 values and how to
-// round an fp32 result back to storage with round-to-nearest-even.
+// round an fp32 result back to storage with round-to-nearest-even.  The 8-bit
+// KV-cache types (FP8E4M3, FP8E5M2) only unpack; their values are scaled per
+// (block, head) (kScaled) and written by the quantizers at the end.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +26,7 @@ __device__ __forceinline__ float word_as_float(uint32_t w) { return __builtin_bi
 struct F32 {
   using storage = float;
   static constexpr int kElems = 4;  // per 16-byte vector
+  static constexpr bool kScaled = false;
   static __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
     const uint32_t w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
     f[0] = word_as_float(w0);
@@ -37,6 +40,7 @@ struct F32 {
 struct F16 {
   using storage = _Float16;
   static constexpr int kElems = 8;
+  static constexpr bool kScaled = false;
   static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
     const f16x2 h = __builtin_bit_cast(f16x2, w);
     f[0] = static_cast<float>(h.x);
@@ -55,6 +59,7 @@ struct F16 {
 struct BF16 {
   using storage = uint16_t;
   static constexpr int kElems = 8;
+  static constexpr bool kScaled = false;
   static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
     f[0] = __builtin_bit_cast(float, w << 16);
     f[1] = __builtin_bit_cast(float, w & 0xffff0000u);
@@ -74,8 +79,86 @@ struct BF16 {
   }
 };
 
+// 8-bit floating-point KV elements, OCP formats: E4M3 (bias 7, no
+// infinities, S.1111.111 = NaN, largest finite 448) and E5M2 (bias 15,
+// IEEE-style infinities and NaNs, largest finite 57344).  gfx950's
+// v_cvt_pk_f32_fp8 / _bf8 decode two codes of one 32-bit word per
+// instruction in these formats.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+struct FP8E4M3 {
+  using storage = uint8_t;
+  static constexpr int kElems = 16;
+  static constexpr bool kScaled = true;
+  static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    f[0] = lo.x;
+    f[1] = lo.y;
+    f[2] = hi.x;
+    f[3] = hi.y;
+  }
+  static __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
+    unpack_word(v.x, f + 0);
+    unpack_word(v.y, f + 4);
+    unpack_word(v.z, f + 8);
+    unpack_word(v.w, f + 12);
+  }
+};
+
+struct FP8E5M2 {
+  using storage = uint8_t;
+  static constexpr int kElems = 16;
+  static constexpr bool kScaled = true;
+  static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
+    f[0] = lo.x;
+    f[1] = lo.y;
+    f[2] = hi.x;
+    f[3] = hi.y;
+  }
+  static __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
+    unpack_word(v.x, f + 0);
+    unpack_word(v.y, f + 4);
+    unpack_word(v.z, f + 8);
+    unpack_word(v.w, f + 12);
+  }
+};
+
+// fp32 -> 8-bit code: nearest value, ties to the even code, saturating to the
+// largest finite value (infinities included), NaN -> 0x7F; the sign bit is
+// y's (so -0 -> 0x80).  Normal results keep the top kMant mantissa bits of
+// y, rounded to nearest even on the fp32 bit pattern (a carry into the
+// exponent field is the correct next binade); subnormal results are
+// rint(|y| * 2^(bias - 1 + kMant)), exact because that scaling is a power of
+// two, and the rounding of the largest subnormal up to the smallest normal
+// lands on the smallest normal's code.
+template <int kExp, int kMant, int kBias>
+__device__ __forceinline__ uint32_t quantize_fp8(float y, float max_finite, uint32_t max_code) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                                    // NaN
+  if (__builtin_bit_cast(float, a) >= max_finite) return sign | max_code;  // saturate
+  constexpr float kMinNormal = __builtin_bit_cast(float, static_cast<uint32_t>(127 + 1 - kBias) << 23);
+  constexpr float kSubScale = __builtin_bit_cast(float, static_cast<uint32_t>(127 + kBias - 1 + kMant) << 23);
+  uint32_t code;
+  if (__builtin_bit_cast(float, a) < kMinNormal) {
+    code = static_cast<uint32_t>(__builtin_rintf(__builtin_bit_cast(float, a) * kSubScale));
+  } else {
+    constexpr int kDrop = 23 - kMant;
+    const uint32_t r = (a + ((1u << (kDrop - 1)) - 1u) + ((a >> kDrop) & 1u)) >> kDrop;
+    code = r - (static_cast<uint32_t>(127 - kBias) << kMant);
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ uint32_t quantize_e4m3(float y) { return quantize_fp8<4, 3, 7>(y, 448.f, 0x7eu); }
+__device__ __forceinline__ uint32_t quantize_e5m2(float y) { return quantize_fp8<5, 2, 15>(y, 57344.f, 0x7bu); }
+
 // ---------------------------------------------------------------------------
-// Cross-lane sums over aligned groups of G consecutive lanes (G = 8, 16, 32),
+// Cross-lane sums over aligned groups of G consecutive lanes (G = 4 ... 32),
 // leaving the group total in every lane of the group.  DPP quad permutes give
 // the xor-1 and xor-2 partners; row_half_mirror (lane i <- 7-i within 8) and
 // row_mirror (lane i <- 15-i within 16) then pair each lane with one in the
@@ -100,13 +183,28 @@ __device__ __forceinline__ float swizzle_xor16(float x) {
 
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(G == 8 || G == 16 || G == 32, "group of 8, 16 or 32 lanes");
+  static_assert(G == 4 || G == 8 || G == 16 || G == 32, "group of 4, 8, 16 or 32 lanes");
   x += dpp_quad_xor1(x);
   x += dpp_quad_xor2(x);
-  x += dpp_row_half_mirror(x);
+  if constexpr (G >= 8) x += dpp_row_half_mirror(x);
   if constexpr (G >= 16) x += dpp_row_mirror(x);
   if constexpr (G >= 32) x += swizzle_xor16(x);
   return x;
+}
+
+// Word 3 of a gfx9-family buffer resource for raw (unformatted, unswizzled)
+// 32-bit accesses.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// One fp32 read from a wave-uniform address through the VECTOR memory path
+// (a 4-byte buffer resource at p).  The compiler would turn a plain uniform
+// load into a scalar load, and it waits for all outstanding scalar loads at
+// once; for per-tile scales that stalled every pipeline stage on the previous
+// tile's scale.  A vector load completes in order with the tile's own loads.
+__device__ __forceinline__ float load_uniform_f32(const float* p) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, sizeof(float), kBufferRsrcWord3);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

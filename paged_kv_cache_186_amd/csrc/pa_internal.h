@@ -54,7 +54,10 @@ struct DecodeArgs {
   int head_dim;
   int num_blocks;
   int max_blocks_per_seq;
-  int dtype;             // pa_dtype_t
+  int dtype;             // pa_dtype_t of q and out
+  int kv_dtype;          // pa_dtype_t of the pools (dtype, or an 8-bit format)
+  const float* k_scales;  // [num_blocks][H] (8-bit pools only)
+  const float* v_scales;
   DecodeMode mode;
   int partition_blocks;  // kPartitioned: blocks per partition
   int max_partitions;    // kPartitioned: ceil(max_blocks_per_seq / partition_blocks)
@@ -125,7 +128,24 @@ hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_ne
                                     const int32_t* slot_mapping, int num_tokens, int num_heads,
                                     int row_bytes, int block_size, int num_blocks, hipStream_t stream);
 
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, int num_pairs,
-                              size_t block_bytes, int num_blocks, hipStream_t stream);
+// k_scales / v_scales: [num_blocks][num_heads] per-block scales copied along
+// with the blocks (8-bit pools), or null.
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                              const int32_t* block_mapping, int num_pairs, size_t block_bytes,
+                              int num_blocks, int num_heads, hipStream_t stream);
+
+struct ReshapeFp8Args {
+  void* k_pool;
+  void* v_pool;
+  const float* k_scales;
+  const float* v_scales;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
+  int num_tokens, num_heads, head_dim, block_size, num_blocks;
+  int in_dtype;  // pa_dtype_t of k_new / v_new
+  int kv_dtype;  // PA_DTYPE_FP8_E4M3 or PA_DTYPE_FP8_E5M2
+};
+hipError_t launch_reshape_and_cache_fp8(const ReshapeFp8Args& a, hipStream_t stream);
 
 }  // namespace pa

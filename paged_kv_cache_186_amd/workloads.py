@@ -144,6 +144,35 @@ def poison_unreferenced(w: PagedWorkload, value: float = float("nan")) -> None:
             w.v_pool[last, :, L % bs:, :] = value
 
 
+FP8_DTYPES = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def fp8_pools(w: PagedWorkload, fmt: str, chunk_blocks: int = 2048):
+    """An 8-bit copy of the workload's K/V pools for the *_fp8 calls.
+
+    Input generation only: each (block, head) gets the scale
+    max|x| / (largest finite value of ``fmt``) over its rows (NaN ignored; an
+    all-zero or all-NaN tile gets scale 1), and each element is cast to the
+    float8 dtype after division by it (torch's cast; the values stay in range).
+    NaN-poisoned rows stay NaN codes.  Returns (k_codes, v_codes, k_scales,
+    v_scales) on the workload's device; the 16-bit pools are left as they are.
+    """
+    out = []
+    for pool in (w.k_pool, w.v_pool):
+        codes = torch.empty(pool.shape, dtype=FP8_DTYPES[fmt], device=pool.device)
+        scales = torch.empty(pool.shape[:2], dtype=torch.float32, device=pool.device)
+        for b0 in range(0, pool.shape[0], chunk_blocks):
+            x = pool[b0:b0 + chunk_blocks].float()
+            amax = torch.nan_to_num(x.abs(), nan=0.0).amax(dim=(2, 3))
+            sc = torch.where(amax > 0, amax / FP8_MAX[fmt], torch.ones_like(amax))
+            scales[b0:b0 + chunk_blocks] = sc
+            codes[b0:b0 + chunk_blocks] = (x / sc[:, :, None, None]).to(FP8_DTYPES[fmt])
+            del x
+        out += [codes, scales]
+    return out[0], out[2], out[1], out[3]
+
+
 def _manager_from_shuffled_free_list(num_blocks, block_size, rng) -> BlockManager:
     return BlockManager(num_blocks, block_size, free_order=rng.permutation(num_blocks).tolist())
 

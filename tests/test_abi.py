@@ -25,7 +25,8 @@ def lib():
 def test_every_declared_function_is_exported(lib):
     declared = B.header_functions()
     assert set(declared) == {"pa_abi_version", "pa_status_string", "pa_decode_workspace_size",
-                             "pa_decode", "pa_reshape_and_cache", "pa_copy_blocks"}
+                             "pa_decode", "pa_reshape_and_cache", "pa_copy_blocks",
+                             "pa_decode_fp8", "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8"}
     raw = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
         assert hasattr(raw, name), name
@@ -33,7 +34,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
     for st in range(5):
         s = B.status_string(st)
         assert s.startswith("PA_")
@@ -149,3 +150,81 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         B.pa_decode(q.clone(), q, torch.zeros(4, 4, 16, 64), torch.zeros(4, 4, 16, 64),
                     torch.zeros(2, 1, dtype=torch.int32), torch.ones(2, dtype=torch.int32), 1.0, 16)
+
+
+# ---- 8-bit KV cache entry points ---------------------------------------------
+
+F16, BF16, F32, E4M3, E5M2 = 1, 2, 0, 3, 4
+
+
+def _decode_fp8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, cl=FAKE, scale=0.125,
+             bs=16, S=4, H=4, D=64, N=16, W=3, P=0, qdt=F16, kvdt=E4M3, ws=None, wsb=0)
+    a.update(kw)
+    return lib.pa_decode_fp8(a["out"], a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["cl"],
+                             a["scale"], a["bs"], a["S"], a["H"], a["D"], a["N"], a["W"], a["P"],
+                             a["qdt"], a["kvdt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qdt=F32), UNSUPPORTED),
+    (dict(qdt=E4M3), UNSUPPORTED),
+    (dict(kvdt=F16), UNSUPPORTED),
+    (dict(kvdt=9), UNSUPPORTED),
+    (dict(D=96), UNSUPPORTED),
+    (dict(ks=None), INVALID),
+    (dict(vs=None), INVALID),
+    (dict(ks=FAKE + 2), INVALID),
+    (dict(k=MISALIGNED), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(H=0), INVALID),
+    (dict(W=2000, P=16), WORKSPACE),
+])
+def test_decode_fp8_rejects_before_launch(lib, kw, status):
+    assert _decode_fp8(lib, **kw) == status
+
+
+def test_decode_fp8_zero_sequences_is_a_no_op(lib):
+    assert _decode_fp8(lib, S=0) == OK
+
+
+def test_unscaled_calls_refuse_8bit_dtypes(lib):
+    assert _decode(lib, dt=E4M3) == UNSUPPORTED
+    assert lib.pa_reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 64, 16, 16, E5M2, None) == UNSUPPORTED
+    assert lib.pa_copy_blocks(FAKE, FAKE, FAKE, 2, 4, 64, 16, 16, E4M3, None) == UNSUPPORTED
+
+
+def _reshape_fp8(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, kn=FAKE, vn=FAKE, sm=FAKE, T=4, H=4, D=64, bs=16,
+             N=16, ndt=F16, kvdt=E4M3)
+    a.update(kw)
+    return lib.pa_reshape_and_cache_fp8(a["k"], a["v"], a["ks"], a["vs"], a["kn"], a["vn"], a["sm"],
+                                        a["T"], a["H"], a["D"], a["bs"], a["N"], a["ndt"], a["kvdt"],
+                                        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kvdt=F16), UNSUPPORTED),
+    (dict(ndt=E4M3), UNSUPPORTED),
+    (dict(bs=8), UNSUPPORTED),
+    (dict(ks=None), INVALID),
+    (dict(vs=FAKE + 1), INVALID),
+    (dict(kn=MISALIGNED), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(T=0), OK),
+])
+def test_reshape_fp8_rejects_before_launch(lib, kw, status):
+    assert _reshape_fp8(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kvdt=BF16), UNSUPPORTED),
+    (dict(ks=None), INVALID),
+    (dict(k=MISALIGNED), INVALID),
+    (dict(n=0, ks=None), OK),
+])
+def test_copy_blocks_fp8_rejects_before_launch(lib, kw, status):
+    a = dict(k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bm=FAKE, n=2, H=4, D=64, bs=16, N=16, kvdt=E5M2)
+    a.update(kw)
+    assert lib.pa_copy_blocks_fp8(a["k"], a["v"], a["ks"], a["vs"], a["bm"], a["n"], a["H"], a["D"],
+                                  a["bs"], a["N"], a["kvdt"], None) == status
