@@ -43,6 +43,7 @@ from .paged_attention import (  # noqa: F401
     lse_merge_ref,
     reshape_and_cache_ref,
     copy_blocks_ref,
+    swap_blocks_ref,
 )
 from .fp8 import (  # noqa: F401
     fp8_values,

@@ -34,6 +34,8 @@ Pin status (tests/test_oracle.py):
   are read back in logical order by the gather; untouched bytes unchanged.
 * ``copy_blocks_ref`` — pinned: destination bytes equal source bytes, all
   other blocks unchanged, and copy-on-write leaves decode output bit-identical.
+* ``swap_blocks_ref`` — pinned: a swap out and back in restores the cache
+  bit for bit and decode over it is unchanged; untouched blocks unchanged.
 """
 
 from __future__ import annotations
@@ -211,4 +213,20 @@ def copy_blocks_ref(k_pool, v_pool, block_mapping):
     for src, dst in pairs:
         k_out[int(dst)] = k_pool[int(src)]
         v_out[int(dst)] = v_pool[int(src)]
+    return k_out, v_out
+
+
+def swap_blocks_ref(dst_k, dst_v, src_k, src_v, block_mapping):
+    """Copy whole blocks between two pools: dst[d] = src[s] for each {s, d}
+    pair, in both the K and the V pool.  This is the data movement of swapping
+    an inactive sequence's cache out to host memory and back in (page
+    "PagedAttention MLX：为Apple Silicon打造的高吞吐量LLM推理引擎", dynamic
+    scheduling in the feature list and the physical KV pool of the
+    architecture list, which can swap out to CPU memory).  Byte copy; returns
+    new destination pools, inputs unchanged."""
+    k_out = dst_k.clone() if isinstance(dst_k, torch.Tensor) else np.array(dst_k, copy=True)
+    v_out = dst_v.clone() if isinstance(dst_v, torch.Tensor) else np.array(dst_v, copy=True)
+    for src, dst in _as_int(block_mapping).reshape(-1, 2):
+        k_out[int(dst)] = src_k[int(src)]
+        v_out[int(dst)] = src_v[int(src)]
     return k_out, v_out

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (copy_blocks_ref, decode_ref, gather_sequence_kv,
+from oracle import (copy_blocks_ref, decode_ref, gather_sequence_kv, swap_blocks_ref,
                     lse_merge_ref, reshape_and_cache_ref, split_decode_ref)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -366,4 +366,33 @@ def test_copy_on_write_keeps_decode_bit_identical():
     t2[1, 0] = free[0]
     t2[3, 0] = free[1]
     after = decode_ref(q, k2, v2, t2, lens, 0.5, bs)
+    np.testing.assert_array_equal(after, before)
+
+
+def test_swap_out_and_back_restores_the_cache_and_the_decode():
+    """Swapping sequence 2's blocks out to a host pool, reusing its device
+    blocks for other data, then swapping them back (into different device
+    blocks, with the table repointed) leaves decode bit-identical."""
+    q, Kc, Vc, k_pool, v_pool, tables, lens, bs = _random_case(33, spare=8)
+    before = decode_ref(q, k_pool, v_pool, tables, lens, 0.5, bs)
+    nb = -(-int(lens[2]) // bs)
+    blocks = [int(b) for b in tables[2, :nb]]
+    host_k = np.zeros((nb + 3,) + k_pool.shape[1:])
+    host_v = np.zeros((nb + 3,) + v_pool.shape[1:])
+    out_map = [[b, i + 1] for i, b in enumerate(blocks)]  # host slots 1..nb
+    hk, hv = swap_blocks_ref(host_k, host_v, k_pool, v_pool, out_map)
+    for src, dst in out_map:
+        assert np.array_equal(hk[dst], k_pool[src]) and np.array_equal(hv[dst], v_pool[src])
+    assert not hk[0].any() and not hk[nb + 1:].any()       # untouched host slots
+    # the device blocks are overwritten, then the data comes back elsewhere
+    used = set(int(x) for x in tables.ravel() if x >= 0)
+    free = [b for b in range(k_pool.shape[0]) if b not in used][:nb]
+    k2, v2 = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    k2[blocks] = np.nan
+    v2[blocks] = np.nan
+    in_map = [[1 + i, f] for i, f in enumerate(free)]
+    k3, v3 = swap_blocks_ref(k2, v2, hk, hv, in_map)
+    t2 = tables.copy()
+    t2[2, :nb] = free
+    after = decode_ref(q, k3, v3, t2, lens, 0.5, bs)
     np.testing.assert_array_equal(after, before)

@@ -219,3 +219,45 @@ def test_copy_pins():
     assert _copy_pins(copy_blocks_ref)
     assert not _copy_pins(_copy_reversed)
     assert not _copy_pins(_copy_k_only)
+
+
+# ---- mutants of the swap between pools ----------------------------------------
+
+from oracle import swap_blocks_ref  # noqa: E402
+
+
+def _swap_pins(swap) -> bool:
+    """Out to a host pool and back into other device blocks restores the data;
+    untouched destination blocks keep theirs."""
+    try:
+        dk = torch.arange(8 * 2 * 2 * 2, dtype=torch.float32).reshape(8, 2, 2, 2)
+        dv = -dk - 1
+        hk, hv = torch.zeros(4, 2, 2, 2), torch.zeros(4, 2, 2, 2)
+        hk2, hv2 = swap(hk, hv, dk, dv, [[5, 1], [2, 3]])
+        if not (torch.equal(hk2[1], dk[5]) and torch.equal(hv2[3], dv[2]) and not hk2[0].any()
+                and not hk2[2].any()):
+            return False
+        dk3, dv3 = swap(dk, dv, hk2, hv2, [[1, 6], [3, 7]])
+        return bool(torch.equal(dk3[6], dk[5]) and torch.equal(dv3[7], dv[2])
+                    and torch.equal(dk3[:6], dk[:6]) and torch.equal(dv3[:6], dv[:6]))
+    except (IndexError, RuntimeError):
+        return False
+
+
+def _swap_reversed(dk, dv, sk, sv, mapping):
+    return swap_blocks_ref(dk, dv, sk, sv, [[d, s] for s, d in mapping])
+
+
+def _swap_k_only(dk, dv, sk, sv, mapping):
+    k2, _ = swap_blocks_ref(dk, dv, sk, sv, mapping)
+    return k2, dv.clone()
+
+
+def _swap_dst_off_by_one(dk, dv, sk, sv, mapping):
+    return swap_blocks_ref(dk, dv, sk, sv, [[s, d - 1] for s, d in mapping])
+
+
+def test_swap_pins():
+    assert _swap_pins(swap_blocks_ref)
+    for mutant in (_swap_reversed, _swap_k_only, _swap_dst_off_by_one):
+        assert not _swap_pins(mutant), mutant.__name__
