@@ -224,6 +224,89 @@ def cpu_baseline(w_host, k_new, v_new, slots, step_bytes: int, seconds: float) -
                        f"host has {len(os.sched_getaffinity(0))} cores available")}
 
 
+HOST_LINK_GBS = 64.0           # PCIe 5.0 x16, per direction (published)
+
+
+def swap_bench(pa, dev, steps: int, warmup: int) -> dict:
+    """pa_swap_blocks between the layer-shape device pools and pinned host
+    pools: 256 scattered blocks out (device -> host), then back in, 128 KiB
+    per block per pool (64 MiB each way).  Beside it, two ways the same bytes
+    could move with the DMA engines: one hipMemcpyAsync per block and pool
+    (torch copy_), and a single contiguous copy of 64 MiB (the host link's
+    practical ceiling for this direction)."""
+    from paged_kv_cache_186_amd import workloads as W
+    w = W.layer_shape(0, device=dev)
+    nblk = 256
+    rng = np.random.default_rng(1)
+    dev_ids = rng.choice(w.num_blocks, size=nblk, replace=False).astype(np.int32)
+    host_ids = rng.permutation(nblk).astype(np.int32)
+    shape = (nblk,) + tuple(w.k_pool.shape[1:])
+    hk = torch.empty(shape, dtype=w.dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=w.dtype, pin_memory=True)
+    out_map = torch.from_numpy(np.stack([dev_ids, host_ids], 1)).to(dev)
+    in_map = torch.from_numpy(np.stack([host_ids, dev_ids], 1)).to(dev)
+    nbytes = 2 * nblk * w.k_pool[0].numel() * w.k_pool.element_size()
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    res = {}
+    res["out_kernel"] = timed(lambda: pa.pa_swap_blocks(hk, hv, w.k_pool, w.v_pool, out_map))
+    res["in_kernel"] = timed(lambda: pa.pa_swap_blocks(w.k_pool, w.v_pool, hk, hv, in_map))
+    di, hi = dev_ids.tolist(), host_ids.tolist()
+
+    def per_block(out: bool):
+        for d, h in zip(di, hi):
+            if out:
+                hk[h].copy_(w.k_pool[d], non_blocking=True)
+                hv[h].copy_(w.v_pool[d], non_blocking=True)
+            else:
+                w.k_pool[d].copy_(hk[h], non_blocking=True)
+                w.v_pool[d].copy_(hv[h], non_blocking=True)
+    res["out_memcpy_per_block"] = timed(lambda: per_block(True))
+    res["in_memcpy_per_block"] = timed(lambda: per_block(False))
+    flat_d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    flat_h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    res["out_one_memcpy"] = timed(lambda: flat_h.copy_(flat_d, non_blocking=True))
+    res["in_one_memcpy"] = timed(lambda: flat_d.copy_(flat_h, non_blocking=True))
+    # the kernel's result must equal the oracle's byte copy
+    from oracle import swap_blocks_ref
+    pa.pa_swap_blocks(hk, hv, w.k_pool, w.v_pool, out_map)
+    torch.cuda.synchronize()
+    rk, _ = swap_blocks_ref(torch.zeros_like(hk), torch.zeros_like(hv), w.k_pool.cpu(), w.v_pool.cpu(),
+                            out_map.cpu().numpy())
+    if not torch.equal(hk.view(torch.int16), rk.view(torch.int16)):
+        raise RuntimeError("swap out differs from the oracle")
+    gbs = {k: round(nbytes / (v * 1e-3) / 1e9, 2) for k, v in res.items()}
+    return {
+        "metric": "pa_swap_blocks: host-link GB/s swapping 256 scattered KV blocks (K+V, 64 MiB) "
+                  "out to pinned host memory and back, 1 MI355X",
+        "value": round((gbs["out_kernel"] + gbs["in_kernel"]) / 2, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(res["out_kernel"] + res["in_kernel"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) layer-shape pools)",
+        "config": {"workload": "swap of 256 of the 1024 layer-shape blocks (32 heads x 16 x 128 fp16, "
+                               "K and V: 128 KiB each per block)", "bytes_each_way": nbytes},
+        "gb_per_s": gbs, "ms": {k: round(v, 4) for k, v in res.items()},
+        "roofline": {"bound": "host link", "achieved": round((gbs["out_kernel"] + gbs["in_kernel"]) / 2, 2),
+                     "peak": HOST_LINK_GBS, "unit": "GB/s",
+                     "frac": round((gbs["out_kernel"] + gbs["in_kernel"]) / 2 / HOST_LINK_GBS, 4),
+                     "traffic": None},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +321,8 @@ def main() -> int:
                          "(OCP E4M3 / E5M2 with per-block, per-head scales; q and out keep their dtype)")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--replicas", type=int, default=0, help="KV pool replicas (0 = enough for 2 GiB)")
+    ap.add_argument("--op", default="decode", choices=["decode", "swap"],
+                    help="decode: the decode step (default); swap: pa_swap_blocks over the host link")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -252,6 +337,10 @@ def main() -> int:
     torch.cuda.set_device(dev)
     pa.load_library()
     stream = torch.cuda.current_stream(dev)
+
+    if args.op == "swap":
+        print(json.dumps(swap_bench(pa, dev, min(args.steps, 50), min(args.warmup, 5))), flush=True)
+        return 0
 
     from paged_kv_cache_186_amd import workloads as W
     log(f"building workload {args.workload} (seed {args.seed})")

@@ -176,6 +176,36 @@ pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapp
                            void* stream);
 
 /*
+ * Copy whole blocks from one pool pair to another (K and V):
+ *   dst_k[d] = src_k[s], dst_v[d] = src_v[s]     for each {s, d} of block_mapping
+ * — swapping an inactive sequence's blocks out to host memory and back in
+ * ("PagedAttention MLX：为Apple Silicon打造的高吞吐量LLM推理引擎": dynamic
+ * scheduling with preemption and swapping, and the physical KV pool that can
+ * swap out to CPU memory).  Either pool pair may live in pinned host memory
+ * that is mapped into the GPU's address space (hipHostMalloc; torch's
+ * pin_memory) and the other in device memory; block_mapping (int32 [n][2])
+ * and the scales may be in either too.  Host pointers are passed as they are:
+ * the library asks HIP for the GPU address of pinned host memory and returns
+ * PA_ERR_INVALID_ARG, launching nothing, for any pointer HIP does not know as
+ * device or pinned host memory (pageable host memory included).  One kernel
+ * moves all pairs, with many 16 KiB chunks in flight over the host link.
+ * Bit-exact.  Pool layout as above, src with src_num_blocks blocks and dst
+ * with dst_num_blocks; pairs naming an id outside its pool are skipped.
+ * dtype may be F32, F16, BF16, or an 8-bit format — then each block's K and
+ * V scales move too (the four scale pointers, [blocks][num_heads] fp32, must
+ * be non-null; they are ignored for the other dtypes).  Destinations must be
+ * distinct; with the same pools on both sides no destination may be a
+ * source.  num_pairs == 0 returns PA_OK.
+ */
+pa_status_t pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                           float* dst_k_scales, float* dst_v_scales,
+                           const float* src_k_scales, const float* src_v_scales,
+                           const int32_t* block_mapping, int32_t num_pairs,
+                           int32_t num_heads, int32_t head_dim, int32_t block_size,
+                           int32_t src_num_blocks, int32_t dst_num_blocks,
+                           pa_dtype_t dtype, void* stream);
+
+/*
  * ---- 8-bit KV cache --------------------------------------------------------
  * The pages name quantization only as future work (page "mlx-paged-attention:
  * Bringing vLLM-level High Throughput Inference to Apple Silicon", future

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     pa_decode_workspace_size,
     pa_reshape_and_cache,
     pa_reshape_and_cache_fp8,
+    pa_swap_blocks,
     status_string,
 )
 from .block_manager import BlockManager  # noqa: F401

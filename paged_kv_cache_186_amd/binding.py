@@ -44,6 +44,7 @@ _SIGNATURES = {
                       + [_c_void, _c_size, _c_void]),
     "pa_reshape_and_cache_fp8": (_c_int, [_c_void] * 7 + [_c_int] * 5 + [_c_int, _c_int, _c_void]),
     "pa_copy_blocks_fp8": (_c_int, [_c_void] * 5 + [_c_int] * 5 + [_c_int, _c_void]),
+    "pa_swap_blocks": (_c_int, [_c_void] * 9 + [_c_int] * 6 + [_c_int, _c_void]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -301,3 +302,50 @@ def pa_copy_blocks_fp8(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scales: tor
                                     block_mapping.shape[0], H, D, BS, N, FP8_CODES[k_pool.dtype],
                                     _stream_handle(k_pool.device, stream))
     _check("pa_copy_blocks_fp8", st)
+
+
+def _gpu_visible(t: torch.Tensor, name: str) -> None:
+    _require(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    _require(t.is_cuda or t.is_pinned(), f"{name} must be in GPU memory or pinned host memory")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def pa_swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
+                   src_v: torch.Tensor, block_mapping: torch.Tensor, *, dst_scales=None,
+                   src_scales=None, device=None, stream=None) -> None:
+    """Copy whole blocks src[s] -> dst[d] between two pool pairs, either of
+    which may be pinned host memory (swap out / swap in).  8-bit pools take
+    ``dst_scales`` / ``src_scales`` = (k_scales, v_scales) pairs."""
+    lib = load_library()
+    for t, n in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_k, "src_k"), (src_v, "src_v"),
+                 (block_mapping, "block_mapping")):
+        _gpu_visible(t, n)
+    _require(dst_k.dim() == 4 and dst_v.shape == dst_k.shape and src_k.dim() == 4
+             and src_v.shape == src_k.shape and src_k.shape[1:] == dst_k.shape[1:],
+             "pools must be [N, H, BS, D] with matching H, BS, D")
+    _require(len({dst_k.dtype, dst_v.dtype, src_k.dtype, src_v.dtype}) == 1, "one dtype for all pools")
+    dt = dst_k.dtype
+    _require(dt in DTYPE_CODES or dt in FP8_CODES, f"unsupported dtype {dt}")
+    code = DTYPE_CODES.get(dt, FP8_CODES.get(dt))
+    _, H, BS, D = dst_k.shape
+    ptrs = [None] * 4
+    if dt in FP8_CODES:
+        _require(dst_scales is not None and src_scales is not None, "8-bit pools need their scales")
+        for (t, n), N in zip(((dst_scales[0], "dst k_scales"), (dst_scales[1], "dst v_scales"),
+                               (src_scales[0], "src k_scales"), (src_scales[1], "src v_scales")),
+                              (dst_k.shape[0],) * 2 + (src_k.shape[0],) * 2):
+            _gpu_visible(t, n)
+            _require(t.dtype == torch.float32 and t.shape == (N, H), f"{n} must be float32 [N, H]")
+        ptrs = [dst_scales[0].data_ptr(), dst_scales[1].data_ptr(), src_scales[0].data_ptr(),
+                src_scales[1].data_ptr()]
+    _require(block_mapping.dtype == torch.int32 and block_mapping.dim() == 2
+             and block_mapping.shape[1] == 2, "block_mapping must be int32 [n, 2]")
+    if device is None:
+        device = next((t.device for t in (dst_k, src_k, block_mapping) if t.is_cuda),
+                      torch.device("cuda", torch.cuda.current_device()))
+    with torch.cuda.device(device):
+        st = lib.pa_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(),
+                                src_v.data_ptr(), *ptrs, block_mapping.data_ptr(),
+                                block_mapping.shape[0], H, D, BS, src_k.shape[0], dst_k.shape[0],
+                                code, _stream_handle(device, stream))
+    _check("pa_swap_blocks", st)

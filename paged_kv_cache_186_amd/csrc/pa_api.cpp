@@ -158,25 +158,57 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-// Shared by pa_copy_blocks (no scales) and pa_copy_blocks_fp8; e = element bytes.
-pa_status_t copy_impl(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
-                      const int32_t* block_mapping, int32_t num_pairs, int32_t num_heads,
-                      int32_t head_dim, int32_t block_size, int32_t num_blocks, int e,
-                      void* stream) {
-  if (num_pairs < 0 || num_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
-  if (num_pairs == 0) return PA_OK;
-  if (!k_pool || !v_pool || !block_mapping) return PA_ERR_INVALID_ARG;
-  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_mapping, 4))
+// The address under which the GPU reaches *p: device memory as is; pinned
+// host memory through the device pointer its mapping has (HIP reports it).
+// Anything else — pageable host memory, an unknown address — is refused
+// here, on the host, instead of faulting in a kernel.
+template <typename P>
+bool device_view(P*& p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the caller
+    return false;
+  }
+  if (at.type == hipMemoryTypeHost) {
+    if (at.devicePointer == nullptr) return false;
+    p = static_cast<P*>(at.devicePointer);
+  } else if (at.type != hipMemoryTypeDevice) {
+    return false;
+  }
+  return true;
+}
+
+// Shared by pa_copy_blocks, pa_copy_blocks_fp8 and pa_swap_blocks; e =
+// element bytes.  The caller has checked dtype and shape.  With host_ok the
+// pools, the scales and the mapping may be pinned host memory.
+pa_status_t copy_impl(const pa::CopyArgs& c, int32_t num_pairs, int32_t head_dim,
+                      int32_t block_size, int e, void* stream, bool host_ok = false) {
+  if (num_pairs < 0 || c.num_heads <= 0 || c.src_blocks <= 0 || c.dst_blocks <= 0)
     return PA_ERR_INVALID_ARG;
-  const size_t block_bytes = static_cast<size_t>(num_heads) * block_size * head_dim * e;
-  const size_t chunks = (block_bytes + pa::kCopyChunkBytes - 1) / pa::kCopyChunkBytes;
+  if (num_pairs == 0) return PA_OK;
+  if (!c.dst_k || !c.dst_v || !c.src_k || !c.src_v || !c.block_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(c.dst_k, 16) || !aligned(c.dst_v, 16) || !aligned(c.src_k, 16) ||
+      !aligned(c.src_v, 16) || !aligned(c.block_mapping, 4))
+    return PA_ERR_INVALID_ARG;
+  pa::CopyArgs a = c;
+  a.num_pairs = num_pairs;
+  a.block_bytes = static_cast<size_t>(c.num_heads) * block_size * head_dim * e;
+  const size_t chunks = (a.block_bytes + pa::kCopyChunkBytes - 1) / pa::kCopyChunkBytes;
   if (chunks * static_cast<size_t>(num_pairs) > static_cast<size_t>(INT_MAX))
     return PA_ERR_INVALID_ARG;
-  const hipError_t err =
-      pa::launch_copy_blocks(k_pool, v_pool, k_scales, v_scales, block_mapping, num_pairs,
-                             block_bytes, num_blocks, num_heads, static_cast<hipStream_t>(stream));
+  if (host_ok) {
+    if (!device_view(a.dst_k) || !device_view(a.dst_v) || !device_view(a.src_k) ||
+        !device_view(a.src_v) || !device_view(a.block_mapping))
+      return PA_ERR_INVALID_ARG;
+    if (a.src_ks && (!device_view(a.dst_ks) || !device_view(a.dst_vs) || !device_view(a.src_ks) ||
+                     !device_view(a.src_vs)))
+      return PA_ERR_INVALID_ARG;
+  }
+  const hipError_t err = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
+
+bool scales_ok(const float* a, const float* b) { return a && b && aligned(a, 4) && aligned(b, 4); }
 
 }  // namespace
 
@@ -261,8 +293,9 @@ pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapp
                            void* stream) {
   const int e = elem_bytes(dtype);
   if (e == 0 || !supported_shape(head_dim, block_size)) return PA_ERR_UNSUPPORTED;
-  return copy_impl(k_pool, v_pool, nullptr, nullptr, block_mapping, num_pairs, num_heads,
-                   head_dim, block_size, num_blocks, e, stream);
+  const pa::CopyArgs c{k_pool,  v_pool,  k_pool,        v_pool,   nullptr,    nullptr,  nullptr,
+                       nullptr, block_mapping, 0, 0, num_blocks, num_blocks, num_heads};
+  return copy_impl(c, num_pairs, head_dim, block_size, e, stream);
 }
 
 pa_status_t pa_reshape_and_cache_fp8(void* k_pool, void* v_pool, const float* k_scales,
@@ -294,10 +327,39 @@ pa_status_t pa_copy_blocks_fp8(void* k_pool, void* v_pool, float* k_scales, floa
                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                pa_dtype_t kv_dtype, void* stream) {
   if (!is_fp8(kv_dtype) || !supported_shape(head_dim, block_size)) return PA_ERR_UNSUPPORTED;
-  if (num_pairs > 0 && (!k_scales || !v_scales || !aligned(k_scales, 4) || !aligned(v_scales, 4)))
+  if (num_pairs > 0 && !scales_ok(k_scales, v_scales)) return PA_ERR_INVALID_ARG;
+  const pa::CopyArgs c{k_pool,   v_pool,   k_pool,        v_pool, k_scales,   v_scales,  k_scales,
+                       v_scales, block_mapping, 0, 0, num_blocks, num_blocks, num_heads};
+  return copy_impl(c, num_pairs, head_dim, block_size, 1, stream);
+}
+
+pa_status_t pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                           float* dst_k_scales, float* dst_v_scales, const float* src_k_scales,
+                           const float* src_v_scales, const int32_t* block_mapping,
+                           int32_t num_pairs, int32_t num_heads, int32_t head_dim,
+                           int32_t block_size, int32_t src_num_blocks, int32_t dst_num_blocks,
+                           pa_dtype_t dtype, void* stream) {
+  const int e = is_fp8(dtype) ? 1 : elem_bytes(dtype);
+  if (e == 0 || !supported_shape(head_dim, block_size)) return PA_ERR_UNSUPPORTED;
+  if (is_fp8(dtype) && num_pairs > 0 &&
+      (!scales_ok(dst_k_scales, dst_v_scales) || !scales_ok(src_k_scales, src_v_scales)))
     return PA_ERR_INVALID_ARG;
-  return copy_impl(k_pool, v_pool, k_scales, v_scales, block_mapping, num_pairs, num_heads,
-                   head_dim, block_size, num_blocks, 1, stream);
+  const bool fp8 = is_fp8(dtype);
+  const pa::CopyArgs c{dst_k,
+                       dst_v,
+                       src_k,
+                       src_v,
+                       fp8 ? dst_k_scales : nullptr,
+                       fp8 ? dst_v_scales : nullptr,
+                       fp8 ? src_k_scales : nullptr,
+                       fp8 ? src_v_scales : nullptr,
+                       block_mapping,
+                       0,
+                       0,
+                       src_num_blocks,
+                       dst_num_blocks,
+                       num_heads};
+  return copy_impl(c, num_pairs, head_dim, block_size, e, stream, /*host_ok=*/true);
 }
 
 }  // extern "C"

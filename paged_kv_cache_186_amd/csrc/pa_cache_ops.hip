@@ -95,29 +95,36 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_fp8_kernel(
   }
 }
 
-// Copy-on-write copy: pool[dst] = pool[src] for every {src, dst} pair, for both
-// pools (blockIdx.y selects K or V), and for an 8-bit cache the block's
-// per-head scales too.  Grid x enumerates (pair, 16 KiB chunk).  Source: page
-// "mlx-paged-attention: Bringing vLLM-level High Throughput Inference to Apple
-// Silicon", core feature 2.  Pairs naming an id outside the pool are skipped.
+// Whole-block copy from a source pool pair to a destination pool pair:
+// dst[d] = src[s] for every {s, d} pair, in the K and V pools (blockIdx.y
+// selects which), and for an 8-bit cache the block's per-head scales too.
+// Grid x enumerates (pair, 16 KiB chunk).  Source and destination are the
+// same pools for copy-on-write (page "mlx-paged-attention: Bringing vLLM-level
+// High Throughput Inference to Apple Silicon", core feature 2) and different
+// pools — one of them in GPU-mapped pinned host memory — for swapping a
+// sequence's cache out and back in (page "PagedAttention MLX：为Apple
+// Silicon打造的高吞吐量LLM推理引擎", dynamic scheduling and the physical KV
+// pool's swap-out).  Every chunk is read into registers before any of it is
+// written, and many chunks are in flight at once, which is what a host link
+// needs to run at speed.  Pairs naming an id outside either pool are skipped.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
-    char* __restrict__ k_pool, char* __restrict__ v_pool, float* __restrict__ k_scales,
-    float* __restrict__ v_scales, const int32_t* __restrict__ block_mapping, size_t block_bytes,
-    int chunks_per_block, int num_blocks, int num_heads) {
+    char* dst_k, char* dst_v, const char* src_k, const char* src_v, float* dst_ks, float* dst_vs,
+    const float* src_ks, const float* src_vs, const int32_t* __restrict__ block_mapping,
+    size_t block_bytes, int chunks_per_block, int src_blocks, int dst_blocks, int num_heads) {
   const int pair = blockIdx.x / chunks_per_block;
   const int chunk = blockIdx.x % chunks_per_block;
-  char* pool = blockIdx.y ? v_pool : k_pool;
   const int src = block_mapping[2 * pair + 0];
   const int dst = block_mapping[2 * pair + 1];
-  if (static_cast<unsigned>(src) >= static_cast<unsigned>(num_blocks) ||
-      static_cast<unsigned>(dst) >= static_cast<unsigned>(num_blocks))
+  if (static_cast<unsigned>(src) >= static_cast<unsigned>(src_blocks) ||
+      static_cast<unsigned>(dst) >= static_cast<unsigned>(dst_blocks))
     return;
-  float* scales = blockIdx.y ? v_scales : k_scales;
-  if (scales != nullptr && chunk == 0)
+  const float* sscale = blockIdx.y ? src_vs : src_ks;
+  float* dscale = blockIdx.y ? dst_vs : dst_ks;
+  if (sscale != nullptr && chunk == 0)
     for (int i = threadIdx.x; i < num_heads; i += kThreads)
-      scales[static_cast<size_t>(dst) * num_heads + i] = scales[static_cast<size_t>(src) * num_heads + i];
-  const char* from = pool + static_cast<size_t>(src) * block_bytes;
-  char* to = pool + static_cast<size_t>(dst) * block_bytes;
+      dscale[static_cast<size_t>(dst) * num_heads + i] = sscale[static_cast<size_t>(src) * num_heads + i];
+  const char* from = (blockIdx.y ? src_v : src_k) + static_cast<size_t>(src) * block_bytes;
+  char* to = (blockIdx.y ? dst_v : dst_k) + static_cast<size_t>(dst) * block_bytes;
   const size_t base = static_cast<size_t>(chunk) * kCopyChunk + threadIdx.x * kVecBytes;
   u32x4 v[kCopyVecs];
 #pragma unroll
@@ -146,13 +153,13 @@ hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_ne
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
-                              const int32_t* block_mapping, int num_pairs, size_t block_bytes,
-                              int num_blocks, int num_heads, hipStream_t stream) {
-  const int chunks = static_cast<int>((block_bytes + kCopyChunk - 1) / kCopyChunk);
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs * chunks, 2), dim3(kThreads), 0, stream,
-                     static_cast<char*>(k_pool), static_cast<char*>(v_pool), k_scales, v_scales,
-                     block_mapping, block_bytes, chunks, num_blocks, num_heads);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream) {
+  const int chunks = static_cast<int>((a.block_bytes + kCopyChunk - 1) / kCopyChunk);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs * chunks, 2), dim3(kThreads), 0, stream,
+                     static_cast<char*>(a.dst_k), static_cast<char*>(a.dst_v),
+                     static_cast<const char*>(a.src_k), static_cast<const char*>(a.src_v), a.dst_ks,
+                     a.dst_vs, a.src_ks, a.src_vs, a.block_mapping, a.block_bytes, chunks,
+                     a.src_blocks, a.dst_blocks, a.num_heads);
   return hipGetLastError();
 }
 

@@ -128,11 +128,24 @@ hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_ne
                                     const int32_t* slot_mapping, int num_tokens, int num_heads,
                                     int row_bytes, int block_size, int num_blocks, hipStream_t stream);
 
-// k_scales / v_scales: [num_blocks][num_heads] per-block scales copied along
-// with the blocks (8-bit pools), or null.
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, float* k_scales, float* v_scales,
-                              const int32_t* block_mapping, int num_pairs, size_t block_bytes,
-                              int num_blocks, int num_heads, hipStream_t stream);
+// Whole-block copies src[s] -> dst[d] (K and V pools); the pools may be the
+// same (copy-on-write) or different (swap to / from host memory).  Scales:
+// [blocks][num_heads] per-block scales copied along (8-bit pools), or null.
+struct CopyArgs {
+  void* dst_k;
+  void* dst_v;
+  const void* src_k;
+  const void* src_v;
+  float* dst_ks;
+  float* dst_vs;
+  const float* src_ks;
+  const float* src_vs;
+  const int32_t* block_mapping;
+  int num_pairs;
+  size_t block_bytes;
+  int src_blocks, dst_blocks, num_heads;
+};
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 
 struct ReshapeFp8Args {
   void* k_pool;

@@ -26,7 +26,8 @@ def test_every_declared_function_is_exported(lib):
     declared = B.header_functions()
     assert set(declared) == {"pa_abi_version", "pa_status_string", "pa_decode_workspace_size",
                              "pa_decode", "pa_reshape_and_cache", "pa_copy_blocks",
-                             "pa_decode_fp8", "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8"}
+                             "pa_decode_fp8", "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8",
+                             "pa_swap_blocks"}
     raw = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
         assert hasattr(raw, name), name
@@ -228,3 +229,25 @@ def test_copy_blocks_fp8_rejects_before_launch(lib, kw, status):
     a.update(kw)
     assert lib.pa_copy_blocks_fp8(a["k"], a["v"], a["ks"], a["vs"], a["bm"], a["n"], a["H"], a["D"],
                                   a["bs"], a["N"], a["kvdt"], None) == status
+
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), UNSUPPORTED),
+    (dict(D=96), UNSUPPORTED),
+    (dict(dt=E4M3, dks=None), INVALID),            # 8-bit pools need every scale pointer
+    (dict(dt=E5M2, svs=FAKE + 2), INVALID),
+    (dict(dk=MISALIGNED), INVALID),
+    (dict(sk=None), INVALID),
+    (dict(bm=None), INVALID),
+    (dict(sN=0), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(n=0, sk=None), OK),
+])
+def test_swap_blocks_rejects_before_launch(lib, kw, status):
+    a = dict(dk=FAKE, dv=FAKE, sk=FAKE, sv=FAKE, dks=FAKE, dvs=FAKE, sks=FAKE, svs=FAKE, bm=FAKE,
+             n=2, H=4, D=64, bs=16, sN=16, dN=16, dt=F16)
+    a.update(kw)
+    assert lib.pa_swap_blocks(a["dk"], a["dv"], a["sk"], a["sv"], a["dks"], a["dvs"], a["sks"],
+                              a["svs"], a["bm"], a["n"], a["H"], a["D"], a["bs"], a["sN"], a["dN"],
+                              a["dt"], None) == status
