@@ -44,6 +44,7 @@ from .paged_attention import (  # noqa: F401
     reshape_and_cache_ref,
     copy_blocks_ref,
     swap_blocks_ref,
+    decode_gqa_ref,
 )
 from .fp8 import (  # noqa: F401
     fp8_values,

@@ -34,6 +34,10 @@ Pin status (tests/test_oracle.py):
   are read back in logical order by the gather; untouched bytes unchanged.
 * ``copy_blocks_ref`` — pinned: destination bytes equal source bytes, all
   other blocks unchanged, and copy-on-write leaves decode output bit-identical.
+* ``decode_gqa_ref`` — pinned: torch ``scaled_dot_product_attention`` with
+  ``enable_gqa`` in float64 on contiguous caches; equal to ``decode_ref`` on
+  pools whose K/V heads are repeated G times (numpy ``repeat``) and when
+  there is one query head per K/V head.
 * ``swap_blocks_ref`` — pinned: a swap out and back in restores the cache
   bit for bit and decode over it is unchanged; untouched blocks unchanged.
 """
@@ -230,3 +234,32 @@ def swap_blocks_ref(dst_k, dst_v, src_k, src_v, block_mapping):
         k_out[int(dst)] = src_k[int(src)]
         v_out[int(dst)] = src_v[int(src)]
     return k_out, v_out
+
+
+def decode_gqa_ref(q, k_pool, v_pool, block_tables, context_lens, scale: float,
+                   block_size: int) -> np.ndarray:
+    """``decode_ref`` with fewer K/V heads than query heads (grouped-query
+    attention): the pools hold Hkv heads, q holds H = G * Hkv, and query head h
+    attends over K/V head h // G (contiguous groups).  The pages only have one
+    head count (usage example of "PagedAttention MLX：为Apple Silicon打造的高吞吐量
+    LLM推理引擎"); the grouping is this library's generalization, and the
+    attention of each query head is exactly ``decode_ref``'s.  float64 [S, H, D]."""
+    qf = _as_f64(q)
+    S, H, D = qf.shape
+    Hkv = k_pool.shape[1]
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of K/V heads")
+    G = H // Hkv
+    tables = _as_int(block_tables)
+    lens = _as_int(context_lens)
+    out = np.zeros((S, H, D), dtype=np.float64)
+    for s in range(S):
+        L = int(lens[s])
+        if L == 0:
+            continue
+        for h in range(H):
+            K, V = gather_sequence_kv(k_pool, v_pool, tables[s], L, h // G, block_size)
+            z = scale * (K @ qf[s, h])
+            w = np.exp(z - z.max())
+            out[s, h] = (w @ V) / w.sum()
+    return out

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (copy_blocks_ref, decode_ref, gather_sequence_kv, swap_blocks_ref,
+from oracle import (copy_blocks_ref, decode_gqa_ref, decode_ref, gather_sequence_kv, swap_blocks_ref,
                     lse_merge_ref, reshape_and_cache_ref, split_decode_ref)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -396,3 +396,32 @@ def test_swap_out_and_back_restores_the_cache_and_the_decode():
     t2[2, :nb] = free
     after = decode_ref(q, k3, v3, t2, lens, 0.5, bs)
     np.testing.assert_array_equal(after, before)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 1), (4, 2), (6, 3), (8, 2), (3, 3)])
+def test_gqa_decode_matches_torch_sdpa_with_grouped_heads(H, Hkv):
+    """torch's scaled_dot_product_attention with enable_gqa (float64, on the
+    contiguous cache) is an independent implementation of grouped heads."""
+    rng = np.random.default_rng(40 + H + Hkv)
+    lens = [1, 9, 20]
+    q, Kc, Vc, k_pool, v_pool, tables, lens, bs = _random_case(41, lens=lens, H=Hkv, D=8, bs=4)
+    q = rng.standard_normal((len(lens), H, 8))
+    out = decode_gqa_ref(q, k_pool, v_pool, tables, lens, 0.6, bs)
+    for s, L in enumerate(lens):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[s][None, :, None, :]), torch.from_numpy(Kc[s][None]),
+            torch.from_numpy(Vc[s][None]), scale=0.6, enable_gqa=True)[0, :, 0, :].numpy()
+        np.testing.assert_allclose(out[s], ref, rtol=0, atol=1e-12)
+
+
+def test_gqa_decode_equals_mha_decode_on_repeated_heads():
+    q, Kc, Vc, k_pool, v_pool, tables, lens, bs = _random_case(42, H=2, D=8, bs=4)
+    q4 = np.random.default_rng(43).standard_normal((len(lens), 6, 8))
+    got = decode_gqa_ref(q4, k_pool, v_pool, tables, lens, 0.3, bs)
+    want = decode_ref(q4, np.repeat(k_pool, 3, axis=1), np.repeat(v_pool, 3, axis=1), tables, lens, 0.3, bs)
+    np.testing.assert_array_equal(got, want)
+    # one query head per K/V head is plain decode
+    np.testing.assert_array_equal(decode_gqa_ref(q, k_pool, v_pool, tables, lens, 0.3, bs),
+                                  decode_ref(q, k_pool, v_pool, tables, lens, 0.3, bs))
+    with pytest.raises(ValueError):
+        decode_gqa_ref(q4[:, :5], k_pool, v_pool, tables, lens, 0.3, bs)

@@ -261,3 +261,53 @@ def test_swap_pins():
     assert _swap_pins(swap_blocks_ref)
     for mutant in (_swap_reversed, _swap_k_only, _swap_dst_off_by_one):
         assert not _swap_pins(mutant), mutant.__name__
+
+
+
+# ---- mutants of the grouped-query head mapping ---------------------------------
+
+from oracle import decode_gqa_ref  # noqa: E402
+from test_oracle import _random_case as _rc  # noqa: E402
+
+
+def _gqa_pins(fn) -> bool:
+    try:
+        q, Kc, Vc, k_pool, v_pool, tables, lens, bs = _rc(44, lens=(3, 17), H=2, D=4, bs=4)
+        q6 = np.random.default_rng(45).standard_normal((2, 6, 4))
+        out = fn(q6, k_pool, v_pool, tables, lens, 0.5, bs)
+        for s in range(2):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q6[s][None, :, None, :]), torch.from_numpy(Kc[s][None]),
+                torch.from_numpy(Vc[s][None]), scale=0.5, enable_gqa=True)[0, :, 0, :].numpy()
+            if not np.allclose(out[s], ref, rtol=0, atol=1e-12):
+                return False
+        return True
+    except (IndexError, ValueError):
+        return False
+
+
+def _gqa_with_map(head_of):
+    def fn(q, k_pool, v_pool, block_tables, context_lens, scale, block_size):
+        qf = opa._as_f64(q)
+        S, H, D = qf.shape
+        Hkv = k_pool.shape[1]
+        out = np.zeros((S, H, D))
+        for s in range(S):
+            L = int(context_lens[s])
+            for h in range(H):
+                K, V = opa.gather_sequence_kv(k_pool, v_pool, block_tables[s], L, head_of(h, H, Hkv),
+                                              block_size)
+                z = scale * (K @ qf[s, h])
+                w = np.exp(z - z.max())
+                out[s, h] = (w @ V) / w.sum()
+        return out
+    return fn
+
+
+def test_gqa_pins():
+    assert _gqa_pins(decode_gqa_ref)
+    assert _gqa_pins(_gqa_with_map(lambda h, H, Hkv: h // (H // Hkv)))   # the builder, no slip
+    for name, m in (("interleaved h % Hkv", lambda h, H, Hkv: h % Hkv),
+                    ("group of the next head", lambda h, H, Hkv: min((h + 1) // (H // Hkv), Hkv - 1)),
+                    ("always K/V head 0", lambda h, H, Hkv: 0)):
+        assert not _gqa_pins(_gqa_with_map(m)), name
