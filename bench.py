@@ -39,8 +39,10 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published peak
 COLD_BYTES = 2 << 30           # replica footprint that defeats the 256 MB last-level cache
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
-                  for f in ("pa_decode.hip", "pa_decode_balanced.hip", "pa_attend.h",
-                            "pa_device.h", "pa_internal.h", "pa_api.cpp")]
+                  for f in ("pa_decode.hip", "pa_decode_balanced.hip", "pa_decode_balanced_gqa2.hip",
+                            "pa_decode_balanced_gqa4.hip", "pa_decode_balanced_gqa8.hip",
+                            "pa_balanced_kernel.h", "pa_attend.h", "pa_device.h", "pa_internal.h",
+                            "pa_api.cpp")]
 
 
 def log(msg: str) -> None:
@@ -55,17 +57,20 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def decode_bytes(lens: np.ndarray, H: int, D: int, e: int, bs: int, e_kv: int = 0) -> int:
-    """Algorithmic bytes of one decode: K+V rows read (e_kv bytes per element,
-    default e), q read, out written (e bytes), the used block-table entries and
+def decode_bytes(lens: np.ndarray, H: int, D: int, e: int, bs: int, e_kv: int = 0,
+                 Hkv: int = 0) -> int:
+    """Algorithmic bytes of one decode: K+V rows of the Hkv K/V heads read
+    (e_kv bytes per element, default e; Hkv defaults to H), q read and out
+    written for the H query heads (e bytes), the used block-table entries and
     the lengths; an 8-bit cache (e_kv == 1) also reads the K and V scale of
-    every (block, head) it visits."""
+    every (block, K/V head) it visits."""
     e_kv = e_kv or e
+    Hkv = Hkv or H
     lens = lens.astype(np.int64)
     S = len(lens)
     nb = -(-lens // bs)
-    scales = 2 * 4 * int(nb.sum()) * H if e_kv == 1 else 0
-    return int(lens.sum() * H * D * 2 * e_kv + 2 * S * H * D * e + 4 * nb.sum() + 4 * S + scales)
+    scales = 2 * 4 * int(nb.sum()) * Hkv if e_kv == 1 else 0
+    return int(lens.sum() * Hkv * D * 2 * e_kv + 2 * S * H * D * e + 4 * nb.sum() + 4 * S + scales)
 
 
 def reshape_bytes(T: int, H: int, D: int, e: int, e_kv: int = 0) -> int:
@@ -76,8 +81,10 @@ def reshape_bytes(T: int, H: int, D: int, e: int, e_kv: int = 0) -> int:
     return 2 * T * H * D * e + 2 * T * H * D * e_kv + 4 * T + scales
 
 
-def profile_path(workload: str, kv: str) -> str:
+def profile_path(workload: str, kv: str, kv_heads: int = 0) -> str:
     tag = workload if kv == "native" else f"{workload}_fp8_{kv}"
+    if kv_heads:
+        tag += f"_kvh{kv_heads}"
     return os.path.join(PROFILES, f"pa_decode_{tag}_traffic.txt")
 
 
@@ -197,7 +204,8 @@ def calibration_copy(pa, dev) -> None:
 def cpu_baseline(w_host, k_new, v_new, slots, step_bytes: int, seconds: float) -> dict:
     """The float64 oracle, as it stands, on the host: one thread, same step."""
     from threadpoolctl import threadpool_limits
-    from oracle import decode_fp8_ref, decode_ref, reshape_and_cache_fp8_ref, reshape_and_cache_ref
+    from oracle import (decode_gqa_ref, decode_ref, dequant_ref, reshape_and_cache_fp8_ref,
+                        reshape_and_cache_ref)
     torch.set_num_threads(1)
     lens = w_host["lens"]
     fmt = w_host["fmt"]
@@ -206,14 +214,14 @@ def cpu_baseline(w_host, k_new, v_new, slots, step_bytes: int, seconds: float) -
     with threadpool_limits(limits=1):
         while True:
             t0 = time.perf_counter()
+            dec = decode_gqa_ref if w_host["gqa"] else decode_ref
             if fmt is None:
                 kp, vp = reshape_and_cache_ref(w_host["k"], w_host["v"], k_new, v_new, slots, w_host["bs"])
-                decode_ref(w_host["q"], kp, vp, w_host["tables"], lens, w_host["scale"], w_host["bs"])
             else:
-                kp, vp = reshape_and_cache_fp8_ref(w_host["k"], w_host["v"], w_host["ks"], w_host["vs"],
+                kc, vc = reshape_and_cache_fp8_ref(w_host["k"], w_host["v"], w_host["ks"], w_host["vs"],
                                                    k_new, v_new, slots, w_host["bs"], fmt)
-                decode_fp8_ref(w_host["q"], kp, vp, w_host["ks"], w_host["vs"], w_host["tables"], lens,
-                               w_host["scale"], w_host["bs"], fmt)
+                kp, vp = dequant_ref(kc, w_host["ks"], fmt), dequant_ref(vc, w_host["vs"], fmt)
+            dec(w_host["q"], kp, vp, w_host["tables"], lens, w_host["scale"], w_host["bs"])
             times.append(time.perf_counter() - t0)
             if time.perf_counter() >= t_end and len(times) >= 1:
                 break
@@ -321,6 +329,9 @@ def main() -> int:
                          "(OCP E4M3 / E5M2 with per-block, per-head scales; q and out keep their dtype)")
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
     ap.add_argument("--replicas", type=int, default=0, help="KV pool replicas (0 = enough for 2 GiB)")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="K/V heads (0 = as many as query heads); fewer runs grouped-query decode "
+                         "(pa_decode_gqa) over the first kv-heads heads of the pools")
     ap.add_argument("--op", default="decode", choices=["decode", "swap"],
                     help="decode: the decode step (default); swap: pa_swap_blocks over the host link")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -345,6 +356,14 @@ def main() -> int:
     from paged_kv_cache_186_amd import workloads as W
     log(f"building workload {args.workload} (seed {args.seed})")
     w = build_workload(args.workload, args.seed, dev)
+    Hkv = args.kv_heads or w.num_heads
+    gqa = Hkv != w.num_heads
+    if gqa:
+        if w.num_heads % Hkv:
+            raise SystemExit(f"--kv-heads {Hkv} does not divide {w.num_heads} query heads")
+        w.k_pool = w.k_pool[:, :Hkv].contiguous()
+        w.v_pool = w.v_pool[:, :Hkv].contiguous()
+        torch.cuda.empty_cache()
     fp8 = args.kv != "native"
     host = None
     if fp8:
@@ -356,7 +375,7 @@ def main() -> int:
         torch.cuda.empty_cache()
     elif not args.no_cpu_baseline:
         host = {"k": w.k_pool.cpu(), "v": w.v_pool.cpu()}
-    log(describe(w) + (f", KV cache fp8 {args.kv}" if fp8 else ""))
+    log(describe(w) + (f", KV cache fp8 {args.kv}" if fp8 else "") + (f", {Hkv} K/V heads" if gqa else ""))
     e = w.q.element_size()
     e_kv = 1 if fp8 else e
     S, H, D, bs = w.num_seqs, w.num_heads, w.head_dim, w.block_size
@@ -369,6 +388,7 @@ def main() -> int:
     slots = [w.manager.slot_of(s, int(lens[i]) - 1) for i, s in enumerate(w.seq_ids)]
     q = w.q
     _, k_new, v_new = W.new_token_values(w, 0)
+    k_new, v_new = k_new[:, :Hkv].contiguous(), v_new[:, :Hkv].contiguous()
     slot_t = torch.tensor(slots, dtype=torch.int32, device=dev)
 
     base = (kc, vc, ks, vs) if fp8 else (w.k_pool, w.v_pool)
@@ -377,7 +397,9 @@ def main() -> int:
     log(f"pool K+V {pool_bytes / 2**20:.0f} MiB; {R} replica(s) for cold-cache timing")
     reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
     out = torch.empty_like(q)
-    ws_bytes = pa.pa_decode_workspace_size(S, H, D, w.table_width, bs, args.partition)
+    ws_bytes = (pa.pa_decode_gqa_workspace_size(S, H, Hkv, D, w.table_width, bs, args.partition, q.dtype,
+                                                 base[0].dtype) if gqa
+                else pa.pa_decode_workspace_size(S, H, D, w.table_width, bs, args.partition))
     ws = pa.new_workspace(ws_bytes, dev)
 
     calibration_copy(pa, dev)
@@ -389,7 +411,12 @@ def main() -> int:
             pa.pa_reshape_and_cache(*reps[i % R], k_new, v_new, slot_t)
 
     def decode(i):
-        if fp8:
+        if gqa:
+            kp, vp = reps[i % R][:2]
+            kss, vss = (reps[i % R][2:] if fp8 else (None, None))
+            pa.pa_decode_gqa(out, q, kp, vp, tables, clens, w.scale, bs, k_scales=kss, v_scales=vss,
+                             partition_size=args.partition, workspace=ws)
+        elif fp8:
             kp, vp, kss, vss = reps[i % R]
             pa.pa_decode_fp8(out, q, kp, vp, kss, vss, tables, clens, w.scale, bs,
                              partition_size=args.partition, workspace=ws)
@@ -420,13 +447,13 @@ def main() -> int:
     warm_ms = time_graph(warm_graph, n_rep, stream) / R
     n_steps = n_rep * R
 
-    b_dec = decode_bytes(lens, H, D, e, bs, e_kv)
-    b_res = reshape_bytes(S, H, D, e, e_kv)
+    b_dec = decode_bytes(lens, H, D, e, bs, e_kv, Hkv)
+    b_res = reshape_bytes(S, Hkv, D, e, e_kv)
     step_s = step_ms * 1e-3
     value = (b_dec + b_res) / step_s / 1e9
     dec_gbs = b_dec / (dec_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
-    traffic = traffic_from_profile(digest, profile_path(args.workload, args.kv))
+    traffic = traffic_from_profile(digest, profile_path(args.workload, args.kv, Hkv if gqa else 0))
 
     result = {
         "metric": METRIC,
@@ -448,6 +475,7 @@ def main() -> int:
             "num_seqs": S, "num_heads": H, "head_dim": D, "block_size": bs,
             "context_tokens": int(lens.sum()),
             "kv_cache": "native" if not fp8 else f"fp8 {args.kv} + fp32 scale per (block, head)",
+            "kv_heads": Hkv,
             "split": ("balanced (partition_size 0)" if args.partition == 0
                       else f"partitions of {args.partition} tokens"),
             "accumulate": "f32",
@@ -473,7 +501,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s on one host thread")
         host.update({"q": q.cpu(), "tables": w.block_tables_np(), "lens": lens, "scale": w.scale,
-                     "bs": bs, "fmt": args.kv if fp8 else None})
+                     "bs": bs, "fmt": args.kv if fp8 else None, "gqa": gqa})
         result["cpu_baseline"] = cpu_baseline(host, k_new.cpu(), v_new.cpu(), slots,
                                               b_dec + b_res, args.cpu_seconds)
     print(json.dumps(result), flush=True)

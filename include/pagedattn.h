@@ -176,6 +176,38 @@ pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapp
                            void* stream);
 
 /*
+ * ---- Grouped-query attention -----------------------------------------------
+ * pa_decode with fewer K/V heads than query heads (grouped-query attention;
+ * multi-query attention is num_kv_heads == 1): query head h attends over K/V
+ * head h / (num_heads / num_kv_heads), the usual contiguous grouping.  The
+ * pages only have num_heads (usage example of "PagedAttention MLX：为Apple
+ * Silicon打造的高吞吐量LLM推理引擎"); this generalization is the library's.
+ * Pools are [num_blocks][num_kv_heads][block_size][head_dim] (scales, for an
+ * 8-bit cache, [num_blocks][num_kv_heads]); q and out are
+ * [num_seqs][num_heads][head_dim].  kv_dtype is q_dtype (F32, F16, BF16) or,
+ * for F16 / BF16 queries, an 8-bit format (then k_scales / v_scales are
+ * required, else ignored).  num_heads must be a multiple of num_kv_heads.
+ * With the default split (partition_size 0, num_seqs <= 2048) and 16-bit
+ * queries, one K/V tile load serves 8, 4 or 2 query heads of a group (the
+ * largest dividing the group size; at most 4 with an 8-bit cache); otherwise
+ * every query head reads its K/V head's tiles itself.  Workspace: pa_decode_gqa_workspace_size() for the
+ * same arguments; same contract as pa_decode_workspace_size().
+ */
+size_t pa_decode_gqa_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t partition_size,
+                                    pa_dtype_t q_dtype, pa_dtype_t kv_dtype);
+
+pa_status_t pa_decode_gqa(void* out, const void* q, const void* k_pool, const void* v_pool,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          float scale, int32_t block_size,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t num_blocks, int32_t max_blocks_per_seq,
+                          int32_t partition_size, pa_dtype_t q_dtype, pa_dtype_t kv_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Copy whole blocks from one pool pair to another (K and V):
  *   dst_k[d] = src_k[s], dst_v[d] = src_v[s]     for each {s, d} of block_mapping
  * — swapping an inactive sequence's blocks out to host memory and back in

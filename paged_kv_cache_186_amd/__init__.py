@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     pa_copy_blocks_fp8,
     pa_decode,
     pa_decode_fp8,
+    pa_decode_gqa,
+    pa_decode_gqa_workspace_size,
     pa_decode_workspace_size,
     pa_reshape_and_cache,
     pa_reshape_and_cache_fp8,

@@ -45,6 +45,9 @@ _SIGNATURES = {
     "pa_reshape_and_cache_fp8": (_c_int, [_c_void] * 7 + [_c_int] * 5 + [_c_int, _c_int, _c_void]),
     "pa_copy_blocks_fp8": (_c_int, [_c_void] * 5 + [_c_int] * 5 + [_c_int, _c_void]),
     "pa_swap_blocks": (_c_int, [_c_void] * 9 + [_c_int] * 6 + [_c_int, _c_void]),
+    "pa_decode_gqa_workspace_size": (_c_size, [_c_int] * 7 + [_c_int, _c_int]),
+    "pa_decode_gqa": (_c_int, [_c_void] * 8 + [_c_float] + [_c_int] * 8 + [_c_int, _c_int]
+                      + [_c_void, _c_size, _c_void]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -136,8 +139,8 @@ def _cached_workspace(device, stream_handle: int, rows: int, need: int) -> torch
 
 
 def _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, block_size, partition_size,
-                 workspace, stream):
-    """Shared checks of pa_decode / pa_decode_fp8; returns (S, H, D, W, ws_ptr, ws_bytes, stream)."""
+                 workspace, stream, need_fn=None):
+    """Shared checks of the decode calls; returns (S, H, D, W, ws_ptr, ws_bytes, stream)."""
     for t, n in ((out, "out"), (q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"),
                  (block_tables, "block_tables"), (context_lens, "context_lens")):
         _dev(t, n)
@@ -145,15 +148,19 @@ def _decode_args(out, q, k_pool, v_pool, block_tables, context_lens, block_size,
     S, H, D = q.shape
     _require(q.dtype in DTYPE_CODES, f"unsupported dtype {q.dtype}")
     _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    _require(k_pool.dim() == 4 and k_pool.shape[1:] == (H, block_size, D),
-             "k_pool must be [num_blocks, num_heads, block_size, head_dim]")
+    Hkv = k_pool.shape[1] if k_pool.dim() == 4 else -1
+    _require(k_pool.dim() == 4 and k_pool.shape[2:] == (block_size, D) and Hkv > 0 and H % Hkv == 0
+             and (need_fn is not None or Hkv == H),
+             "k_pool must be [num_blocks, num_kv_heads, block_size, head_dim] "
+             "(num_kv_heads == num_heads except for pa_decode_gqa)")
     _require(v_pool.shape == k_pool.shape and v_pool.dtype == k_pool.dtype, "v_pool must match k_pool")
     _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2
              and block_tables.shape[0] == S, "block_tables must be int32 [num_seqs, max_blocks]")
     _require(context_lens.dtype == torch.int32 and context_lens.shape == (S,),
              "context_lens must be int32 [num_seqs]")
     W = block_tables.shape[1]
-    need = pa_decode_workspace_size(S, H, D, W, block_size, partition_size)
+    need = (pa_decode_workspace_size(S, H, D, W, block_size, partition_size) if need_fn is None
+            else need_fn(S, H, Hkv, D, W))
     handle = _stream_handle(q.device, stream)
     ws_ptr, ws_bytes = None, 0
     if need:
@@ -184,6 +191,47 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
                            block_size, S, H, D, k_pool.shape[0], W, partition_size,
                            DTYPE_CODES[q.dtype], ws_ptr, ws_bytes, handle)
     _check("pa_decode", st)
+    return out
+
+
+def pa_decode_gqa_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                 max_blocks_per_seq: int, block_size: int, partition_size: int,
+                                 q_dtype: torch.dtype, kv_dtype: torch.dtype) -> int:
+    kv = DTYPE_CODES.get(kv_dtype, FP8_CODES.get(kv_dtype, -1))
+    return int(load_library().pa_decode_gqa_workspace_size(
+        num_seqs, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, partition_size,
+        DTYPE_CODES.get(q_dtype, -1), kv))
+
+
+def pa_decode_gqa(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                  block_size: int, *, k_scales: Optional[torch.Tensor] = None,
+                  v_scales: Optional[torch.Tensor] = None, partition_size: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Grouped-query paged decode: pools [N, num_kv_heads, BS, D] (16-bit, or
+    float8 with per-(block, K/V head) float32 scales), q / out [S, H, D] with
+    H a multiple of num_kv_heads; query head h reads K/V head h // (H / num_kv_heads)."""
+    lib = load_library()
+    need_fn = (lambda S, H, Hkv, D, W: pa_decode_gqa_workspace_size(
+        S, H, Hkv, D, W, block_size, partition_size, q.dtype, k_pool.dtype))
+    S, H, D, W, ws_ptr, ws_bytes, handle = _decode_args(
+        out, q, k_pool, v_pool, block_tables, context_lens, block_size, partition_size,
+        workspace, stream, need_fn=need_fn)
+    Hkv = k_pool.shape[1]
+    fp8 = k_pool.dtype in FP8_CODES
+    _require(fp8 or k_pool.dtype == q.dtype, "a 16/32-bit cache has q's dtype")
+    kp = vp = None
+    if fp8:
+        _scales(k_scales, v_scales, k_pool.shape[0], Hkv)
+        kp, vp = k_scales.data_ptr(), v_scales.data_ptr()
+    kv_code = FP8_CODES[k_pool.dtype] if fp8 else DTYPE_CODES[q.dtype]
+    with torch.cuda.device(q.device):
+        st = lib.pa_decode_gqa(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                               kp, vp, block_tables.data_ptr(), context_lens.data_ptr(),
+                               float(scale), block_size, S, H, Hkv, D, k_pool.shape[0], W,
+                               partition_size, DTYPE_CODES[q.dtype], kv_code, ws_ptr, ws_bytes,
+                               handle)
+    _check("pa_decode_gqa", st)
     return out
 
 

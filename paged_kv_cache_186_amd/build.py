@@ -23,7 +23,8 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
-SOURCES = ["pa_decode.hip", "pa_decode_balanced.hip", "pa_cache_ops.hip", "pa_api.cpp"]
+SOURCES = ["pa_decode.hip", "pa_decode_balanced.hip", "pa_decode_balanced_gqa2.hip",
+           "pa_decode_balanced_gqa4.hip", "pa_decode_balanced_gqa8.hip", "pa_cache_ops.hip", "pa_api.cpp"]
 
 # Packed-FP32 VALU forms are disabled: plain fp32 code only.
 COMMON_FLAGS = [

@@ -51,16 +51,32 @@ struct DecodePlan {
   int part_blocks;
   int max_parts;
   int workgroups;
+  int group_width;
   pa::WorkspaceLayout ws;
 };
 
+// Query heads that one K/V tile load serves in the balanced kernel: the
+// largest of 8, 4, 2 dividing the group size, for 16-bit queries (the built
+// variants; at most 4 with an 8-bit cache, whose 16 elements per lane leave
+// registers for only 4 heads' state); 1 otherwise.
+int group_width(int num_heads, int num_kv_heads, pa_dtype_t dtype, pa_dtype_t kv_dtype) {
+  const int g = num_heads / num_kv_heads;
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return 1;
+  for (int w : {8, 4, 2})
+    if (g % w == 0 && !(w == 8 && is_fp8(kv_dtype))) return w;
+  return 1;
+}
+
 // partition_size 0 selects the balanced split whenever it applies (at most
 // kBalancedMaxSeqs sequences); otherwise, or with an explicit partition size,
-// the partitioned kernel runs.
-DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                       int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
-  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, {0, 0, 0, 0}};
-  if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0) {
+// the partitioned kernel runs.  Balanced work rows are (sequence, group of
+// group_width query heads); each partial slot holds group_width partials.
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t partition_size, pa_dtype_t dtype, pa_dtype_t kv_dtype) {
+  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, 1, {0, 0, 0, 0}};
+  if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0 || num_kv_heads <= 0 ||
+      num_heads % num_kv_heads != 0) {
     p.status = PA_ERR_INVALID_ARG;
     return p;
   }
@@ -77,9 +93,17 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
   const long long tiles = static_cast<long long>(rows) * max_blocks_per_seq;
   if (partition_size == 0 && num_seqs <= pa::kBalancedMaxSeqs && tiles < (1LL << 40)) {
     p.mode = pa::DecodeMode::kBalanced;
-    p.workgroups = pa::balanced_workgroups(num_seqs, num_heads, max_blocks_per_seq);
-    const size_t slots = static_cast<size_t>(p.workgroups) * pa::kBalancedWaves + rows;
-    p.ws = pa::workspace_layout(rows, slots, head_dim);
+    p.group_width = group_width(num_heads, num_kv_heads, dtype, kv_dtype);
+    const int row_heads = num_heads / p.group_width;
+    const size_t wrows = static_cast<size_t>(num_seqs) * row_heads;
+    p.workgroups = pa::balanced_workgroups(num_seqs, row_heads, max_blocks_per_seq);
+    const size_t slots = static_cast<size_t>(p.workgroups) * pa::kBalancedWaves + wrows;
+    // the counter region is sized for one counter per (sequence, query head)
+    // whatever the grouping (only the first wrows are used here), so that
+    // every call with the same num_seqs * num_heads lays the workspace out
+    // with its partials after the same counter region: calls of different
+    // kinds can share one workspace without a partial landing on a counter
+    p.ws = pa::workspace_layout(rows, slots * p.group_width, head_dim);
     return p;
   }
   p.part_blocks =
@@ -103,12 +127,14 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
 pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
                         const float* k_scales, const float* v_scales,
                         const int32_t* block_tables, const int32_t* context_lens, float scale,
-                        int32_t block_size, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t partition_size,
-                        pa_dtype_t dtype, pa_dtype_t kv_dtype, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  const DecodePlan plan =
-      plan_decode(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size);
+                        int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                        int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
+                        pa_dtype_t kv_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
+                                      max_blocks_per_seq, block_size, partition_size, dtype,
+                                      kv_dtype);
   if (plan.status != PA_OK) return plan.status;
   if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
@@ -135,6 +161,8 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void
   a.block_size = block_size;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group_width = plan.group_width;
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -236,8 +264,19 @@ const char* pa_status_string(pa_status_t status) {
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t max_blocks_per_seq, int32_t block_size,
                                 int32_t partition_size) {
-  const DecodePlan p =
-      plan_decode(num_seqs, num_heads, head_dim, max_blocks_per_seq, block_size, partition_size);
+  const DecodePlan p = plan_decode(num_seqs, num_heads, num_heads, head_dim, max_blocks_per_seq,
+                                   block_size, partition_size, PA_DTYPE_F32, PA_DTYPE_F32);
+  return p.status == PA_OK ? p.ws.total : 0;
+}
+
+size_t pa_decode_gqa_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t partition_size,
+                                    pa_dtype_t q_dtype, pa_dtype_t kv_dtype) {
+  if (elem_bytes(q_dtype) == 0) return 0;
+  const DecodePlan p = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
+                                   max_blocks_per_seq, block_size, partition_size, q_dtype,
+                                   kv_dtype);
   return p.status == PA_OK ? p.ws.total : 0;
 }
 
@@ -248,8 +287,9 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
                       pa_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
   return decode_impl(out, q, k_pool, v_pool, nullptr, nullptr, block_tables, context_lens, scale,
-                     block_size, num_seqs, num_heads, head_dim, num_blocks, max_blocks_per_seq,
-                     partition_size, dtype, dtype, workspace, workspace_bytes, stream);
+                     block_size, num_seqs, num_heads, num_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, partition_size, dtype, dtype, workspace, workspace_bytes,
+                     stream);
 }
 
 pa_status_t pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -262,7 +302,25 @@ pa_status_t pa_decode_fp8(void* out, const void* q, const void* k_pool, const vo
   if ((q_dtype != PA_DTYPE_F16 && q_dtype != PA_DTYPE_BF16) || !is_fp8(kv_dtype))
     return PA_ERR_UNSUPPORTED;
   return decode_impl(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens,
-                     scale, block_size, num_seqs, num_heads, head_dim, num_blocks,
+                     scale, block_size, num_seqs, num_heads, num_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, partition_size, q_dtype, kv_dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_gqa(void* out, const void* q, const void* k_pool, const void* v_pool,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* block_tables, const int32_t* context_lens, float scale,
+                          int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t q_dtype,
+                          pa_dtype_t kv_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (elem_bytes(q_dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if (kv_dtype != q_dtype && !(is_fp8(kv_dtype) && q_dtype != PA_DTYPE_F32))
+    return PA_ERR_UNSUPPORTED;
+  return decode_impl(out, q, k_pool, v_pool, is_fp8(kv_dtype) ? k_scales : nullptr,
+                     is_fp8(kv_dtype) ? v_scales : nullptr, block_tables, context_lens, scale,
+                     block_size, num_seqs, num_heads, num_kv_heads, head_dim, num_blocks,
                      max_blocks_per_seq, partition_size, q_dtype, kv_dtype, workspace,
                      workspace_bytes, stream);
 }

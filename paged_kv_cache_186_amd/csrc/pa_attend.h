@@ -80,6 +80,66 @@ __device__ __forceinline__ void attend_tile(const u32x4 (&kv)[Tile<T, D, BS>::kL
   m = mn;
 }
 
+// attend_tile for GW query heads that share one K/V tile (grouped-query
+// attention): every K and V vector is unpacked once and serves all GW heads'
+// dot products, online softmax updates and weighted V sums.
+template <typename T, int D, int BS, int GW, bool kMasked>
+__device__ __forceinline__ void attend_tile_heads(const u32x4 (&kv)[Tile<T, D, BS>::kLoads],
+                                                  const u32x4 (&vv)[Tile<T, D, BS>::kLoads],
+                                                  const float (&qf)[GW][T::kElems], float (&m)[GW],
+                                                  float (&l)[GW], float (&acc)[GW][T::kElems], int tok0,
+                                                  int L, float sk, float sv) {
+  using C = Tile<T, D, BS>;
+  float sc[GW][C::kLoads];
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    float kf[T::kElems];
+    T::unpack(kv[i], kf);
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < T::kElems; ++e) d = fmaf(qf[g][e], kf[e], d);
+      sc[g][i] = group_sum<C::kLanesPerRow>(d);
+      if constexpr (T::kScaled) sc[g][i] *= sk;
+    }
+  }
+  bool ok[C::kLoads];
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) ok[i] = !kMasked || (tok0 + i * C::kRowsPerLoad < L);
+  float p[GW][C::kLoads];
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i)
+      if (ok[i]) bm = fmaxf(bm, sc[g][i]);
+    const float mn = fmaxf(m[g], bm);
+    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m[g] - mn);
+    l[g] *= alpha;
+#pragma unroll
+    for (int e = 0; e < T::kElems; ++e) acc[g][e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) p[g][i] = ok[i] ? fast_exp2(sc[g][i] - mn) : 0.f;
+    m[g] = mn;
+  }
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    float vf[T::kElems];
+    T::unpack(vv[i], vf);
+#pragma unroll
+    for (int e = 0; e < T::kElems; ++e) vf[e] = ok[i] ? vf[e] : 0.f;
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      l[g] += p[g][i];
+      float pv = p[g][i];
+      if constexpr (T::kScaled) pv *= sv;
+#pragma unroll
+      for (int e = 0; e < T::kElems; ++e) acc[g][e] = fmaf(pv, vf[e], acc[g][e]);
+    }
+  }
+}
+
 // The query / output side of a lane: E = KT::kElems consecutive elements of a
 // row, stored as QT — one 16-byte vector when QT and KT have the same width,
 // two for an 8-bit KV cache read with a 16-bit query.

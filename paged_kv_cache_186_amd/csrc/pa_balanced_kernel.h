@@ -1,0 +1,500 @@
+// Balanced-split decode kernel template (gfx950), included by
+// pa_decode_balanced.hip (one query head per K/V head) and
+// pa_decode_balanced_gqa.hip (grouped-query heads).
+//
+// Same computation as the partitioned kernel (pa_decode.hip): single-query
+// softmax attention per (sequence, head) over K/V rows found through the block
+// table — page "PagedAttentionMetal：基于Metal 3的Apple Silicon原生LLM推理加速方案",
+// section 注意力计算优化; vLLM tutorial page "3. PagedAttention原理", §3.2 and
+// the closing remarks of §3.4 — with the log-sum-exp merge of split rows (the
+// "Flash-Dec" milestone named on the "PagedAttention MLX：为Apple Silicon打造的
+// 高吞吐量LLM推理引擎" page).  Only the distribution of work differs.
+//
+// Work decomposition (our design): all (sequence, head, block) tiles are laid
+// out in one sequence — sequence-major, then head, then logical block — and
+// W = min(waves of a fixed grid, T) waves take equal contiguous shares of it:
+// wave k takes tiles [floor(k*T/W), floor((k+1)*T/W)), never an empty share.  Every wave therefore moves the same
+// number of bytes (+-1 tile) whatever the mix of context lengths, every
+// workgroup starts at once, and consecutive shares — which land on different
+// XCDs — read every head.  Each workgroup rebuilds the per-sequence tile
+// offsets in LDS from context_lens (an exclusive prefix sum), so the host
+// needs no knowledge of the lengths.
+//
+// A wave walks its share with the same two-stage load pipeline and per-lane-
+// group online softmax as the partitioned kernel.  When the row (sequence,
+// head) changes it folds its lane groups into one (max, sum, weighted V sum):
+//  * a row lying entirely inside the share is final: written to out at once;
+//  * only the first and the last row of a share can straddle a boundary; for
+//    those the wave stores a partial in slot (k + row) — distinct for every
+//    (wave, row) pair, because a later wave never touches an earlier row — and
+//    after its loop takes a ticket from the row's counter.  The wave that draws
+//    the last ticket merges the row's partials (slots kf+row .. kl+row for the
+//    first and last waves kf, kl covering it) and resets the counter.
+// Partials and tickets use L2-bypassing agent-scope accesses: the shares of one
+// row run on different XCDs, whose L2 caches are not coherent with each other.
+
+#pragma once
+
+#include "pa_attend.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaveMergeBatch = 8;  // partials in flight per lane group while merging
+
+// One pipeline stage: one tile's K/V, its row's query slice, and its place.
+// A unit is R consecutive rows of one (block, head) tile, at most
+// kUnitLoads wave loads per tensor, so two pipeline stages stay well inside
+// the register budget of 4 waves per SIMD (16 waves per CU keep far more
+// bytes in flight than the memory system needs).  A 16-row fp16 block is two
+// units of 8 rows by default.
+#ifndef PA_UNIT_LOADS
+#define PA_UNIT_LOADS 2
+#endif
+constexpr int kUnitLoads = PA_UNIT_LOADS;
+
+template <typename T, int D, int BS>
+struct Unit {
+  static constexpr int kRowsPerLoad = kWave / (D / T::kElems);
+  static constexpr int kRows =
+      (kUnitLoads * kRowsPerLoad < BS) ? kUnitLoads * kRowsPerLoad : BS;  // R
+  static constexpr int kPerBlock = BS / kRows;
+  static_assert(BS % kRows == 0, "units tile a block");
+};
+
+template <typename QT, typename KT, int D, int BS, int GW>
+struct BStage {
+  u32x4 k[Tile<KT, D, Unit<KT, D, BS>::kRows>::kLoads];
+  u32x4 v[Tile<KT, D, Unit<KT, D, BS>::kRows>::kLoads];
+  u32x4 q[GW][QSlice<QT, KT>::kVecs];  // the query slices of the row's GW heads
+  float sk, sv;         // K and V scales of the unit's (block, head) (8-bit KV only)
+  int s, h, u, L, bad;  // u: unit index within the row
+};
+
+// The wave whose share holds tile x: the largest k with floor(k*T/W) <= x.
+__device__ __forceinline__ long long wave_of_tile(long long x, long long T, long long W) {
+  return ((x + 1) * W - 1) / T;
+}
+
+// Log-sum-exp merge of one row's partials by a single wave (64 lanes).
+// Every load is independent of every other, so a batch of kWaveMergeBatch
+// partials per lane group — their (max, sum) pairs and 16-byte slices of their
+// vectors — is issued at once: rows split over up to kG*kWaveMergeBatch waves
+// merge in one memory round trip.  Each batch is folded into a running
+// (max, sum, vector) with the online rescaling, so any number of partials works.
+// Partial i of this head sits at ml + 2*GW*i and acc + D*GW*i (a slot holds
+// the partials of GW heads side by side).
+template <typename T, int D, int GW>
+__device__ __forceinline__ void merge_row_wave(typename T::storage* __restrict__ out_row,
+                                               const float* __restrict__ ml,
+                                               const float* __restrict__ acc, int nparts, int lane) {
+  constexpr int kChunks = D / 4;       // 16-byte slices of a partial row
+  constexpr int kG = kWave / kChunks;  // partials read side by side
+  const int c = lane % kChunks;
+  const int g = lane / kChunks;
+  float M = -INFINITY;  // running max (identical in every lane)
+  float den = 0.f;      // running sum of this lane group's partials, scaled to M
+  float num[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < nparts; i0 += kG * kWaveMergeBatch) {
+    uint64_t pr[kWaveMergeBatch], lo[kWaveMergeBatch], hi[kWaveMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kWaveMergeBatch; ++u) {
+      const int i = min(i0 + u * kG + g, nparts - 1);  // clamped: always issue the loads
+      pr[u] = load_coherent_u64(ml + 2 * GW * static_cast<size_t>(i));
+      lo[u] = load_coherent_u64(acc + static_cast<size_t>(i) * D * GW + 4 * c);
+      hi[u] = load_coherent_u64(acc + static_cast<size_t>(i) * D * GW + 4 * c + 2);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kWaveMergeBatch; ++u)
+      if (i0 + u * kG + g < nparts) bm = fmaxf(bm, lo_float(pr[u]));
+#pragma unroll
+    for (int off = kChunks; off < kWave; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+    const float Mn = fmaxf(M, bm);
+    const float rs = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+    den *= rs;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] *= rs;
+#pragma unroll
+    for (int u = 0; u < kWaveMergeBatch; ++u) {
+      const float wi = (i0 + u * kG + g < nparts) ? fast_exp2(lo_float(pr[u]) - Mn) : 0.f;
+      den = fmaf(wi, hi_float(pr[u]), den);
+      num[0] = fmaf(wi, lo_float(lo[u]), num[0]);
+      num[1] = fmaf(wi, hi_float(lo[u]), num[1]);
+      num[2] = fmaf(wi, lo_float(hi[u]), num[2]);
+      num[3] = fmaf(wi, hi_float(hi[u]), num[3]);
+    }
+    M = Mn;
+  }
+#pragma unroll
+  for (int off = kChunks; off < kWave; off <<= 1) {
+    den += __shfl_xor(den, off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] += __shfl_xor(num[e], off);
+  }
+  if (g == 0)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out_row[4 * c + e] = T::pack(num[e] / den);
+}
+
+// QT: query / output storage; KT: K/V cache storage (QT itself, or an 8-bit
+// type whose (block, head) scales come from k_scales / v_scales).  GW: query
+// heads served by each K/V tile load (grouped-query attention: the GW heads
+// of a work row share one K/V head; 1 for plain multi-head attention).  A work
+// "row" is (sequence, group of GW query heads); query head h reads K/V head
+// h / group, group = num_heads / num_kv_heads.
+// Launch bounds: the plain 16-bit kernels fit 4 waves per SIMD (<= 128
+// VGPRs); the 8-bit and grouped ones need more registers and are allowed up
+// to 256 (the launch shape has one wave per SIMD).
+template <typename QT, typename KT, int D, int BS, int NW, int GW>
+__global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) void decode_balanced_kernel(
+    typename QT::storage* __restrict__ out, uint32_t* __restrict__ counters,
+    float* __restrict__ ws_ml, float* __restrict__ ws_acc, const typename QT::storage* __restrict__ q,
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    float q_scale, int num_seqs, int num_heads, int num_kv_heads, int group, int num_blocks,
+    int max_blocks) {
+  constexpr int R = Unit<KT, D, BS>::kRows;
+  constexpr int kUnitsPerBlock = Unit<KT, D, BS>::kPerBlock;
+  using C = Tile<KT, D, R>;
+  using St = BStage<QT, KT, D, BS, GW>;
+  using QS = QSlice<QT, KT>;
+  constexpr int E = KT::kElems;
+  constexpr int kThreads = NW * kWave;
+  constexpr int kPer = (kBalancedMaxSeqs + kThreads - 1) / kThreads;  // sequences per thread
+  __shared__ int s_off[kBalancedMaxSeqs + 1];  // units of all sequences before s
+  __shared__ int s_len[kBalancedMaxSeqs];
+  __shared__ int s_wsum[NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int S = num_seqs;
+  const int NH = num_heads;      // query heads
+  const int H = num_heads / GW;  // work rows per sequence
+  const int HKV = num_kv_heads;
+  const int cap = max_blocks * BS;
+
+  // 1. clamped lengths and the exclusive prefix sum of units per sequence;
+  //    thread t owns sequences [t*kPer, (t+1)*kPer)
+  for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);  // coalesced
+  __syncthreads();
+  int nbl[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    nbl[i] = s < S ? (s_len[s] + R - 1) / R : 0;  // units of sequence s (per head)
+    mine += nbl[i];
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int v = s_wsum[w];
+    before += (w < wave) ? v : 0;
+    total += v;
+  }
+  int run = before + incl - mine;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    if (s < S) s_off[s] = run;
+    run += nbl[i];
+  }
+  if (tid == 0) s_off[S] = total;
+  __syncthreads();
+  total = __builtin_amdgcn_readfirstlane(total);
+
+  // 2. empty contexts give zero rows (spread over the workgroups)
+  for (int s = blockIdx.x; s < S; s += gridDim.x)
+    if (s_len[s] == 0)
+      for (int i = tid; i < NH * D; i += kThreads) out[static_cast<size_t>(s) * NH * D + i] = QT::pack(0.f);
+
+  // 3. this wave's share of the T units (no workgroup barrier after this point)
+  // Wn = min(waves in the grid, T): with at most one wave per unit no share is
+  // empty, so the waves kf..kl covering a row each store exactly one partial.
+  const long long T_all = static_cast<long long>(H) * total;
+  const long long Wn = min(static_cast<long long>(gridDim.x) * NW, T_all);
+  const long long k = static_cast<long long>(blockIdx.x) * NW + wave;
+  if (k >= Wn) return;
+  const long long t0 = k * T_all / Wn;
+  const long long t1 = (k + 1) * T_all / Wn;
+  const int nt = static_cast<int>(t1 - t0);
+
+  // walker: the largest s with H*off[s] <= t0 has units (off[s+1] > off[s])
+  int lo = 0;
+  int hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (static_cast<long long>(H) * s_off[mid] <= t0)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  int w_s = __builtin_amdgcn_readfirstlane(lo);
+  int w_nb = __builtin_amdgcn_readfirstlane(s_off[w_s + 1] - s_off[w_s]);
+  const long long u0 = t0 - static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_off[w_s]);
+  int w_h = static_cast<int>(u0 / w_nb);
+  int w_j = static_cast<int>(u0 % w_nb);
+  auto advance = [&]() {
+    if (++w_j < w_nb) return;
+    w_j = 0;
+    if (++w_h < H) return;
+    w_h = 0;
+    do {
+      ++w_s;
+    } while (w_s < S && __builtin_amdgcn_readfirstlane(s_off[w_s + 1] - s_off[w_s]) == 0);
+    if (w_s < S) w_nb = __builtin_amdgcn_readfirstlane(s_off[w_s + 1] - s_off[w_s]);
+  };
+
+  const int grp = lane / C::kLanesPerRow;
+  const int col = lane % C::kLanesPerRow;
+
+  auto load_stage = [&](St& st) {
+    const int blk = w_j / kUnitsPerBlock;
+    const int sub = w_j % kUnitsPerBlock;
+    int phys = block_tables[static_cast<size_t>(w_s) * max_blocks + blk];
+    st.bad = 0;
+    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
+      st.bad = 1;  // never dereference an id outside the pool
+      phys = 0;
+    }
+    const int kvh = (w_h * GW) / group;  // the K/V head of this row's query heads
+    const size_t tile = ((static_cast<size_t>(phys) * HKV + kvh) * BS + sub * R) * C::kRowBytes;
+    const char* kb = k_pool + tile + lane * kVecBytes;
+    const char* vb = v_pool + tile + lane * kVecBytes;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) st.k[i] = load16(kb + i * C::kLoadBytes);
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) st.v[i] = load16(vb + i * C::kLoadBytes);
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      const char* qrow =
+          reinterpret_cast<const char*>(q + (static_cast<size_t>(w_s) * NH + w_h * GW + g) * D);
+#pragma unroll
+      for (int i = 0; i < QS::kVecs; ++i) st.q[g][i] = load16(qrow + col * QS::kBytes + i * kVecBytes);
+    }
+    if constexpr (KT::kScaled) {
+      st.sk = load_uniform_f32(k_scales + static_cast<size_t>(phys) * HKV + kvh);
+      st.sv = load_uniform_f32(v_scales + static_cast<size_t>(phys) * HKV + kvh);
+    } else {
+      st.sk = st.sv = 1.f;
+    }
+    st.s = w_s;
+    st.h = w_h;
+    st.u = w_j;
+    st.L = __builtin_amdgcn_readfirstlane(s_len[w_s]);
+    advance();
+    // keep the scheduler from sinking these loads below the compute that
+    // follows: they must be in flight while the previous stage is consumed
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // state of the current row segment
+  int cur_s = -1;
+  int cur_h = 0;
+  int seg_bad = 0;
+  float m[GW];
+  float l[GW];
+  float acc[GW][E];
+  float qf[GW][E];
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = qf[g][e] = 0.f;
+  }
+  // rows whose partial is stored and whose ticket is still to be taken (<= 2)
+  int pend = 0;
+  size_t pend_row[2] = {0, 0};
+  int pend_n[2] = {0, 0};
+  size_t pend_slot0[2] = {0, 0};
+
+  auto flush = [&]() {
+    const int nb = __builtin_amdgcn_readfirstlane(s_off[cur_s + 1] - s_off[cur_s]);
+    const int off_s = __builtin_amdgcn_readfirstlane(s_off[cur_s]);
+    const long long first = static_cast<long long>(H) * off_s + static_cast<long long>(cur_h) * nb;
+    const long long kf = wave_of_tile(first, T_all, Wn);
+    const long long kl = wave_of_tile(first + nb - 1, T_all, Wn);
+    const size_t row = static_cast<size_t>(cur_s) * H + cur_h;
+    const size_t slot = static_cast<size_t>(k) + row;
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      // fold the lane groups of the wave into one state
+      float M = m[g];
+#pragma unroll
+      for (int off = C::kLanesPerRow; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float sc = (m[g] == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
+      float lt = l[g] * sc;
+      float a[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) a[e] = acc[g][e] * sc;
+#pragma unroll
+      for (int off = C::kLanesPerRow; off < kWave; off <<= 1) {
+        lt += __shfl_xor(lt, off);
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[e] += __shfl_xor(a[e], off);
+      }
+      if (kf == kl) {  // the whole row is in this share: final
+        if (grp == 0) {
+          float o[E];
+          const float inv = 1.f / lt;
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = seg_bad ? __builtin_nanf("") : a[e] * inv;
+          QS::store(out + (static_cast<size_t>(cur_s) * NH + cur_h * GW + g) * D, col, o);
+        }
+      } else {  // partial of head g in slot `slot`
+        const size_t sg = slot * GW + g;
+        if (grp == 0)
+#pragma unroll
+          for (int e = 0; e < E; e += 2) store_coherent_u64(ws_acc + sg * D + col * E + e, a[e], a[e + 1]);
+        if (lane == 0) store_coherent_u64(ws_ml + sg * 2, M, seg_bad ? __builtin_nanf("") : lt);
+      }
+    }
+    if (kf != kl) {
+      if (pend == 0) {
+        pend_row[0] = row;
+        pend_n[0] = static_cast<int>(kl - kf + 1);
+        pend_slot0[0] = static_cast<size_t>(kf) + row;
+      } else {
+        pend_row[1] = row;
+        pend_n[1] = static_cast<int>(kl - kf + 1);
+        pend_slot0[1] = static_cast<size_t>(kf) + row;
+      }
+      ++pend;
+    }
+  };
+
+  auto attend_stage = [&](const St& st) {
+    if (st.s != cur_s || st.h != cur_h) {  // a new row begins
+      if (cur_s >= 0) flush();
+      cur_s = st.s;
+      cur_h = st.h;
+      seg_bad = 0;
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < QS::kVecs; ++i) QT::unpack(st.q[g][i], qf[g] + i * QT::kElems);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          acc[g][e] = 0.f;
+          qf[g][e] *= q_scale;
+        }
+      }
+    }
+    seg_bad |= st.bad;
+    const int tok0 = st.u * R + grp;  // unit u holds tokens [u*R, (u+1)*R)
+    if constexpr (GW == 1) {
+      if ((st.u + 1) * R <= st.L)
+        attend_tile<KT, D, R, false>(st.k, st.v, qf[0], m[0], l[0], acc[0], tok0, st.L, st.sk, st.sv);
+      else
+        attend_tile<KT, D, R, true>(st.k, st.v, qf[0], m[0], l[0], acc[0], tok0, st.L, st.sk, st.sv);
+    } else {
+      if ((st.u + 1) * R <= st.L)
+        attend_tile_heads<KT, D, R, GW, false>(st.k, st.v, qf, m, l, acc, tok0, st.L, st.sk, st.sv);
+      else
+        attend_tile_heads<KT, D, R, GW, true>(st.k, st.v, qf, m, l, acc, tok0, st.L, st.sk, st.sv);
+    }
+  };
+
+  // two-stage pipeline over the share (steady state without conditional
+  // loads, then a one- or two-stage epilogue), then the last segment
+  St a, b;
+  load_stage(a);
+  int st = 0;
+  for (; st + 2 < nt; st += 2) {
+    load_stage(b);
+    attend_stage(a);
+    load_stage(a);
+    attend_stage(b);
+  }
+  if (st + 1 < nt) {
+    load_stage(b);
+    attend_stage(a);
+    attend_stage(b);
+  } else {
+    attend_stage(a);
+  }
+  flush();
+
+  if (pend == 0) return;
+  // tickets: this wave's partial stores must be performed first
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // lane p (< pend) takes pending row p's ticket: both in one round trip
+  uint32_t ticket = 0;
+  const size_t my_row = lane == 1 ? pend_row[1] : pend_row[0];
+  if (lane < pend)
+    ticket = __hip_atomic_fetch_add(&counters[my_row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t tk[2] = {static_cast<uint32_t>(__builtin_amdgcn_readlane(ticket, 0)),
+                          static_cast<uint32_t>(__builtin_amdgcn_readlane(ticket, 1))};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if (p >= pend) break;
+    if (tk[p] == static_cast<uint32_t>(pend_n[p] - 1)) {
+      const size_t rs = pend_row[p] / H;  // sequence and head group of the row
+      const size_t rh = pend_row[p] % H;
+#pragma unroll
+      for (int g = 0; g < GW; ++g)
+        merge_row_wave<QT, D, GW>(out + (rs * NH + rh * GW + g) * D, ws_ml + (pend_slot0[p] * GW + g) * 2,
+                                  ws_acc + (pend_slot0[p] * GW + g) * D, pend_n[p], lane);
+      if (lane == 0)  // ready for the next call
+        __hip_atomic_store(&counters[pend_row[p]], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <typename QT, typename KT, int D, int BS, int GW>
+hipError_t run_balanced(const DecodeArgs& a, hipStream_t stream) {
+  using S = typename QT::storage;
+  hipLaunchKernelGGL((decode_balanced_kernel<QT, KT, D, BS, kBalancedWaves, GW>), dim3(a.workgroups),
+                     dim3(kBalancedWaves * kWave), 0, stream, static_cast<S*>(a.out), a.counters,
+                     a.ws_ml, a.ws_acc, static_cast<const S*>(a.q),
+                     static_cast<const char*>(a.k_pool), static_cast<const char*>(a.v_pool),
+                     a.k_scales, a.v_scales, a.block_tables, a.context_lens, a.scale * kLog2e,
+                     a.num_seqs, a.num_heads, a.num_kv_heads, a.num_heads / a.num_kv_heads,
+                     a.num_blocks, a.max_blocks_per_seq);
+  return hipGetLastError();
+}
+
+template <typename QT, typename KT, int D, int GW>
+hipError_t run_balanced_bs(const DecodeArgs& a, hipStream_t stream) {
+  return a.block_size == 16 ? run_balanced<QT, KT, D, 16, GW>(a, stream)
+                            : run_balanced<QT, KT, D, 32, GW>(a, stream);
+}
+
+template <typename QT, typename KT, int GW>
+hipError_t run_balanced_d(const DecodeArgs& a, hipStream_t stream) {
+  return a.head_dim == 64 ? run_balanced_bs<QT, KT, 64, GW>(a, stream)
+                          : run_balanced_bs<QT, KT, 128, GW>(a, stream);
+}
+
+template <typename QT, int GW>
+hipError_t run_balanced_kv(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.kv_dtype) {
+    case PA_DTYPE_FP8_E4M3:
+      return run_balanced_d<QT, FP8E4M3, GW>(a, stream);
+    case PA_DTYPE_FP8_E5M2:
+      return run_balanced_d<QT, FP8E5M2, GW>(a, stream);
+    default:
+      return run_balanced_d<QT, QT, GW>(a, stream);
+  }
+}
+
+}  // namespace
+}  // namespace pa

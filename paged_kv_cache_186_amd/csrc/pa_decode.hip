@@ -162,6 +162,9 @@ __device__ __forceinline__ void merge_partials(typename T::storage* __restrict__
 // (h, p, s) covers blocks [p*PB, min((p+1)*PB, nblk)) of sequence s; wave w
 // takes blocks w, w+NW, ... of that range.  QT: query / output storage; KT:
 // K/V cache storage (QT itself, or an 8-bit type scaled per (block, head)).
+// Query head h reads K/V head h / group (grouped-query attention; each query
+// head reads its K/V head's tiles itself here — the balanced kernel is the
+// one that shares a tile load between the heads of a group).
 template <typename QT, typename KT, int D, int BS, int NW, int G>
 __global__ __launch_bounds__(NW* kWave) void decode_kernel(
     typename QT::storage* __restrict__ out, uint32_t* __restrict__ counters,
@@ -169,7 +172,8 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
     const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    float q_scale, int num_heads, int num_blocks, int max_blocks, int part_blocks, int max_parts) {
+    float q_scale, int num_heads, int num_kv_heads, int group, int num_blocks, int max_blocks,
+    int part_blocks, int max_parts) {
   using C = Tile<KT, D, BS>;
   using St = Stage<KT, D, BS, G>;
   constexpr int E = KT::kElems;
@@ -200,6 +204,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
   }
   if (p >= nparts) return;
 
+  const int kvh = h / group;  // K/V head read by query head h
   const int b_begin = p * part_blocks;
   const int b_end = min(nblk, b_begin + part_blocks);
   const int grp = lane / C::kLanesPerRow;
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
       bad = true;  // never dereference an id outside the pool
       phys = 0;
     }
-    const size_t tile = (static_cast<size_t>(phys) * num_heads + h) * C::kTileBytes;
+    const size_t tile = (static_cast<size_t>(phys) * num_kv_heads + kvh) * C::kTileBytes;
     const char* kb = k_pool + tile + lane * kVecBytes;
     const char* vb = v_pool + tile + lane * kVecBytes;
 #pragma unroll
@@ -237,8 +242,8 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) st.v[g][i] = load16(vb + i * C::kLoadBytes);
     if constexpr (KT::kScaled) {
-      st.sk[g] = load_uniform_f32(k_scales + static_cast<size_t>(phys) * num_heads + h);
-      st.sv[g] = load_uniform_f32(v_scales + static_cast<size_t>(phys) * num_heads + h);
+      st.sk[g] = load_uniform_f32(k_scales + static_cast<size_t>(phys) * num_kv_heads + kvh);
+      st.sv[g] = load_uniform_f32(v_scales + static_cast<size_t>(phys) * num_kv_heads + kvh);
     } else {
       st.sk[g] = st.sv[g] = 1.f;
     }
@@ -382,8 +387,8 @@ hipError_t run_decode(const DecodeArgs& a, hipStream_t stream) {
                      a.ws_ml, a.ws_acc, static_cast<const S*>(a.q),
                      static_cast<const char*>(a.k_pool), static_cast<const char*>(a.v_pool),
                      a.k_scales, a.v_scales, a.block_tables, a.context_lens, a.scale * kLog2e,
-                     a.num_heads, a.num_blocks, a.max_blocks_per_seq, a.partition_blocks,
-                     a.max_partitions);
+                     a.num_heads, a.num_kv_heads, a.num_heads / a.num_kv_heads, a.num_blocks,
+                     a.max_blocks_per_seq, a.partition_blocks, a.max_partitions);
   return hipGetLastError();
 }
 

@@ -50,7 +50,9 @@ struct DecodeArgs {
   float scale;
   int block_size;
   int num_seqs;
-  int num_heads;
+  int num_heads;         // query heads
+  int num_kv_heads;      // K/V heads (divides num_heads)
+  int group_width;       // kBalanced: query heads per K/V tile load (1, 2, 4 or 8)
   int head_dim;
   int num_blocks;
   int max_blocks_per_seq;
@@ -123,6 +125,10 @@ inline int balanced_workgroups(int num_seqs, int num_heads, int max_blocks) {
 
 hipError_t launch_decode_partitioned(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeArgs& a, hipStream_t stream);
+// group_width 2, 4, 8 (8: 16-bit caches only)
+hipError_t launch_decode_balanced_gqa2(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_balanced_gqa4(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_balanced_gqa8(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                                     const int32_t* slot_mapping, int num_tokens, int num_heads,

@@ -27,7 +27,7 @@ def test_every_declared_function_is_exported(lib):
     assert set(declared) == {"pa_abi_version", "pa_status_string", "pa_decode_workspace_size",
                              "pa_decode", "pa_reshape_and_cache", "pa_copy_blocks",
                              "pa_decode_fp8", "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8",
-                             "pa_swap_blocks"}
+                             "pa_swap_blocks", "pa_decode_gqa", "pa_decode_gqa_workspace_size"}
     raw = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
         assert hasattr(raw, name), name
@@ -251,3 +251,43 @@ def test_swap_blocks_rejects_before_launch(lib, kw, status):
     assert lib.pa_swap_blocks(a["dk"], a["dv"], a["sk"], a["sv"], a["dks"], a["dvs"], a["sks"],
                               a["svs"], a["bm"], a["n"], a["H"], a["D"], a["bs"], a["sN"], a["dN"],
                               a["dt"], None) == status
+
+
+
+def _decode_gqa(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, cl=FAKE, scale=0.125,
+             bs=16, S=4, H=8, Hkv=2, D=64, N=16, W=3, P=0, qdt=F16, kvdt=F16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.pa_decode_gqa(a["out"], a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["cl"],
+                             a["scale"], a["bs"], a["S"], a["H"], a["Hkv"], a["D"], a["N"], a["W"],
+                             a["P"], a["qdt"], a["kvdt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=3), INVALID),               # 8 query heads are not a multiple of 3
+    (dict(Hkv=0), INVALID),
+    (dict(Hkv=16), INVALID),
+    (dict(qdt=F16, kvdt=BF16), UNSUPPORTED),
+    (dict(qdt=F32, kvdt=E4M3), UNSUPPORTED),
+    (dict(qdt=E4M3, kvdt=E4M3), UNSUPPORTED),
+    (dict(kvdt=E4M3, ks=None), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(q=MISALIGNED), INVALID),
+    (dict(S=0), OK),
+])
+def test_decode_gqa_rejects_before_launch(lib, kw, status):
+    assert _decode_gqa(lib, **kw) == status
+
+
+def test_gqa_workspace_rules(lib):
+    # balanced split: one row per (sequence, group of query heads a tile load serves)
+    mha = lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 0)
+    assert lib.pa_decode_gqa_workspace_size(8, 32, 32, 128, 128, 16, 0, F16, F16) == mha
+    g8 = lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 0, F16, F16)   # 8 heads per load
+    g4 = lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 0, F16, E4M3)  # 8-bit: 4 per load
+    assert g8 > 0 and g4 > 0 and g8 % 256 == 0
+    assert lib.pa_decode_gqa_workspace_size(8, 32, 3, 128, 128, 16, 0, F16, F16) == 0   # invalid
+    assert lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 0, 9, F16) == 0
+    # explicit partitions: the same layout as pa_decode
+    assert lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 512, F16, F16) == \
+        lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 512)
