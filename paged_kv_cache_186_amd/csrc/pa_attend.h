@@ -81,27 +81,46 @@ __device__ __forceinline__ void attend_tile(const u32x4 (&kv)[Tile<T, D, BS>::kL
 }
 
 // attend_tile for GW query heads that share one K/V tile (grouped-query
-// attention): every K and V vector is unpacked once and serves all GW heads'
-// dot products, online softmax updates and weighted V sums.
+// attention): every K and V vector is loaded once and serves all GW heads'
+// dot products, online softmax updates and weighted V sums.  This is where the
+// per-byte arithmetic grows GW-fold, so it is kept lean:
+//  * 16-bit caches (T::kDot2) take the scores with v_dot2 on the packed
+//    words of K and of the query (qw: the query's own 16-bit words, unscaled;
+//    qscale is applied to each score), with no unpacking of K;
+//  * the running sums are rescaled only when some lane's maximum grew (a
+//    wave-uniform test; after the first tiles of a row it rarely does).
 template <typename T, int D, int BS, int GW, bool kMasked>
 __device__ __forceinline__ void attend_tile_heads(const u32x4 (&kv)[Tile<T, D, BS>::kLoads],
                                                   const u32x4 (&vv)[Tile<T, D, BS>::kLoads],
-                                                  const float (&qf)[GW][T::kElems], float (&m)[GW],
-                                                  float (&l)[GW], float (&acc)[GW][T::kElems], int tok0,
-                                                  int L, float sk, float sv) {
+                                                  const float (&qf)[GW][T::kElems],
+                                                  const uint32_t (&qw)[GW][T::kElems / 2], float qscale,
+                                                  float (&m)[GW], float (&l)[GW],
+                                                  float (&acc)[GW][T::kElems], int tok0, int L, float sk,
+                                                  float sv) {
   using C = Tile<T, D, BS>;
   float sc[GW][C::kLoads];
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
-    float kf[T::kElems];
-    T::unpack(kv[i], kf);
+    if constexpr (T::kDot2) {
+      const uint32_t kw[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      float d = 0.f;
+      for (int g = 0; g < GW; ++g) {
+        float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < T::kElems; ++e) d = fmaf(qf[g][e], kf[e], d);
-      sc[g][i] = group_sum<C::kLanesPerRow>(d);
-      if constexpr (T::kScaled) sc[g][i] *= sk;
+        for (int w = 0; w < 4; ++w) d = T::dot2(qw[g][w], kw[w], d);
+        sc[g][i] = group_sum<C::kLanesPerRow>(d) * qscale;
+      }
+    } else {
+      float kf[T::kElems];
+      T::unpack(kv[i], kf);
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < T::kElems; ++e) d = fmaf(qf[g][e], kf[e], d);
+        sc[g][i] = group_sum<C::kLanesPerRow>(d);
+        if constexpr (T::kScaled) sc[g][i] *= sk;
+      }
     }
   }
   bool ok[C::kLoads];
@@ -115,13 +134,16 @@ __device__ __forceinline__ void attend_tile_heads(const u32x4 (&kv)[Tile<T, D, B
     for (int i = 0; i < C::kLoads; ++i)
       if (ok[i]) bm = fmaxf(bm, sc[g][i]);
     const float mn = fmaxf(m[g], bm);
-    const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m[g] - mn);
-    l[g] *= alpha;
+    if (__builtin_amdgcn_ballot_w64(mn > m[g]) != 0) {  // some lane's maximum grew
+      // mn is -inf only while a group has met no token: nothing to rescale then
+      const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m[g] - mn);
+      l[g] *= alpha;
 #pragma unroll
-    for (int e = 0; e < T::kElems; ++e) acc[g][e] *= alpha;
+      for (int e = 0; e < T::kElems; ++e) acc[g][e] *= alpha;
+      m[g] = mn;
+    }
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) p[g][i] = ok[i] ? fast_exp2(sc[g][i] - mn) : 0.f;
-    m[g] = mn;
+    for (int i = 0; i < C::kLoads; ++i) p[g][i] = ok[i] ? fast_exp2(sc[g][i] - m[g]) : 0.f;
   }
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {

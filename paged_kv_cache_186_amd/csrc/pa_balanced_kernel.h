@@ -147,10 +147,11 @@ __device__ __forceinline__ void merge_row_wave(typename T::storage* __restrict__
 // "row" is (sequence, group of GW query heads); query head h reads K/V head
 // h / group, group = num_heads / num_kv_heads.
 // Launch bounds: the plain 16-bit kernels fit 4 waves per SIMD (<= 128
-// VGPRs); the 8-bit and grouped ones need more registers and are allowed up
-// to 256 (the launch shape has one wave per SIMD).
+// VGPRs); the 8-bit ones 2 (<= 256); the grouped ones, which hold several
+// heads' state per lane, may use the whole register file of one wave per
+// SIMD (the launch shape has one wave per SIMD in every case).
 template <typename QT, typename KT, int D, int BS, int NW, int GW>
-__global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) void decode_balanced_kernel(
+__global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)) void decode_balanced_kernel(
     typename QT::storage* __restrict__ out, uint32_t* __restrict__ counters,
     float* __restrict__ ws_ml, float* __restrict__ ws_acc, const typename QT::storage* __restrict__ q,
     const char* __restrict__ k_pool, const char* __restrict__ v_pool,
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) v
   const long long u0 = t0 - static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_off[w_s]);
   int w_h = static_cast<int>(u0 / w_nb);
   int w_j = static_cast<int>(u0 % w_nb);
-  auto advance = [&]() {
+  auto advance = [&]() __attribute__((always_inline)) {
     if (++w_j < w_nb) return;
     w_j = 0;
     if (++w_h < H) return;
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) v
   const int grp = lane / C::kLanesPerRow;
   const int col = lane % C::kLanesPerRow;
 
-  auto load_stage = [&](St& st) {
+  auto load_stage = [&](St& st) __attribute__((always_inline)) {
     const int blk = w_j / kUnitsPerBlock;
     const int sub = w_j % kUnitsPerBlock;
     int phys = block_tables[static_cast<size_t>(w_s) * max_blocks + blk];
@@ -311,6 +312,9 @@ __global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) v
   float l[GW];
   float acc[GW][E];
   float qf[GW][E];
+  uint32_t qw[GW][E / 2];  // grouped heads over a 16-bit cache: the query's own words
+  static_assert(!(GW > 1 && KT::kDot2) || (__is_same(QT, KT) && E == 8),
+                "packed dot products need the query in the cache's 16-bit format");
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
     m[g] = -INFINITY;
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) v
   int pend_n[2] = {0, 0};
   size_t pend_slot0[2] = {0, 0};
 
-  auto flush = [&]() {
+  auto flush = [&]() __attribute__((always_inline)) {
     const int nb = __builtin_amdgcn_readfirstlane(s_off[cur_s + 1] - s_off[cur_s]);
     const int off_s = __builtin_amdgcn_readfirstlane(s_off[cur_s]);
     const long long first = static_cast<long long>(H) * off_s + static_cast<long long>(cur_h) * nb;
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) v
     }
   };
 
-  auto attend_stage = [&](const St& st) {
+  auto attend_stage = [&](const St& st) __attribute__((always_inline)) {
     if (st.s != cur_s || st.h != cur_h) {  // a new row begins
       if (cur_s >= 0) flush();
       cur_s = st.s;
@@ -396,6 +400,12 @@ __global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) v
           acc[g][e] = 0.f;
           qf[g][e] *= q_scale;
         }
+        if constexpr (GW > 1 && KT::kDot2) {
+          qw[g][0] = st.q[g][0].x;
+          qw[g][1] = st.q[g][0].y;
+          qw[g][2] = st.q[g][0].z;
+          qw[g][3] = st.q[g][0].w;
+        }
       }
     }
     seg_bad |= st.bad;
@@ -407,9 +417,11 @@ __global__ __launch_bounds__(NW* kWave, (KT::kScaled || GW > 1) ? 2 : 16 / NW) v
         attend_tile<KT, D, R, true>(st.k, st.v, qf[0], m[0], l[0], acc[0], tok0, st.L, st.sk, st.sv);
     } else {
       if ((st.u + 1) * R <= st.L)
-        attend_tile_heads<KT, D, R, GW, false>(st.k, st.v, qf, m, l, acc, tok0, st.L, st.sk, st.sv);
+        attend_tile_heads<KT, D, R, GW, false>(st.k, st.v, qf, qw, q_scale, m, l, acc, tok0, st.L, st.sk,
+                                               st.sv);
       else
-        attend_tile_heads<KT, D, R, GW, true>(st.k, st.v, qf, m, l, acc, tok0, st.L, st.sk, st.sv);
+        attend_tile_heads<KT, D, R, GW, true>(st.k, st.v, qf, qw, q_scale, m, l, acc, tok0, st.L, st.sk,
+                                              st.sv);
     }
   };
 

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
   const int nt = first < b_end ? (b_end - first + NW - 1) / NW : 0;  // tiles of this wave
 
   // Issue the K/V loads of tile k of this wave (k < nt).
-  auto load_tile = [&](St& st, int g, int k) {
+  auto load_tile = [&](St& st, int g, int k) __attribute__((always_inline)) {
     const int j = first + k * NW;
     int phys = tbl[j];
     if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
     }
     st.block[g] = j;
   };
-  auto attend_slot = [&](const St& st, int g) {
+  auto attend_slot = [&](const St& st, int g) __attribute__((always_inline)) {
     const int j = st.block[g];
     const int tok0 = j * BS + grp;
     if ((j + 1) * BS <= L)
@@ -260,14 +260,14 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
   // A full stage holds G existing tiles: no per-slot guards, so every load it
   // issues is consumed on every path (the compiler then knows which loads are
   // outstanding and never waits on the prefetched stage early).
-  auto load_full = [&](St& st, int k0) {
+  auto load_full = [&](St& st, int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < G; ++g) load_tile(st, g, k0 + g);
     // keep the scheduler from sinking these loads below the compute that
     // follows: they must be in flight while the previous stage is consumed
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto attend_full = [&](const St& st) {
+  auto attend_full = [&](const St& st) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < G; ++g) attend_slot(st, g);
   };

@@ -23,10 +23,17 @@ constexpr int kVecBytes = 16;
 // ext-vector element (v.y, v.z, ...) as a cast of the vector's FIRST word.
 __device__ __forceinline__ float word_as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// kDot2: the type has a two-element dot product with fp32 accumulation
+// (v_dot2_f32_f16 / _bf16), dot2(a, b, c) = a.x*b.x + a.y*b.y + c, on packed
+// 32-bit words of two elements each.
 struct F32 {
   using storage = float;
   static constexpr int kElems = 4;  // per 16-byte vector
   static constexpr bool kScaled = false;
+  static constexpr bool kDot2 = false;
   static __device__ __forceinline__ void unpack(const u32x4 v, float* f) {
     const uint32_t w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
     f[0] = word_as_float(w0);
@@ -41,6 +48,10 @@ struct F16 {
   using storage = _Float16;
   static constexpr int kElems = 8;
   static constexpr bool kScaled = false;
+  static constexpr bool kDot2 = true;
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+  }
   static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
     const f16x2 h = __builtin_bit_cast(f16x2, w);
     f[0] = static_cast<float>(h.x);
@@ -60,6 +71,11 @@ struct BF16 {
   using storage = uint16_t;
   static constexpr int kElems = 8;
   static constexpr bool kScaled = false;
+  static constexpr bool kDot2 = true;
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+  }
   static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
     f[0] = __builtin_bit_cast(float, w << 16);
     f[1] = __builtin_bit_cast(float, w & 0xffff0000u);
@@ -90,6 +106,7 @@ struct FP8E4M3 {
   using storage = uint8_t;
   static constexpr int kElems = 16;
   static constexpr bool kScaled = true;
+  static constexpr bool kDot2 = false;
   static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
     const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
     const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
@@ -110,6 +127,7 @@ struct FP8E5M2 {
   using storage = uint8_t;
   static constexpr int kElems = 16;
   static constexpr bool kScaled = true;
+  static constexpr bool kDot2 = false;
   static __device__ __forceinline__ void unpack_word(uint32_t w, float* f) {
     const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
     const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
