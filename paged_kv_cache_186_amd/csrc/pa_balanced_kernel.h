@@ -55,23 +55,32 @@ constexpr int kWaveMergeBatch = 8;  // partials in flight per lane group while m
 #define PA_UNIT_LOADS 2
 #endif
 constexpr int kUnitLoads = PA_UNIT_LOADS;
+// Grouped-query waves spend GW times the arithmetic on each byte, so between
+// two loads they compute for much longer; a unit twice as large keeps as many
+// bytes in flight per wave relative to that work.
+#ifndef PA_UNIT_LOADS_GROUPED
+#define PA_UNIT_LOADS_GROUPED 4
+#endif
+constexpr int kUnitLoadsGrouped = PA_UNIT_LOADS_GROUPED;
 
-template <typename T, int D, int BS>
+template <typename T, int D, int BS, int GW>
 struct Unit {
+  static constexpr int kLoads = GW > 1 ? kUnitLoadsGrouped : kUnitLoads;
   static constexpr int kRowsPerLoad = kWave / (D / T::kElems);
   static constexpr int kRows =
-      (kUnitLoads * kRowsPerLoad < BS) ? kUnitLoads * kRowsPerLoad : BS;  // R
+      (kLoads * kRowsPerLoad < BS) ? kLoads * kRowsPerLoad : BS;  // R
   static constexpr int kPerBlock = BS / kRows;
   static_assert(BS % kRows == 0, "units tile a block");
 };
 
 template <typename QT, typename KT, int D, int BS, int GW>
 struct BStage {
-  u32x4 k[Tile<KT, D, Unit<KT, D, BS>::kRows>::kLoads];
-  u32x4 v[Tile<KT, D, Unit<KT, D, BS>::kRows>::kLoads];
+  u32x4 k[Tile<KT, D, Unit<KT, D, BS, GW>::kRows>::kLoads];
+  u32x4 v[Tile<KT, D, Unit<KT, D, BS, GW>::kRows>::kLoads];
   u32x4 q[GW][QSlice<QT, KT>::kVecs];  // the query slices of the row's GW heads
   float sk, sv;         // K and V scales of the unit's (block, head) (8-bit KV only)
   int s, h, u, L, bad;  // u: unit index within the row
+  int newrow;           // the unit opens a row segment of this wave (q is loaded)
 };
 
 // The wave whose share holds tile x: the largest k with floor(k*T/W) <= x.
@@ -79,65 +88,83 @@ __device__ __forceinline__ long long wave_of_tile(long long x, long long T, long
   return ((x + 1) * W - 1) / T;
 }
 
-// Log-sum-exp merge of one row's partials by a single wave (64 lanes).
-// Every load is independent of every other, so a batch of kWaveMergeBatch
-// partials per lane group — their (max, sum) pairs and 16-byte slices of their
-// vectors — is issued at once: rows split over up to kG*kWaveMergeBatch waves
-// merge in one memory round trip.  Each batch is folded into a running
-// (max, sum, vector) with the online rescaling, so any number of partials works.
-// Partial i of this head sits at ml + 2*GW*i and acc + D*GW*i (a slot holds
-// the partials of GW heads side by side).
+// Log-sum-exp merge of one row's partials by a single wave (64 lanes), for
+// the GW heads of the row at once.  A slot holds the partials of GW heads side
+// by side: head g of partial i sits at ml + 2*(i*GW + g) and acc + D*(i*GW + g).
+// Every load is independent of every other, so a batch of B partials per lane
+// group and head — their (max, sum) pairs and 16-byte slices of their vectors —
+// is issued at once: a row split over up to kG*B waves merges in one memory
+// round trip, whatever GW.  Each batch is folded into a running (max, sum,
+// vector) per head with the online rescaling, so any number of partials works.
+// out_row: the output of the row's first head (head g at out_row + g*D).
 template <typename T, int D, int GW>
 __device__ __forceinline__ void merge_row_wave(typename T::storage* __restrict__ out_row,
                                                const float* __restrict__ ml,
                                                const float* __restrict__ acc, int nparts, int lane) {
   constexpr int kChunks = D / 4;       // 16-byte slices of a partial row
   constexpr int kG = kWave / kChunks;  // partials read side by side
+  constexpr int B = GW <= 2 ? kWaveMergeBatch : (4 * kWaveMergeBatch) / GW;  // <= 48 loads per lane
   const int c = lane % kChunks;
-  const int g = lane / kChunks;
-  float M = -INFINITY;  // running max (identical in every lane)
-  float den = 0.f;      // running sum of this lane group's partials, scaled to M
-  float num[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int i0 = 0; i0 < nparts; i0 += kG * kWaveMergeBatch) {
-    uint64_t pr[kWaveMergeBatch], lo[kWaveMergeBatch], hi[kWaveMergeBatch];
+  const int gl = lane / kChunks;
+  float M[GW];       // running max per head (identical in every lane)
+  float den[GW];     // running sum of this lane group's partials, scaled to M
+  float num[GW][4];
 #pragma unroll
-    for (int u = 0; u < kWaveMergeBatch; ++u) {
-      const int i = min(i0 + u * kG + g, nparts - 1);  // clamped: always issue the loads
-      pr[u] = load_coherent_u64(ml + 2 * GW * static_cast<size_t>(i));
-      lo[u] = load_coherent_u64(acc + static_cast<size_t>(i) * D * GW + 4 * c);
-      hi[u] = load_coherent_u64(acc + static_cast<size_t>(i) * D * GW + 4 * c + 2);
+  for (int h = 0; h < GW; ++h) {
+    M[h] = -INFINITY;
+    den[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[h][e] = 0.f;
+  }
+  for (int i0 = 0; i0 < nparts; i0 += kG * B) {
+    uint64_t pr[GW][B], lo[GW][B], hi[GW][B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const size_t i = min(i0 + u * kG + gl, nparts - 1);  // clamped: always issue the loads
+#pragma unroll
+      for (int h = 0; h < GW; ++h) {
+        pr[h][u] = load_coherent_u64(ml + 2 * (i * GW + h));
+        lo[h][u] = load_coherent_u64(acc + (i * GW + h) * D + 4 * c);
+        hi[h][u] = load_coherent_u64(acc + (i * GW + h) * D + 4 * c + 2);
+      }
     }
-    float bm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kWaveMergeBatch; ++u)
-      if (i0 + u * kG + g < nparts) bm = fmaxf(bm, lo_float(pr[u]));
+    for (int h = 0; h < GW; ++h) {
+      float bm = -INFINITY;
 #pragma unroll
-    for (int off = kChunks; off < kWave; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
-    const float Mn = fmaxf(M, bm);
-    const float rs = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
-    den *= rs;
+      for (int u = 0; u < B; ++u)
+        if (i0 + u * kG + gl < nparts) bm = fmaxf(bm, lo_float(pr[h][u]));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) num[e] *= rs;
+      for (int off = kChunks; off < kWave; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+      const float Mn = fmaxf(M[h], bm);
+      const float rs = (M[h] == -INFINITY) ? 0.f : fast_exp2(M[h] - Mn);
+      den[h] *= rs;
 #pragma unroll
-    for (int u = 0; u < kWaveMergeBatch; ++u) {
-      const float wi = (i0 + u * kG + g < nparts) ? fast_exp2(lo_float(pr[u]) - Mn) : 0.f;
-      den = fmaf(wi, hi_float(pr[u]), den);
-      num[0] = fmaf(wi, lo_float(lo[u]), num[0]);
-      num[1] = fmaf(wi, hi_float(lo[u]), num[1]);
-      num[2] = fmaf(wi, lo_float(hi[u]), num[2]);
-      num[3] = fmaf(wi, hi_float(hi[u]), num[3]);
+      for (int e = 0; e < 4; ++e) num[h][e] *= rs;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const float wi = (i0 + u * kG + gl < nparts) ? fast_exp2(lo_float(pr[h][u]) - Mn) : 0.f;
+        den[h] = fmaf(wi, hi_float(pr[h][u]), den[h]);
+        num[h][0] = fmaf(wi, lo_float(lo[h][u]), num[h][0]);
+        num[h][1] = fmaf(wi, hi_float(lo[h][u]), num[h][1]);
+        num[h][2] = fmaf(wi, lo_float(hi[h][u]), num[h][2]);
+        num[h][3] = fmaf(wi, hi_float(hi[h][u]), num[h][3]);
+      }
+      M[h] = Mn;
     }
-    M = Mn;
   }
 #pragma unroll
-  for (int off = kChunks; off < kWave; off <<= 1) {
-    den += __shfl_xor(den, off);
+  for (int h = 0; h < GW; ++h) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) num[e] += __shfl_xor(num[e], off);
+    for (int off = kChunks; off < kWave; off <<= 1) {
+      den[h] += __shfl_xor(den[h], off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[h][e] += __shfl_xor(num[h][e], off);
+    }
+    if (gl == 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out_row[h * D + 4 * c + e] = T::pack(num[h][e] / den[h]);
   }
-  if (g == 0)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out_row[4 * c + e] = T::pack(num[e] / den);
 }
 
 // QT: query / output storage; KT: K/V cache storage (QT itself, or an 8-bit
@@ -159,8 +186,8 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     float q_scale, int num_seqs, int num_heads, int num_kv_heads, int group, int num_blocks,
     int max_blocks) {
-  constexpr int R = Unit<KT, D, BS>::kRows;
-  constexpr int kUnitsPerBlock = Unit<KT, D, BS>::kPerBlock;
+  constexpr int R = Unit<KT, D, BS, GW>::kRows;
+  constexpr int kUnitsPerBlock = Unit<KT, D, BS, GW>::kPerBlock;
   using C = Tile<KT, D, R>;
   using St = BStage<QT, KT, D, BS, GW>;
   using QS = QSlice<QT, KT>;
@@ -264,7 +291,26 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   const int grp = lane / C::kLanesPerRow;
   const int col = lane % C::kLanesPerRow;
 
+  bool first_stage = true;
   auto load_stage = [&](St& st) __attribute__((always_inline)) {
+    // a row segment of this wave opens with its first stage or a row's first unit
+    st.newrow = first_stage || w_j == 0;
+    first_stage = false;
+    // the query is needed only when a segment opens; grouped kernels load it
+    // only then (first, so that the loads of the previous stage can be waited
+    // for exactly whether or not these were issued)
+    auto load_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        const char* qrow =
+            reinterpret_cast<const char*>(q + (static_cast<size_t>(w_s) * NH + w_h * GW + g) * D);
+#pragma unroll
+        for (int i = 0; i < QS::kVecs; ++i) st.q[g][i] = load16(qrow + col * QS::kBytes + i * kVecBytes);
+      }
+    };
+    if constexpr (GW > 1) {
+      if (st.newrow) load_q();
+    }
     const int blk = w_j / kUnitsPerBlock;
     const int sub = w_j % kUnitsPerBlock;
     int phys = block_tables[static_cast<size_t>(w_s) * max_blocks + blk];
@@ -281,13 +327,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     for (int i = 0; i < C::kLoads; ++i) st.k[i] = load16(kb + i * C::kLoadBytes);
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) st.v[i] = load16(vb + i * C::kLoadBytes);
-#pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      const char* qrow =
-          reinterpret_cast<const char*>(q + (static_cast<size_t>(w_s) * NH + w_h * GW + g) * D);
-#pragma unroll
-      for (int i = 0; i < QS::kVecs; ++i) st.q[g][i] = load16(qrow + col * QS::kBytes + i * kVecBytes);
-    }
+    if constexpr (GW == 1) load_q();
     if constexpr (KT::kScaled) {
       st.sk = load_uniform_f32(k_scales + static_cast<size_t>(phys) * HKV + kvh);
       st.sv = load_uniform_f32(v_scales + static_cast<size_t>(phys) * HKV + kvh);
@@ -384,7 +424,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   };
 
   auto attend_stage = [&](const St& st) __attribute__((always_inline)) {
-    if (st.s != cur_s || st.h != cur_h) {  // a new row begins
+    if (st.newrow) {  // a new row segment begins
       if (cur_s >= 0) flush();
       cur_s = st.s;
       cur_h = st.h;
@@ -461,10 +501,8 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     if (tk[p] == static_cast<uint32_t>(pend_n[p] - 1)) {
       const size_t rs = pend_row[p] / H;  // sequence and head group of the row
       const size_t rh = pend_row[p] % H;
-#pragma unroll
-      for (int g = 0; g < GW; ++g)
-        merge_row_wave<QT, D, GW>(out + (rs * NH + rh * GW + g) * D, ws_ml + (pend_slot0[p] * GW + g) * 2,
-                                  ws_acc + (pend_slot0[p] * GW + g) * D, pend_n[p], lane);
+      merge_row_wave<QT, D, GW>(out + (rs * NH + rh * GW) * D, ws_ml + pend_slot0[p] * GW * 2,
+                                ws_acc + pend_slot0[p] * GW * D, pend_n[p], lane);
       if (lane == 0)  // ready for the next call
         __hip_atomic_store(&counters[pend_row[p]], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

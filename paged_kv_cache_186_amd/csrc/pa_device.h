@@ -181,19 +181,23 @@ __device__ __forceinline__ uint32_t quantize_e5m2(float y) { return quantize_fp8
 // the xor-1 and xor-2 partners; row_half_mirror (lane i <- 7-i within 8) and
 // row_mirror (lane i <- 15-i within 16) then pair each lane with one in the
 // other half, which completes the 8- and 16-lane sums; ds_swizzle with xor
-// mask 16 crosses the two rows of a 32-lane half-wave.
+// mask 16 crosses the two rows of a 32-lane half-wave.  Every source lane of
+// these permutations is a valid lane of the same row and the sums run with
+// the whole wave active, so the bound-control bit (a zero source for invalid
+// or inactive lanes) never takes effect; setting it lets the compiler fold
+// each move into the following add (one DPP add per step).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float dpp_quad_xor1(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float dpp_quad_xor2(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float dpp_row_half_mirror(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float dpp_row_mirror(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float swizzle_xor16(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
