@@ -25,9 +25,13 @@ Sources, cited by page title and section:
 * Page "mlx-paged-attention: Bringing vLLM-level High Throughput Inference to
   Apple Silicon", core feature 2 (shared prefixes with copy-on-write).
 * Page "PagedAttention MLX：为Apple Silicon打造的高吞吐量LLM推理引擎",
-  architecture list (the kernel gathers K/V from the physical pool) and
-  roadmap milestone 4 (the name "Flash-Dec", the only hint of a split-context
+  architecture list (the kernel gathers K/V from the physical pool),
+  roadmap milestone 3 (multi-head latent attention, ``oracle.multi_query``)
+  and milestone 4 (the name "Flash-Dec", the only hint of a split-context
   decode on the pages).
+* Page "mlx-paged-attention: ...", comparison with vLLM and future plans
+  (speculative decoding: several new query tokens per sequence,
+  ``oracle.multi_query``).
 
 Pins: every function here is checked in ``tests/test_oracle.py`` against facts
 that do not come from the oracle itself (hand-derived fixtures under
@@ -45,6 +49,10 @@ from .paged_attention import (  # noqa: F401
     copy_blocks_ref,
     swap_blocks_ref,
     decode_gqa_ref,
+)
+from .multi_query import (  # noqa: F401
+    prefill_ref,
+    mla_decode_ref,
 )
 from .fp8 import (  # noqa: F401
     fp8_values,
