@@ -208,6 +208,84 @@ pa_status_t pa_decode_gqa(void* out, const void* q, const void* k_pool, const vo
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ---- Several query tokens per sequence (chunked prefill, speculative
+ * verification) ----------------------------------------------------------------
+ * Causal attention of each sequence's LAST Tq_s tokens over its paged cache
+ * ("mlx-paged-attention: Bringing vLLM-level High Throughput Inference to
+ * Apple Silicon": speculative decoding, named in the comparison with vLLM and
+ * in the future plans; the pages give no semantics, this is the library's
+ * reading).  The new tokens' K/V must already be in the cache
+ * (pa_reshape_and_cache), so context_lens[s] = L_s counts them; query token
+ * i < Tq_s of sequence s sits at position p = L_s - Tq_s + i and attends over
+ * the keys at positions 0..p.  Query head h reads K/V head h / (num_heads /
+ * num_kv_heads).
+ *   q, out:       [num_query_tokens][num_heads][head_dim], packed by sequence:
+ *                 sequence s owns rows query_start[s] .. query_start[s+1]-1
+ *   query_start:  int32 [num_seqs + 1] device array, query_start[0] = 0,
+ *                 non-decreasing, query_start[num_seqs] = num_query_tokens,
+ *                 Tq_s <= L_s
+ *   pools:        [num_blocks][num_kv_heads][block_size][head_dim]
+ *   dtype:        PA_DTYPE_F16 or PA_DTYPE_BF16 (q, pools and out; the
+ *                 products run on the matrix cores with fp32 accumulation and
+ *                 the probabilities rounded to dtype before the V product);
+ *                 anything else is PA_ERR_UNSUPPORTED.  head_dim 64 or 128,
+ *                 block_size 16 or 32.
+ *   partition_size: 0 lets the library split long contexts only when the
+ *                 query rows alone would not fill the GPU; otherwise keys per
+ *                 partition, a positive multiple of 16.
+ *   workspace:    pa_prefill_workspace_size() bytes for the same sizes, 0
+ *                 when nothing is split (then workspace may be NULL).  Its
+ *                 counters must be zero before the first call; every call
+ *                 leaves them zero.  Its layout differs from pa_decode*'s:
+ *                 do not hand one workspace to both kinds without zeroing it.
+ * Device-side contents never cause an access outside the arrays: lengths are
+ * clamped to [0, max_blocks_per_seq * block_size], query bounds to
+ * [0, num_query_tokens], and a table id outside the pool makes NaN every
+ * output row of each 16-row tile (query rows of one K/V head, token-major)
+ * whose keys include that block.  A row that sees no key at all comes out
+ * zero, as an empty context does in pa_decode (with Tq_s > L_s, which breaks
+ * the contract, the rows that would sit before position 0).
+ */
+size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_query_tokens, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                 int32_t block_size, int32_t partition_size);
+
+pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, float scale, int32_t block_size,
+                       int32_t num_seqs, int32_t num_query_tokens, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ---- Decode over a multi-head latent (MLA) cache ------------------------------
+ * "PagedAttention MLX：为Apple Silicon打造的高吞吐量LLM推理引擎", roadmap
+ * milestone 3, names multi-head latent attention (DeepSeek-V3).  Reading (the
+ * published absorbed form of MLA decode): the cache keeps one 576-element
+ * row per token — the 512-element compressed latent followed by the 64-element
+ * shared rotary key; every query head brings a 576-element query (its
+ * no-position part already multiplied by the key up-projection); the score of
+ * token t is scale * <q_h, row_t> and its value the row's first 512 elements.
+ *   q:        [num_seqs][num_heads][576]
+ *   kv_pool:  [num_blocks][block_size][576]
+ *   out:      [num_seqs][num_heads][512] (the weighted latent; the value
+ *             up-projection is the model's)
+ *   dtype:    PA_DTYPE_F16 or PA_DTYPE_BF16; block_size 16 or 32.
+ * Everything else (tables, lengths, partition_size, workspace from
+ * pa_decode_mla_workspace_size(), error behaviour) as for pa_prefill with one
+ * query token per sequence.
+ */
+size_t pa_decode_mla_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t partition_size);
+
+pa_status_t pa_decode_mla(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                          const int32_t* context_lens, float scale, int32_t block_size,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Copy whole blocks from one pool pair to another (K and V):
  *   dst_k[d] = src_k[s], dst_v[d] = src_v[s]     for each {s, d} of block_mapping
  * — swapping an inactive sequence's blocks out to host memory and back in

@@ -17,7 +17,11 @@ from .binding import (  # noqa: F401
     pa_decode_fp8,
     pa_decode_gqa,
     pa_decode_gqa_workspace_size,
+    pa_decode_mla,
+    pa_decode_mla_workspace_size,
     pa_decode_workspace_size,
+    pa_prefill,
+    pa_prefill_workspace_size,
     pa_reshape_and_cache,
     pa_reshape_and_cache_fp8,
     pa_swap_blocks,

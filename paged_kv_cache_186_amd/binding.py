@@ -48,7 +48,16 @@ _SIGNATURES = {
     "pa_decode_gqa_workspace_size": (_c_size, [_c_int] * 7 + [_c_int, _c_int]),
     "pa_decode_gqa": (_c_int, [_c_void] * 8 + [_c_float] + [_c_int] * 8 + [_c_int, _c_int]
                       + [_c_void, _c_size, _c_void]),
+    "pa_prefill_workspace_size": (_c_size, [_c_int] * 8),
+    "pa_prefill": (_c_int, [_c_void] * 7 + [_c_float] + [_c_int] * 9 + [_c_int]
+                   + [_c_void, _c_size, _c_void]),
+    "pa_decode_mla_workspace_size": (_c_size, [_c_int] * 5),
+    "pa_decode_mla": (_c_int, [_c_void] * 5 + [_c_float] + [_c_int] * 6 + [_c_int]
+                      + [_c_void, _c_size, _c_void]),
 }
+
+MLA_QK_DIM = 576   # latent 512 + rotary 64
+MLA_V_DIM = 512
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -129,7 +138,7 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def _cached_workspace(device, stream_handle: int, rows: int, need: int) -> torch.Tensor:
+def _cached_workspace(device, stream_handle: int, rows, need: int) -> torch.Tensor:
     key = (torch.device(device).index, stream_handle, rows)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < need:
@@ -397,3 +406,99 @@ def pa_swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor
                                 block_mapping.shape[0], H, D, BS, src_k.shape[0], dst_k.shape[0],
                                 code, _stream_handle(device, stream))
     _check("pa_swap_blocks", st)
+
+
+def pa_prefill_workspace_size(num_seqs: int, num_query_tokens: int, num_heads: int, num_kv_heads: int,
+                              head_dim: int, max_blocks_per_seq: int, block_size: int,
+                              partition_size: int = 0) -> int:
+    return int(load_library().pa_prefill_workspace_size(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                                        head_dim, max_blocks_per_seq, block_size,
+                                                        partition_size))
+
+
+def _query_call_args(out, q, block_tables, context_lens, partition_size, workspace, stream, need):
+    handle = _stream_handle(q.device, stream)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:   # never shared with the decode calls (another layout)
+            workspace = _cached_workspace(q.device, handle, ("queries", tuple(q.shape)), need)
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return ws_ptr, ws_bytes, handle
+
+
+def pa_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+               block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+               scale: float, block_size: int, *, partition_size: int = 0,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal attention of each sequence's last Tq_s tokens over its paged
+    cache (chunked prefill, speculative verification): q / out [T, H, D]
+    packed by sequence (rows query_start[s] .. query_start[s+1]-1), pools
+    [N, num_kv_heads, BS, D] holding the new tokens already, context_lens
+    counting them; fp16 or bf16."""
+    lib = load_library()
+    for t, n in ((out, "out"), (q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (query_start, "query_start")):
+        _dev(t, n)
+    _require(q.dim() == 3 and q.dtype in (torch.float16, torch.bfloat16),
+             "q must be float16 or bfloat16 [num_query_tokens, num_heads, head_dim]")
+    T, H, D = q.shape
+    _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _require(k_pool.dim() == 4 and k_pool.shape[2:] == (block_size, D) and k_pool.dtype == q.dtype
+             and H % k_pool.shape[1] == 0, "k_pool must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    _require(v_pool.shape == k_pool.shape and v_pool.dtype == k_pool.dtype, "v_pool must match k_pool")
+    S = context_lens.shape[0] if context_lens.dim() == 1 else -1
+    _require(context_lens.dtype == torch.int32 and S >= 0, "context_lens must be int32 [num_seqs]")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S,
+             "block_tables must be int32 [num_seqs, max_blocks]")
+    _require(query_start.dtype == torch.int32 and query_start.shape == (S + 1,),
+             "query_start must be int32 [num_seqs + 1]")
+    Hkv, W = k_pool.shape[1], block_tables.shape[1]
+    need = pa_prefill_workspace_size(S, T, H, Hkv, D, W, block_size, partition_size)
+    ws_ptr, ws_bytes, handle = _query_call_args(out, q, block_tables, context_lens, partition_size,
+                                                workspace, stream, need)
+    with torch.cuda.device(q.device):
+        st = lib.pa_prefill(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                            block_tables.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(),
+                            float(scale), block_size, S, T, H, Hkv, D, k_pool.shape[0], W, partition_size,
+                            DTYPE_CODES[q.dtype], ws_ptr, ws_bytes, handle)
+    _check("pa_prefill", st)
+    return out
+
+
+def pa_decode_mla_workspace_size(num_seqs: int, num_heads: int, max_blocks_per_seq: int, block_size: int,
+                                 partition_size: int = 0) -> int:
+    return int(load_library().pa_decode_mla_workspace_size(num_seqs, num_heads, max_blocks_per_seq,
+                                                           block_size, partition_size))
+
+
+def pa_decode_mla(out: torch.Tensor, q: torch.Tensor, kv_pool: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, scale: float, block_size: int, *, partition_size: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode over a multi-head latent cache: q [S, H, 576], kv_pool
+    [N, BS, 576] (latent 512 then rotary 64 per token), out [S, H, 512] =
+    the softmax-weighted latents; fp16 or bf16."""
+    lib = load_library()
+    for t, n in ((out, "out"), (q, "q"), (kv_pool, "kv_pool"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens")):
+        _dev(t, n)
+    _require(q.dim() == 3 and q.shape[2] == MLA_QK_DIM and q.dtype in (torch.float16, torch.bfloat16),
+             f"q must be float16 or bfloat16 [num_seqs, num_heads, {MLA_QK_DIM}]")
+    S, H, _ = q.shape
+    _require(out.shape == (S, H, MLA_V_DIM) and out.dtype == q.dtype, f"out must be [num_seqs, num_heads, {MLA_V_DIM}]")
+    _require(kv_pool.dim() == 3 and kv_pool.shape[1:] == (block_size, MLA_QK_DIM) and kv_pool.dtype == q.dtype,
+             f"kv_pool must be [num_blocks, block_size, {MLA_QK_DIM}] in q's dtype")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == S,
+             "block_tables must be int32 [num_seqs, max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (S,), "context_lens must be int32 [num_seqs]")
+    W = block_tables.shape[1]
+    need = pa_decode_mla_workspace_size(S, H, W, block_size, partition_size)
+    ws_ptr, ws_bytes, handle = _query_call_args(out, q, block_tables, context_lens, partition_size,
+                                                workspace, stream, need)
+    with torch.cuda.device(q.device):
+        st = lib.pa_decode_mla(out.data_ptr(), q.data_ptr(), kv_pool.data_ptr(), block_tables.data_ptr(),
+                               context_lens.data_ptr(), float(scale), block_size, S, H, kv_pool.shape[0], W,
+                               partition_size, DTYPE_CODES[q.dtype], ws_ptr, ws_bytes, handle)
+    _check("pa_decode_mla", st)
+    return out

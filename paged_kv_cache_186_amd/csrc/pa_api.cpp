@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 // Bytes of one element of a 16/32-bit dtype (0 for anything else).
 int elem_bytes(pa_dtype_t dtype) {
@@ -184,6 +184,137 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void
                            ? pa::launch_decode_balanced(a, static_cast<hipStream_t>(stream))
                            : pa::launch_decode_partitioned(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// ---- multi-token queries and the latent cache (matrix-core kernel) ----------
+
+struct PrefillPlan {
+  pa_status_t status;
+  int part_tokens;
+  long long max_items;  // over all launches of the call (the workspace holds this many)
+  int workgroups;
+  pa::WorkspaceLayout ws;
+};
+
+constexpr long long kPfTargetItems = 2048;  // ~2 waves per SIMD of a 256-CU GPU
+constexpr int kPfMinPartTokens = 256;
+
+// Items are (sequence, K/V head, tile of 16 query rows, value slice,
+// partition).  Their number is bounded from host-known sizes: the tiles of a
+// call are at most ceil(T*G/16) + S (a sequence's partial tile adds at most
+// one), partitions at most ceil(W*BS / part_tokens).  partition_size 0 splits
+// the context only when the unsplit items would not fill the GPU.
+PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_query_rows, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t block_size,
+                         int32_t partition_size, int32_t v_per_item, int32_t slices) {
+  PrefillPlan p{PA_OK, 0, 0, 0, {0, 0, 0, 0}};
+  if (num_seqs < 0 || num_query_rows < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_heads % num_kv_heads != 0 || max_blocks_per_seq <= 0 ||
+      max_blocks_per_seq > INT_MAX / block_size / 2) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  const long long ctx = static_cast<long long>(max_blocks_per_seq) * block_size;
+  const long long group = num_heads / num_kv_heads;
+  const long long tiles = (static_cast<long long>(num_query_rows) * group + 15) / 16 + num_seqs;
+  const long long base = tiles * num_kv_heads * slices;
+  if (partition_size == 0) {
+    long long parts = 1;
+    if (base > 0 && base < kPfTargetItems) {
+      parts = (kPfTargetItems + base - 1) / base;
+      const long long most = (ctx + kPfMinPartTokens - 1) / kPfMinPartTokens;
+      parts = parts < most ? parts : most;
+      parts = parts < 1 ? 1 : parts;
+    }
+    const long long per = (ctx + parts - 1) / parts;
+    p.part_tokens = static_cast<int>((per + 15) / 16 * 16);
+  } else {
+    if (partition_size < 0 || partition_size % 16 != 0) {
+      p.status = PA_ERR_INVALID_ARG;
+      return p;
+    }
+    p.part_tokens = partition_size;
+  }
+  const long long max_parts = (ctx + p.part_tokens - 1) / p.part_tokens;
+  p.max_items = base * max_parts;
+  if (p.max_items > INT_MAX / 16) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  const long long wg = (p.max_items + 3) / 4;
+  p.workgroups = static_cast<int>(wg < 1 ? 1 : (wg > pa::kPfMaxWorkgroups ? pa::kPfMaxWorkgroups : wg));
+  if (max_parts > 1)
+    p.ws = pa::workspace_layout(static_cast<size_t>(p.max_items), static_cast<size_t>(p.max_items) * 16,
+                                v_per_item);
+  return p;
+}
+
+// Shared by pa_prefill and pa_decode_mla; the caller has checked dtype and
+// the head dimension.  Launches once per group of kPfMaxSeqs sequences (the
+// query bounds are absolute row numbers, so q and out are passed whole).
+pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start, float scale, int32_t block_size,
+                         int32_t num_seqs, int32_t num_query_rows, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
+                         bool latent, void* workspace, size_t workspace_bytes, void* stream) {
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  const int v_per_item = latent ? pa::kMlaVSlice : head_dim;
+  const int slices = latent ? pa::kMlaVDim / pa::kMlaVSlice : 1;
+  const PrefillPlan plan = plan_prefill(num_seqs, num_query_rows, num_heads, num_kv_heads,
+                                        max_blocks_per_seq, block_size, partition_size,
+                                        v_per_item, slices);
+  if (plan.status != PA_OK) return plan.status;
+  if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_query_rows == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (!latent && !query_start) return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PA_ERR_INVALID_ARG;
+  if (plan.ws.total > 0) {
+    if (!workspace || workspace_bytes < plan.ws.total) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+  }
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.scale = scale;
+  a.block_size = block_size;
+  a.num_query_rows = num_query_rows;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.dtype = dtype;
+  a.latent = latent;
+  a.part_tokens = plan.part_tokens;
+  a.max_items = static_cast<int>(plan.max_items);
+  a.workgroups = plan.workgroups;
+  if (plan.ws.total > 0) {
+    char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(ws + plan.ws.counter_offset);
+    a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
+    a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
+  }
+  for (int32_t s0 = 0; s0 < num_seqs; s0 += pa::kPfMaxSeqs) {
+    a.num_seqs = num_seqs - s0 < pa::kPfMaxSeqs ? num_seqs - s0 : pa::kPfMaxSeqs;
+    a.block_tables = block_tables + static_cast<size_t>(s0) * max_blocks_per_seq;
+    a.context_lens = context_lens + s0;
+    a.query_start = query_start ? query_start + s0 : nullptr;
+    if (!query_start) {  // one row per sequence: rows s0 .. s0 + n - 1
+      a.q = static_cast<const char*>(q) + static_cast<size_t>(s0) * num_heads * head_dim * 2;
+      a.out = static_cast<char*>(out) +
+              static_cast<size_t>(s0) * num_heads * (latent ? pa::kMlaVDim : head_dim) * 2;
+      a.num_query_rows = a.num_seqs;
+    }
+    if (pa::launch_prefill(a, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
 }
 
 // The address under which the GPU reaches *p: device memory as is; pinned
@@ -418,6 +549,50 @@ pa_status_t pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const vo
                        dst_num_blocks,
                        num_heads};
   return copy_impl(c, num_pairs, head_dim, block_size, e, stream, /*host_ok=*/true);
+}
+
+size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_query_tokens, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                 int32_t block_size, int32_t partition_size) {
+  if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32)) return 0;
+  const PrefillPlan p = plan_prefill(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                     max_blocks_per_seq, block_size, partition_size, head_dim, 1);
+  return p.status == PA_OK ? p.ws.total : 0;
+}
+
+pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* query_start, float scale, int32_t block_size,
+                       int32_t num_seqs, int32_t num_query_tokens, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  return prefill_impl(out, q, k_pool, v_pool, block_tables, context_lens, query_start, scale,
+                      block_size, num_seqs, num_query_tokens, num_heads, num_kv_heads, head_dim,
+                      num_blocks, max_blocks_per_seq, partition_size, dtype, false, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t pa_decode_mla_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t partition_size) {
+  if (block_size != 16 && block_size != 32) return 0;
+  const PrefillPlan p = plan_prefill(num_seqs, num_seqs, num_heads, 1, max_blocks_per_seq, block_size,
+                                     partition_size, pa::kMlaVSlice, pa::kMlaVDim / pa::kMlaVSlice);
+  return p.status == PA_OK ? p.ws.total : 0;
+}
+
+pa_status_t pa_decode_mla(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                          const int32_t* context_lens, float scale, int32_t block_size,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  return prefill_impl(out, q, kv_pool, kv_pool, block_tables, context_lens, nullptr, scale,
+                      block_size, num_seqs, num_seqs, num_heads, 1, pa::kMlaQkDim, num_blocks,
+                      max_blocks_per_seq, partition_size, dtype, true, workspace, workspace_bytes,
+                      stream);
 }
 
 }  // extern "C"

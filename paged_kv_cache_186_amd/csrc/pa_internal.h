@@ -130,6 +130,41 @@ hipError_t launch_decode_balanced_gqa2(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced_gqa4(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced_gqa8(const DecodeArgs& a, hipStream_t stream);
 
+// Attention of several query rows per (sequence, K/V head) on the matrix
+// cores: multi-token queries (pa_prefill) and decode over an MLA latent cache
+// (pa_decode_mla, latent == true: 576-element key rows whose first 512
+// elements are the values, one K/V head, v_pool == k_pool).  Items are
+// (sequence, K/V head, tile of 16 query rows, context partition); each
+// workgroup rebuilds the per-sequence item offsets in LDS, hence the sequence
+// limit per launch (the host launches once per group of kPfMaxSeqs).
+constexpr int kPfMaxSeqs = 2048;
+constexpr int kPfMaxWorkgroups = 1024;
+constexpr int kMlaQkDim = 576;  // latent 512 + rotary 64 (DeepSeek-V2/V3)
+constexpr int kMlaVDim = 512;
+constexpr int kMlaVSlice = 256;  // value elements per work item (two items per row tile)
+
+struct PrefillArgs {
+  void* out;                    // [T][H][DV]
+  const void* q;                // [T][H][DQK]
+  const void* k_pool;           // [num_blocks][Hkv][BS][DQK]
+  const void* v_pool;           // [num_blocks][Hkv][BS][DV] (latent: == k_pool)
+  const int32_t* block_tables;  // [S][W]
+  const int32_t* context_lens;  // [S]
+  const int32_t* query_start;   // [S+1]; null: one query row per sequence
+  float scale;
+  int block_size, num_seqs, num_query_rows, num_heads, num_kv_heads, head_dim, num_blocks,
+      max_blocks_per_seq;
+  int dtype;        // PA_DTYPE_F16 or PA_DTYPE_BF16
+  bool latent;
+  int part_tokens;  // keys per context partition (multiple of 16)
+  int max_items;    // workspace capacity in items; the kernel never goes past it
+  int workgroups;
+  uint32_t* counters;  // [max_items] (null when no row can be split)
+  float* ws_ml;        // [max_items][16][2]
+  float* ws_acc;       // [max_items][16][value elements per item: DV, or kMlaVSlice]
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                                     const int32_t* slot_mapping, int num_tokens, int num_heads,
                                     int row_bytes, int block_size, int num_blocks, hipStream_t stream);

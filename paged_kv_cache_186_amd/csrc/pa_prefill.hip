@@ -1,0 +1,499 @@
+// Attention of several query rows at once over the paged KV cache, on the
+// matrix cores (gfx950 MFMA).
+//
+// What is computed: for every sequence s, its last Tq_s tokens attend
+// causally over its cache — query token i at position p = L_s - Tq_s + i sees
+// the keys at positions 0..p — and query head h reads K/V head h / G (page
+// "mlx-paged-attention: Bringing vLLM-level High Throughput Inference to Apple
+// Silicon", comparison with vLLM and future plans: speculative decoding,
+// i.e. verifying several drafted tokens in one pass; the attention itself is
+// the ordinary softmax attention read through the block table, vLLM tutorial
+// page "3. PagedAttention原理", §3.2 and the closing remarks of §3.4).  The
+// same kernel, with one latent K/V "head" whose value is a prefix of the key
+// row, is decode over a multi-head latent (MLA) cache ("PagedAttention MLX：
+// 为Apple Silicon打造的高吞吐量LLM推理引擎", roadmap milestone 3).
+//
+// Work decomposition (our design).  The rows of one (sequence, K/V head) are
+// its (query token, head of the group) pairs, token-major: M_s = Tq_s * G
+// rows.  A wave owns a tile of 16 rows; the context may be cut into
+// partitions of part_tokens tokens.  Items (sequence, K/V head, row tile,
+// partition) are numbered with the partition fastest and taken by the waves
+// of the grid in turn; each workgroup rebuilds the per-sequence item offsets
+// in LDS from context_lens and query_start.
+//
+// One 16-token chunk of one item, per wave:
+//   S^T = K Q^T   with v_mfma_f32_16x16x32_{f16,bf16}: A = 16 keys x 32
+//                 head elements (lane l: key l%16, elements 8*(l/16)..+7 of
+//                 the slice — four lanes read 64 contiguous bytes of a key
+//                 row), B = the same elements of the 16 query rows;
+//                 the result gives lane l the scores of keys 4*(l/16)+i,
+//                 i < 4, for query row l%16;
+//   softmax       per query row: the lane's four scores, then across the
+//                 four lanes of the row (two cross-lane maxima); the running
+//                 sum stays a per-lane partial until the end;
+//   O^T += V^T P^T with v_mfma_f32_16x16x16_{f16,bf16}: B = the
+//                 probabilities exactly as the scores came out (lane l: keys
+//                 4*(l/16)+i of row l%16, rounded to the 16-bit type), A =
+//                 V transposed — lane l reads 8 bytes (4 elements) of each of
+//                 its 4 keys, 16 lanes cover a 128-byte line, and byte
+//                 permutes regroup the elements by column; the column labels
+//                 of the 4 products of a 64-element slice are chosen so that
+//                 lane l ends with 16 consecutive output elements of row l%16.
+// Two chunks are in flight (loads of the next chunk are issued before the
+// current one is consumed).  Masked keys (after a row's position, or past the
+// context in the last block) get probability 0 by selection, and V rows past
+// the context are zeroed, so poisoned cache slots never reach a result.
+// A row split over several partitions stores (max, sum, weighted V sum) per
+// partition; the wave that draws the last ticket merges them with the
+// log-sum-exp identity and resets the counter.
+
+#include "pa_attend.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<F16> {
+  static __device__ __forceinline__ f4_t qk(u32x4 a, u32x4 b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c,
+                                                  0, 0, 0);
+  }
+  static __device__ __forceinline__ f4_t pv(u32x2 a, u32x2 b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a), __builtin_bit_cast(h4_t, b), c,
+                                                 0, 0, 0);
+  }
+  // two fp32 values -> one word of two f16 (round to nearest even)
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(lo))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(hi))) << 16);
+  }
+};
+
+template <>
+struct Mfma<BF16> {
+  static __device__ __forceinline__ f4_t qk(u32x4 a, u32x4 b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a), __builtin_bit_cast(b8_t, b), c,
+                                                   0, 0, 0);
+  }
+  static __device__ __forceinline__ f4_t pv(u32x2 a, u32x2 b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a), __builtin_bit_cast(s4_t, b), c,
+                                                     0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return static_cast<uint32_t>(BF16::pack(lo)) | (static_cast<uint32_t>(BF16::pack(hi)) << 16);
+  }
+};
+
+// Element e (< 4) of a lane's 8-byte slice, in the low 16 bits.
+__device__ __forceinline__ uint32_t half_of(u32x2 v, int e) {
+  const uint32_t w = (e < 2) ? v.x : v.y;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+constexpr int kPfWaves = 4;
+constexpr int kPfRows = 16;      // query rows per item (MFMA N of S^T)
+constexpr int kPfChunk = 16;     // keys per step (MFMA M of S^T)
+
+// T: storage of q, pools and out (F16 or BF16).  DQK: elements of a query /
+// key row; DV: elements of a value row; DVS: value elements one item
+// produces (DV, or a slice of it: the 512-element latent values are split in
+// two items of 256 that share the scores, so that one wave's registers hold
+// the query, two chunks in flight and the accumulators without spilling);
+// KV_STRIDE: elements between consecutive value rows of the V pool (DV for a
+// separate V pool; DQK when values are the first DV elements of the key rows,
+// v_pool == k_pool).
+template <typename T, int DQK, int DV, int DVS, int KV_STRIDE, int BS>
+__global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 ? 1 : 2)) void prefill_kernel(
+    typename T::storage* __restrict__ out, const typename T::storage* __restrict__ q,
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    const int32_t* __restrict__ query_start, uint32_t* __restrict__ counters, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc, float qk_scale, int num_seqs, int num_rows, int num_heads, int num_kv_heads,
+    int group, int num_blocks, int max_blocks, int part_tokens, int max_items) {
+  static_assert(DQK % 32 == 0 && DVS % 64 == 0 && DV % DVS == 0, "MFMA slices");
+  static_assert(BS % kPfChunk == 0, "a chunk never crosses a block");
+  using S16 = typename T::storage;
+  using M = Mfma<T>;
+  constexpr int kQK = DQK / 32;   // S^T products per chunk
+  constexpr int kDq = DVS / 64;   // 64-element value slices of an item
+  constexpr int kSlices = DV / DVS;
+  constexpr int kMergeBatch = DVS <= 128 ? 4 : 1;  // partials loaded at once while merging
+  constexpr int kThreads = kPfWaves * kWave;
+  constexpr int kPer = (kPfMaxSeqs + kThreads - 1) / kThreads;
+  __shared__ int s_off[kPfMaxSeqs + 1];  // items of all sequences before s
+  __shared__ int s_len[kPfMaxSeqs];
+  __shared__ int s_q0[kPfMaxSeqs + 1];   // first query row of s (s_q0[S] = rows)
+  __shared__ int s_wsum[kPfWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int S = num_seqs;
+  const int HKV = num_kv_heads;
+  const int cap = max_blocks * BS;
+
+  // 1. lengths, query bounds and the exclusive prefix sum of items
+  for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);
+  // query bounds clamped to the q / out rows, so that no value in
+  // query_start can send an access outside them
+  for (int s = tid; s <= S; s += kThreads) s_q0[s] = min(max(query_start ? query_start[s] : s, 0), num_rows);
+  __syncthreads();
+  int cnt[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    int c = 0;
+    if (s < S) {
+      const int rows = max(s_q0[s + 1] - s_q0[s], 0) * group;
+      const int tiles = rows > 0 ? (rows + kPfRows - 1) / kPfRows : 0;
+      const int parts = max(1, (s_len[s] + part_tokens - 1) / part_tokens);
+      c = HKV * tiles * kSlices * parts;
+    }
+    cnt[i] = c;
+    mine += c;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kPfWaves; ++w) {
+    const int v = s_wsum[w];
+    before += (w < wave) ? v : 0;
+    total += v;
+  }
+  int run = before + incl - mine;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    if (s < S) s_off[s] = run;
+    run += cnt[i];
+  }
+  if (tid == 0) s_off[S] = total;
+  __syncthreads();
+  // the host sized the workspace for max_items; query bounds that break the
+  // contract (overlapping ranges) could ask for more: those items are dropped
+  total = min(__builtin_amdgcn_readfirstlane(total), max_items);
+
+  const int col = lane % 16;  // query row of the tile / key of a chunk (A rows)
+  const int g4 = lane / 16;   // lane group: 8-element slice of S^T's K dim, key quad of P
+  const int NH = num_heads;
+
+  for (int item = blockIdx.x * kPfWaves + wave; item < total; item += gridDim.x * kPfWaves) {
+    // 2. which (sequence, K/V head, tile, partition)
+    int lo = 0;
+    int hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= item)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(lo);
+    const int L = __builtin_amdgcn_readfirstlane(s_len[s]);
+    const int q0 = __builtin_amdgcn_readfirstlane(s_q0[s]);
+    const int Tq = max(__builtin_amdgcn_readfirstlane(s_q0[s + 1]) - q0, 0);
+    const int Mrows = Tq * group;
+    const int tiles = (Mrows + kPfRows - 1) / kPfRows;
+    const int parts = max(1, (L + part_tokens - 1) / part_tokens);
+    const int local = item - __builtin_amdgcn_readfirstlane(s_off[s]);
+    const int part = local % parts;
+    const int rest = local / parts;
+    const int slice = rest % kSlices;
+    const int rest2 = rest / kSlices;
+    const int tile = rest2 % tiles;
+    const int hk = rest2 / tiles;
+    const int v_off = slice * DVS;  // first value element of the item
+
+    // this lane's query row
+    const int r = tile * kPfRows + col;
+    const bool row_ok = r < Mrows;
+    const int ti = row_ok ? r / group : 0;
+    const int h = hk * group + (row_ok ? r % group : 0);
+    const int pos = row_ok ? L - Tq + ti : -1;  // keys 0..pos are visible
+    // wave-uniform key range of the item
+    const int r_last = min(Mrows, (tile + 1) * kPfRows) - 1;
+    const int pos_max = L - Tq + r_last / group;
+    const int pos_min = L - Tq + (tile * kPfRows) / group;
+    const int k_begin = part * part_tokens;
+    const int k_end = min(min(k_begin + part_tokens, L), pos_max + 1);
+
+    // query slices (B operand of S^T): lane holds elements 32j + 8*g4 .. +7
+    u32x4 qv[kQK];
+    {
+      const S16* qrow = q + (static_cast<size_t>(q0 + ti) * NH + h) * DQK + 8 * g4;
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) {
+        const u32x4 v = load16(qrow + 32 * j);
+        qv[j] = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+
+    float m = -INFINITY;  // running max of row `col` (same in its 4 lanes)
+    float lsum = 0.f;     // this lane's share of the row's running sum
+    f4_t acc[kDq][4];     // O^T products: [slice][column label e]
+#pragma unroll
+    for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[dq][e] = f4_t{0.f, 0.f, 0.f, 0.f};
+    int bad = 0;
+
+    struct Stage {
+      u32x4 k[kQK];
+      u32x2 v[kDq][4];
+      int c;  // first key of the chunk
+      int bad;
+    };
+    const int32_t* tbl = block_tables + static_cast<size_t>(s) * max_blocks;
+    auto load_chunk = [&](Stage& st, int c) __attribute__((always_inline)) {
+      st.c = c;
+      int phys = tbl[c / BS];
+      st.bad = 0;
+      if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
+        st.bad = 1;  // never dereference an id outside the pool
+        phys = 0;
+      }
+      const size_t row0 = (static_cast<size_t>(phys) * HKV + hk) * BS + (c % BS);
+      const char* kb = k_pool + ((row0 + col) * DQK + 8 * g4) * sizeof(S16);
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) st.k[j] = load16(kb + 32 * j * sizeof(S16));
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const char* vb = v_pool + ((row0 + 4 * g4 + e) * KV_STRIDE + v_off + 64 * dq + 4 * col) * sizeof(S16);
+          st.v[dq][e] = *reinterpret_cast<const u32x2*>(vb);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto attend_chunk = [&](Stage& st) __attribute__((always_inline)) {
+      bad |= st.bad;
+      f4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) sc = M::qk(st.k[j], qv[j], sc);
+      const int key0 = st.c + 4 * g4;  // key of sc[0]
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = sc[i] * qk_scale;
+      if (st.c + kPfChunk - 1 > pos_min) {  // some key is after some row's position
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] = (key0 + i <= pos) ? z[i] : -INFINITY;
+      }
+      if (st.c + kPfChunk > L) {  // value rows past the context: zero
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key0 + e >= L)
+#pragma unroll
+            for (int dq = 0; dq < kDq; ++dq) st.v[dq][e] = u32x2{0u, 0u};
+      }
+      float cm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      const float mn = fmaxf(m, cm);
+      if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
+        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[dq][e] *= alpha;
+        m = mn;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = (z[i] == -INFINITY) ? 0.f : fast_exp2(z[i] - m);
+      lsum += (p[0] + p[1]) + (p[2] + p[3]);
+      const u32x2 pw = {M::pack2(p[0], p[1]), M::pack2(p[2], p[3])};
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // column e of this slice for the lane's 4 keys: rows 4*g4 .. +3 of V
+          const u32x2 a = {half_of(st.v[dq][0], e) | (half_of(st.v[dq][1], e) << 16),
+                           half_of(st.v[dq][2], e) | (half_of(st.v[dq][3], e) << 16)};
+          acc[dq][e] = M::pv(a, pw, acc[dq][e]);
+        }
+    };
+
+    // 3. the chunks of the item, two in flight
+    const int c_first = k_begin;
+    const int n_chunks = k_end > k_begin ? (k_end - k_begin + kPfChunk - 1) / kPfChunk : 0;
+    if (n_chunks > 0) {
+      Stage a, b;
+      load_chunk(a, c_first);
+      int t = 0;
+      for (; t + 2 < n_chunks; t += 2) {
+        load_chunk(b, c_first + (t + 1) * kPfChunk);
+        attend_chunk(a);
+        load_chunk(a, c_first + (t + 2) * kPfChunk);
+        attend_chunk(b);
+      }
+      if (t + 1 < n_chunks) {
+        load_chunk(b, c_first + (t + 1) * kPfChunk);
+        attend_chunk(a);
+        attend_chunk(b);
+      } else {
+        attend_chunk(a);
+      }
+    }
+    float lrow = lsum + __shfl_xor(lsum, 16);
+    lrow += __shfl_xor(lrow, 32);
+    if (bad) lrow = __builtin_nanf("");
+
+    // lane holds, for row `col`, output elements 64*dq + 16*g4 + 4*i + e
+    auto write_row = [&](const float (&o)[kDq][16]) __attribute__((always_inline)) {
+      S16* orow = out + (static_cast<size_t>(q0 + ti) * NH + h) * DV + v_off + 16 * g4;
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq) {
+        uint32_t w[8];
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) w[k2] = M::pack2(o[dq][2 * k2], o[dq][2 * k2 + 1]);
+        store16(orow + 64 * dq, u32x4{w[0], w[1], w[2], w[3]});
+        store16(orow + 64 * dq + 8, u32x4{w[4], w[5], w[6], w[7]});
+      }
+    };
+
+    if (parts == 1) {
+      if (row_ok) {
+        float o[kDq][16];
+        const float inv = (lrow == 0.f) ? 0.f : 1.f / lrow;  // no visible key (empty context): zeros
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[dq][4 * i + e] = acc[dq][e][i] * inv;
+        write_row(o);
+      }
+      continue;
+    }
+
+    // 4. a partial of a split row: slot `item`, 16 rows of (max, sum) and DVS sums
+    {
+      float* ml = ws_ml + (static_cast<size_t>(item) * kPfRows + col) * 2;
+      float* av = ws_acc + (static_cast<size_t>(item) * kPfRows + col) * DVS + 16 * g4;
+      if (g4 == 0) store_coherent_u64(ml, m, lrow);
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          store_coherent_u64(av + 64 * dq + 4 * i, acc[dq][0][i], acc[dq][1][i]);
+          store_coherent_u64(av + 64 * dq + 4 * i + 2, acc[dq][2][i], acc[dq][3][i]);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partial stores before the ticket
+    const int item0 = item - part;
+    uint32_t ticket = 0;
+    if (lane == 0)
+      ticket = __hip_atomic_fetch_add(&counters[item0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    if (ticket != static_cast<uint32_t>(parts - 1)) continue;
+
+    // 5. last arrival: merge the row tile's partials (slots item0 .. item0+parts-1)
+    float Mx = -INFINITY;
+    float den = 0.f;
+    float num[kDq][16];
+#pragma unroll
+    for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+      for (int k2 = 0; k2 < 16; ++k2) num[dq][k2] = 0.f;
+    for (int p0 = 0; p0 < parts; p0 += kMergeBatch) {
+      uint64_t pml[kMergeBatch];
+      uint64_t pv[kMergeBatch][kDq][8];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const size_t slot = static_cast<size_t>(item0 + min(p0 + u, parts - 1)) * kPfRows + col;
+        pml[u] = load_coherent_u64(ws_ml + slot * 2);
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int k2 = 0; k2 < 8; ++k2)
+            pv[u][dq][k2] = load_coherent_u64(ws_acc + slot * DVS + 64 * dq + 16 * g4 + 2 * k2);
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        if (p0 + u >= parts) break;
+        const float mu = lo_float(pml[u]);
+        if (mu == -INFINITY) continue;  // an empty partition
+        const float mn = fmaxf(Mx, mu);
+        const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
+        const float b = fast_exp2(mu - mn);
+        den = den * a + hi_float(pml[u]) * b;
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int k2 = 0; k2 < 8; ++k2) {
+            num[dq][2 * k2] = num[dq][2 * k2] * a + lo_float(pv[u][dq][k2]) * b;
+            num[dq][2 * k2 + 1] = num[dq][2 * k2 + 1] * a + hi_float(pv[u][dq][k2]) * b;
+          }
+        Mx = mn;
+      }
+    }
+    if (row_ok) {
+      float o[kDq][16];
+      const float inv = (den == 0.f) ? 0.f : 1.f / den;
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int k2 = 0; k2 < 16; ++k2) o[dq][k2] = num[dq][k2] * inv;
+      write_row(o);
+    }
+    if (lane == 0)  // ready for the next call
+      __hip_atomic_store(&counters[item0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <typename T, int DQK, int DV, int DVS, int KV_STRIDE, int BS>
+hipError_t run_prefill(const PrefillArgs& a, hipStream_t stream) {
+  using S16 = typename T::storage;
+  hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, DVS, KV_STRIDE, BS>), dim3(a.workgroups), dim3(kPfWaves * kWave), 0,
+                     stream, static_cast<S16*>(a.out), static_cast<const S16*>(a.q),
+                     static_cast<const char*>(a.k_pool), static_cast<const char*>(a.v_pool), a.block_tables,
+                     a.context_lens, a.query_start, a.counters, a.ws_ml, a.ws_acc, a.scale * kLog2e, a.num_seqs,
+                     a.num_query_rows, a.num_heads, a.num_kv_heads, a.num_heads / a.num_kv_heads, a.num_blocks,
+                     a.max_blocks_per_seq, a.part_tokens, a.max_items);
+  return hipGetLastError();
+}
+
+template <typename T, int DQK, int DV, int DVS, int KV_STRIDE>
+hipError_t run_prefill_bs(const PrefillArgs& a, hipStream_t stream) {
+  return a.block_size == 16 ? run_prefill<T, DQK, DV, DVS, KV_STRIDE, 16>(a, stream)
+                            : run_prefill<T, DQK, DV, DVS, KV_STRIDE, 32>(a, stream);
+}
+
+template <typename T>
+hipError_t run_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+  if (a.latent) return run_prefill_bs<T, kMlaQkDim, kMlaVDim, kMlaVSlice, kMlaQkDim>(a, stream);
+  return a.head_dim == 64 ? run_prefill_bs<T, 64, 64, 64, 64>(a, stream)
+                          : run_prefill_bs<T, 128, 128, 128, 128>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  return a.dtype == PA_DTYPE_BF16 ? run_prefill_t<BF16>(a, stream) : run_prefill_t<F16>(a, stream);
+}
+
+}  // namespace pa

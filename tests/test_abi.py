@@ -27,7 +27,9 @@ def test_every_declared_function_is_exported(lib):
     assert set(declared) == {"pa_abi_version", "pa_status_string", "pa_decode_workspace_size",
                              "pa_decode", "pa_reshape_and_cache", "pa_copy_blocks",
                              "pa_decode_fp8", "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8",
-                             "pa_swap_blocks", "pa_decode_gqa", "pa_decode_gqa_workspace_size"}
+                             "pa_swap_blocks", "pa_decode_gqa", "pa_decode_gqa_workspace_size",
+                             "pa_prefill", "pa_prefill_workspace_size", "pa_decode_mla",
+                             "pa_decode_mla_workspace_size"}
     raw = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
         assert hasattr(raw, name), name
@@ -35,7 +37,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
     for st in range(5):
         s = B.status_string(st)
         assert s.startswith("PA_")
@@ -291,3 +293,71 @@ def test_gqa_workspace_rules(lib):
     # explicit partitions: the same layout as pa_decode
     assert lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 512, F16, F16) == \
         lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 512)
+
+
+def _prefill(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, scale=0.125, bs=16, S=4, T=10,
+             H=8, Hkv=2, D=128, N=16, W=3, P=0, dt=F16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["scale"], a["bs"],
+                          a["S"], a["T"], a["H"], a["Hkv"], a["D"], a["N"], a["W"], a["P"], a["dt"], a["ws"],
+                          a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=F32), UNSUPPORTED),           # the matrix-core path takes 16-bit inputs
+    (dict(dt=E4M3), UNSUPPORTED),
+    (dict(D=96), UNSUPPORTED),
+    (dict(bs=8), UNSUPPORTED),
+    (dict(Hkv=3), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(S=-1), INVALID),
+    (dict(W=0), INVALID),
+    (dict(N=0), INVALID),
+    (dict(P=24), INVALID),                 # not a multiple of 16
+    (dict(P=-16), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(qs=None), INVALID),
+    (dict(q=MISALIGNED), INVALID),
+    (dict(qs=FAKE + 2), INVALID),
+    (dict(W=400, P=16), WORKSPACE),        # 400 partitions of 16 keys need a workspace
+    (dict(S=0), OK),
+    (dict(T=0), OK),
+])
+def test_prefill_rejects_before_launch(lib, kw, status):
+    assert _prefill(lib, **kw) == status
+
+
+def test_prefill_workspace_rules(lib):
+    # enough query rows to fill the GPU: no split, no workspace
+    assert lib.pa_prefill_workspace_size(8, 8192, 32, 8, 128, 256, 16, 0) == 0
+    # a few rows over long contexts: split, counters + partials, 256-byte multiple
+    ws = lib.pa_prefill_workspace_size(2, 8, 32, 8, 128, 8192, 16, 0)
+    assert ws > 0 and ws % 256 == 0
+    # one explicit partition covering the table: nothing to merge
+    assert lib.pa_prefill_workspace_size(2, 8, 32, 8, 128, 64, 16, 1024) == 0
+    assert lib.pa_prefill_workspace_size(2, 8, 32, 8, 128, 64, 16, 512) > 0
+    assert lib.pa_prefill_workspace_size(2, 8, 32, 3, 128, 64, 16, 0) == 0    # invalid grouping
+    assert lib.pa_prefill_workspace_size(2, 8, 32, 8, 96, 64, 16, 0) == 0     # unsupported head_dim
+
+
+def _mla(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kv=FAKE, bt=FAKE, cl=FAKE, scale=0.1, bs=16, S=4, H=16, N=16, W=3, P=0,
+             dt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.pa_decode_mla(a["out"], a["q"], a["kv"], a["bt"], a["cl"], a["scale"], a["bs"], a["S"],
+                             a["H"], a["N"], a["W"], a["P"], a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=F32), UNSUPPORTED),
+    (dict(bs=64), UNSUPPORTED),
+    (dict(H=0), INVALID),
+    (dict(S=-2), INVALID),
+    (dict(kv=None), INVALID),
+    (dict(kv=MISALIGNED), INVALID),
+    (dict(W=1000, P=16), WORKSPACE),
+    (dict(S=0), OK),
+])
+def test_decode_mla_rejects_before_launch(lib, kw, status):
+    assert _mla(lib, **kw) == status
