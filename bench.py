@@ -315,6 +315,180 @@ def swap_bench(pa, dev, steps: int, warmup: int) -> dict:
     }
 
 
+PEAK_MFMA_16BIT_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak (published)
+
+# multi-token query workloads (pa_prefill) and the latent cache (pa_decode_mla)
+QUERY_OPS = {
+    # a prompt chunk per sequence: 4 sequences whose last 1024 of 4096 tokens
+    # are new (chunked prefill), 32 query / 8 K/V heads, D=128, BS=16, fp16
+    "prefill": dict(S=4, lens="4096", tq=1024, H=32, Hkv=8, D=128, bs=16, dtype=torch.float16),
+    # speculative verification: 64 sequences with lengths as in continuous
+    # batching (log-normal, median 512, clipped to [32, 4096]), 4 drafted
+    # tokens each, 32 query / 8 K/V heads, D=128, BS=32, fp16
+    "verify": dict(S=64, lens="lognormal", tq=4, H=32, Hkv=8, D=128, bs=32, dtype=torch.float16),
+    # MLA decode: 32 sequences, lengths uniform in [1024, 8192], 16 heads (a
+    # 128-head model split over 8 GPUs by heads), 576-element latent rows,
+    # BS=32, bf16
+    "mla": dict(S=32, lens="uniform", tq=1, H=16, Hkv=1, D=576, bs=32, dtype=torch.bfloat16),
+}
+
+
+def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: int, cpu: bool,
+                  cpu_seconds: float) -> dict:
+    """One call of pa_prefill / pa_decode_mla per step, cold cache (pool
+    replicas rotated), HIP-graph replays timed with HIP events."""
+    from paged_kv_cache_186_amd import workloads as W
+    cfg = dict(QUERY_OPS[op])
+    if heads:
+        cfg["H"] = heads
+    S, H, Hkv, D, bs, dtype, tq = cfg["S"], cfg["H"], cfg["Hkv"], cfg["D"], cfg["bs"], cfg["dtype"], cfg["tq"]
+    mla = op == "mla"
+    Dv = pa.binding.MLA_V_DIM if mla else D
+    rng = np.random.default_rng(seed)
+    if cfg["lens"] == "4096":
+        lens = np.full(S, 4096, dtype=np.int64)
+    elif cfg["lens"] == "lognormal":
+        lens = np.clip(np.rint(rng.lognormal(math.log(512.0), 1.0, S)), 32, 4096).astype(np.int64)
+    else:
+        lens = rng.integers(1024, 8192, size=S, endpoint=True)
+    nb = int(sum(-(-int(L) // bs) for L in lens)) + 8
+    m = W.BlockManager(nb, bs, free_order=rng.permutation(nb).tolist())
+    for s, L in enumerate(lens):
+        m.allocate(s)
+        m.append_slots(s, int(L))
+    width = int(max(-(-int(L) // bs) for L in lens))
+    tables_np = m.block_tables(list(range(S)), width)
+    tables = torch.from_numpy(tables_np).to(dev)
+    clens = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    tq_s = np.full(S, tq, dtype=np.int64)
+    qs_np = np.concatenate([[0], np.cumsum(tq_s)]).astype(np.int32)
+    T = int(qs_np[-1])
+    qs = torch.from_numpy(qs_np).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed * 1000003 + 29)
+    base = (W.normal((nb, bs, D), dtype, dev, g),) if mla else \
+        (W.normal((nb, Hkv, bs, D), dtype, dev, g), W.normal((nb, Hkv, bs, D), dtype, dev, g))
+    q = W.normal((T, H, D), dtype, dev, g)
+    out = torch.empty((T, H, Dv), dtype=dtype, device=dev)
+    scale = 1.0 / math.sqrt(192.0 if mla else D)
+    pool_bytes = sum(t.numel() * t.element_size() for t in base)
+    R = max(1, math.ceil(COLD_BYTES / pool_bytes))
+    reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
+    ws_need = (pa.pa_decode_mla_workspace_size(S, H, width, bs) if mla
+               else pa.pa_prefill_workspace_size(S, T, H, Hkv, D, width, bs))
+    ws = pa.new_workspace(ws_need, dev)
+    log(f"{op}: {S} seqs, context {int(lens.min())}..{int(lens.max())} ({int(lens.sum())} tokens), "
+        f"{tq} query tokens each, {H} query / {Hkv} K/V heads, D={D}, BS={bs}, {dtype}; "
+        f"{R} pool replicas ({R * pool_bytes / 2**30:.2f} GiB)")
+
+    def call(i):
+        if mla:
+            pa.pa_decode_mla(out, q, reps[i % R][0], tables, clens, scale, bs, workspace=ws)
+        else:
+            kp, vp = reps[i % R]
+            pa.pa_prefill(out, q, kp, vp, tables, clens, qs, scale, bs, workspace=ws)
+
+    for i in range(max(1, warmup)):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    graph = capture(lambda: [call(i) for i in range(R)])
+    call(R - 1)
+    torch.cuda.synchronize()
+    want = out.clone()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out.view(torch.int16), want.view(torch.int16)):
+        raise RuntimeError("graph replay differs from the eager call")
+    n_rep = max(1, math.ceil(steps / R))
+    ms = time_graph(graph, n_rep, stream) / R
+
+    # algorithmic work: every (query row, visible key) pair once
+    e = 2
+    pairs = int(sum(sum(int(L) - tq + i + 1 for i in range(tq)) for L in lens))   # per query head
+    flops = pairs * H * 2 * (D + Dv)
+    kv_rows = int(lens.sum())
+    bytes_ = (kv_rows * Hkv * (D if mla else 2 * D) * e + T * H * (D + Dv) * e
+              + 4 * int(sum(-(-int(L) // bs) for L in lens)) + 4 * S + (4 * (S + 1) if not mla else 0))
+    t = ms * 1e-3
+    tflops = flops / t / 1e12
+    gbs = bytes_ / t / 1e9
+    mfma_bound = op == "prefill"
+    metric = {"prefill": "chunked prefill over the paged cache (pa_prefill): achieved TFLOP/s, 1 MI355X",
+              "verify": "speculative verification over the paged cache (pa_prefill): achieved HBM GB/s, 1 MI355X",
+              "mla": "MLA latent-cache decode (pa_decode_mla): achieved HBM GB/s, 1 MI355X"}[op]
+    result = {
+        "metric": metric,
+        "value": round(tflops if mfma_bound else gbs, 2),
+        "unit": "TFLOP/s" if mfma_bound else "GB/s",
+        "n_gpus": 1, "steps": n_rep * R, "warmup": warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if dtype == torch.float16 else "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block layout)",
+        "config": {"workload": f"{op}: {S} seqs x {tq} query tokens, context {int(lens.min())}..{int(lens.max())}, "
+                               f"{H} query / {Hkv} K/V heads, D={D}{' (latent, values 512)' if mla else ''}, "
+                               f"BS={bs}",
+                   "context_tokens": kv_rows, "query_rows": T,
+                   "cache": f"cold: rotates {R} pool replicas", "parallelism": "none (1 GPU)"},
+        "us_per_step": round(ms * 1e3, 3),
+        "flops_per_step": flops, "bytes_per_step": bytes_,
+        "achieved": {"TFLOP/s": round(tflops, 2), "GB/s": round(gbs, 2)},
+        "roofline": ({"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tflops, 2),
+                      "peak": PEAK_MFMA_16BIT_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(tflops / PEAK_MFMA_16BIT_TFLOPS, 4), "traffic": None}
+                     if mfma_bound else
+                     {"bound": "hbm", "kernel": "prefill_kernel", "achieved": round(gbs, 2),
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "traffic": None}),
+    }
+    if cpu:
+        result["cpu_baseline"] = queries_cpu_baseline(op, reps[0], q, tables_np, lens, qs_np, scale, bs, H, Hkv,
+                                                      D, Dv, tq, mfma_bound, cpu_seconds)
+    return result
+
+
+def queries_cpu_baseline(op, pools, q, tables_np, lens, qs_np, scale, bs, H, Hkv, D, Dv, tq, mfma_bound,
+                         seconds):
+    """The float64 oracle on a bounded sample: the first sequence's query
+    rows for the first K/V head's query heads (prefill, verify) or the first
+    two sequences (MLA), on one host thread, scaled to the metric's unit."""
+    from threadpoolctl import threadpool_limits
+    from oracle import mla_decode_ref, prefill_ref
+    torch.set_num_threads(1)
+    G = H // Hkv
+    if op == "mla":
+        n = 2
+        args = (q[:n].cpu(), pools[0].cpu(), tables_np[:n], lens[:n], scale, bs, Dv)
+        fn = mla_decode_ref
+        pairs = int(lens[:n].sum()) * H
+        work = pairs * 2 * (D + Dv) if mfma_bound else int(lens[:n].sum()) * D * 2 + n * H * (D + Dv) * 2
+        sample = f"MLA decode of the first {n} sequences, all {H} heads"
+    else:
+        rows = slice(int(qs_np[0]), int(qs_np[1]))
+        kp = pools[0][:, :1].cpu()
+        vp = pools[1][:, :1].cpu()
+        args = (q[rows, :G].cpu(), kp, vp, tables_np[:1], lens[:1], np.array([0, tq], np.int32), scale, bs)
+        fn = prefill_ref
+        L = int(lens[0])
+        pairs = sum(L - tq + i + 1 for i in range(tq)) * G
+        work = pairs * 2 * (D + Dv) if mfma_bound else L * D * 2 * 2 + tq * G * D * 2 * 2
+        sample = f"the first sequence's {tq} query rows for the {G} query heads of K/V head 0"
+    times = []
+    t_end = time.perf_counter() + seconds
+    with threadpool_limits(limits=1):
+        while True:
+            t0 = time.perf_counter()
+            fn(*args)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() >= t_end:
+                break
+    t = float(np.median(times))
+    return {"value": round(work / t / (1e12 if mfma_bound else 1e9), 6),
+            "unit": "TFLOP/s" if mfma_bound else "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}, run {len(times)} times on one host thread (float64 numpy), "
+                      f"median {t * 1e3:.1f} ms"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,8 +506,11 @@ def main() -> int:
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="K/V heads (0 = as many as query heads); fewer runs grouped-query decode "
                          "(pa_decode_gqa) over the first kv-heads heads of the pools")
-    ap.add_argument("--op", default="decode", choices=["decode", "swap"],
-                    help="decode: the decode step (default); swap: pa_swap_blocks over the host link")
+    ap.add_argument("--op", default="decode", choices=["decode", "swap", "prefill", "verify", "mla"],
+                    help="decode: the decode step (default); swap: pa_swap_blocks over the host link; "
+                         "prefill / verify: pa_prefill on a prompt-chunk / drafted-token workload; "
+                         "mla: pa_decode_mla")
+    ap.add_argument("--heads", type=int, default=0, help="query heads for --op prefill/verify/mla (0 = default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -351,6 +528,10 @@ def main() -> int:
 
     if args.op == "swap":
         print(json.dumps(swap_bench(pa, dev, min(args.steps, 50), min(args.warmup, 5))), flush=True)
+        return 0
+    if args.op in QUERY_OPS:
+        print(json.dumps(queries_bench(pa, dev, args.op, args.steps, min(args.warmup, 10), args.seed, args.heads,
+                                       not args.no_cpu_baseline, args.cpu_seconds)), flush=True)
         return 0
 
     from paged_kv_cache_186_amd import workloads as W
