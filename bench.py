@@ -45,13 +45,17 @@ KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
                             "pa_api.cpp")]
 
 
+PF_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
+              for f in ("pa_prefill.hip", "pa_attend.h", "pa_device.h", "pa_internal.h", "pa_api.cpp")]
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (sources or KERNEL_SOURCES):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -326,6 +330,9 @@ QUERY_OPS = {
     # batching (log-normal, median 512, clipped to [32, 4096]), 4 drafted
     # tokens each, 32 query / 8 K/V heads, D=128, BS=32, fp16
     "verify": dict(S=64, lens="lognormal", tq=4, H=32, Hkv=8, D=128, bs=32, dtype=torch.float16),
+    # the same batch with one query token each: grouped-query decode through
+    # the matrix-core kernel (compare pa_decode_gqa on continuous batching)
+    "verify1": dict(S=64, lens="lognormal", tq=1, H=32, Hkv=8, D=128, bs=32, dtype=torch.float16),
     # MLA decode: 32 sequences, lengths uniform in [1024, 8192], 16 heads (a
     # 128-head model split over 8 GPUs by heads), 576-element latent rows,
     # BS=32, bf16
@@ -334,7 +341,7 @@ QUERY_OPS = {
 
 
 def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: int, cpu: bool,
-                  cpu_seconds: float) -> dict:
+                  cpu_seconds: float, partition: int = 0) -> dict:
     """One call of pa_prefill / pa_decode_mla per step, cold cache (pool
     replicas rotated), HIP-graph replays timed with HIP events."""
     from paged_kv_cache_186_amd import workloads as W
@@ -344,6 +351,7 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
     S, H, Hkv, D, bs, dtype, tq = cfg["S"], cfg["H"], cfg["Hkv"], cfg["D"], cfg["bs"], cfg["dtype"], cfg["tq"]
     mla = op == "mla"
     Dv = pa.binding.MLA_V_DIM if mla else D
+    calibration_copy(pa, dev)
     rng = np.random.default_rng(seed)
     if cfg["lens"] == "4096":
         lens = np.full(S, 4096, dtype=np.int64)
@@ -374,8 +382,8 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
     pool_bytes = sum(t.numel() * t.element_size() for t in base)
     R = max(1, math.ceil(COLD_BYTES / pool_bytes))
     reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
-    ws_need = (pa.pa_decode_mla_workspace_size(S, H, width, bs) if mla
-               else pa.pa_prefill_workspace_size(S, T, H, Hkv, D, width, bs))
+    ws_need = (pa.pa_decode_mla_workspace_size(S, H, width, bs, partition) if mla
+               else pa.pa_prefill_workspace_size(S, T, H, Hkv, D, width, bs, partition))
     ws = pa.new_workspace(ws_need, dev)
     log(f"{op}: {S} seqs, context {int(lens.min())}..{int(lens.max())} ({int(lens.sum())} tokens), "
         f"{tq} query tokens each, {H} query / {Hkv} K/V heads, D={D}, BS={bs}, {dtype}; "
@@ -383,10 +391,11 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
 
     def call(i):
         if mla:
-            pa.pa_decode_mla(out, q, reps[i % R][0], tables, clens, scale, bs, workspace=ws)
+            pa.pa_decode_mla(out, q, reps[i % R][0], tables, clens, scale, bs, partition_size=partition,
+                             workspace=ws)
         else:
             kp, vp = reps[i % R]
-            pa.pa_prefill(out, q, kp, vp, tables, clens, qs, scale, bs, workspace=ws)
+            pa.pa_prefill(out, q, kp, vp, tables, clens, qs, scale, bs, partition_size=partition, workspace=ws)
 
     for i in range(max(1, warmup)):
         call(i)
@@ -414,8 +423,12 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
     tflops = flops / t / 1e12
     gbs = bytes_ / t / 1e9
     mfma_bound = op == "prefill"
+    digest = kernel_source_digest(PF_SOURCES)
+    tag = op + (f"_h{H}" if heads else "") + (f"_p{partition}" if partition else "")
+    traffic = traffic_from_profile(digest, os.path.join(PROFILES, f"prefill_kernel_{tag}_traffic.txt"))
     metric = {"prefill": "chunked prefill over the paged cache (pa_prefill): achieved TFLOP/s, 1 MI355X",
               "verify": "speculative verification over the paged cache (pa_prefill): achieved HBM GB/s, 1 MI355X",
+              "verify1": "one-token queries through pa_prefill: achieved HBM GB/s, 1 MI355X",
               "mla": "MLA latent-cache decode (pa_decode_mla): achieved HBM GB/s, 1 MI355X"}[op]
     result = {
         "metric": metric,
@@ -425,7 +438,8 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if dtype == torch.float16 else "bf16",
         "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block layout)",
-        "config": {"workload": f"{op}: {S} seqs x {tq} query tokens, context {int(lens.min())}..{int(lens.max())}, "
+        "config": {"partition": partition or "library default",
+                   "workload": f"{op}: {S} seqs x {tq} query tokens, context {int(lens.min())}..{int(lens.max())}, "
                                f"{H} query / {Hkv} K/V heads, D={D}{' (latent, values 512)' if mla else ''}, "
                                f"BS={bs}",
                    "context_tokens": kv_rows, "query_rows": T,
@@ -435,11 +449,12 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
         "achieved": {"TFLOP/s": round(tflops, 2), "GB/s": round(gbs, 2)},
         "roofline": ({"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tflops, 2),
                       "peak": PEAK_MFMA_16BIT_TFLOPS, "unit": "TFLOP/s",
-                      "frac": round(tflops / PEAK_MFMA_16BIT_TFLOPS, 4), "traffic": None}
+                      "frac": round(tflops / PEAK_MFMA_16BIT_TFLOPS, 4), "traffic": traffic,
+                      "kernel_source_sha": digest}
                      if mfma_bound else
                      {"bound": "hbm", "kernel": "prefill_kernel", "achieved": round(gbs, 2),
                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                      "traffic": None}),
+                      "traffic": traffic, "kernel_source_sha": digest}),
     }
     if cpu:
         result["cpu_baseline"] = queries_cpu_baseline(op, reps[0], q, tables_np, lens, qs_np, scale, bs, H, Hkv,
@@ -506,7 +521,7 @@ def main() -> int:
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="K/V heads (0 = as many as query heads); fewer runs grouped-query decode "
                          "(pa_decode_gqa) over the first kv-heads heads of the pools")
-    ap.add_argument("--op", default="decode", choices=["decode", "swap", "prefill", "verify", "mla"],
+    ap.add_argument("--op", default="decode", choices=["decode", "swap", "prefill", "verify", "verify1", "mla"],
                     help="decode: the decode step (default); swap: pa_swap_blocks over the host link; "
                          "prefill / verify: pa_prefill on a prompt-chunk / drafted-token workload; "
                          "mla: pa_decode_mla")
@@ -531,7 +546,7 @@ def main() -> int:
         return 0
     if args.op in QUERY_OPS:
         print(json.dumps(queries_bench(pa, dev, args.op, args.steps, min(args.warmup, 10), args.seed, args.heads,
-                                       not args.no_cpu_baseline, args.cpu_seconds)), flush=True)
+                                       not args.no_cpu_baseline, args.cpu_seconds, args.partition)), flush=True)
         return 0
 
     from paged_kv_cache_186_amd import workloads as W

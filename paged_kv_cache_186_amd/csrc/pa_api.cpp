@@ -197,16 +197,37 @@ struct PrefillPlan {
 };
 
 constexpr long long kPfTargetItems = 2048;  // ~2 waves per SIMD of a 256-CU GPU
-constexpr int kPfMinPartTokens = 256;
+// Default partition when contexts are split (measured on 64 sequences of
+// log-normal lengths, 4 query tokens, 8 K/V heads: 256 keys 86 us, 512 keys
+// 90 us, 1024 keys 70 us, 2048 keys 101 us; the latent cache, whose items
+// take 16 keys per step, did best at 512)
+constexpr int kPfPartTokens = 1024;
+constexpr int kPfPartTokensLatent = 512;
+constexpr int kPfMaxDefaultParts = 64;     // ... but no row merges more partials than this
 
-// Items are (sequence, K/V head, tile of 16 query rows, value slice,
-// partition).  Their number is bounded from host-known sizes: the tiles of a
-// call are at most ceil(T*G/16) + S (a sequence's partial tile adds at most
-// one), partitions at most ceil(W*BS / part_tokens).  partition_size 0 splits
-// the context only when the unsplit items would not fill the GPU.
+// 16-row tiles per wave: two when the sequences have at least 32 query rows
+// per K/V head on average (each K/V load then feeds twice the matrix work),
+// else one.  The latent cache always takes one (register budget).
+int prefill_row_tiles(int32_t num_seqs, int32_t num_query_rows, int32_t num_heads, int32_t num_kv_heads,
+                      bool latent) {
+#ifdef PA_PF_FORCE_ROW_TILES
+  if (!latent) return PA_PF_FORCE_ROW_TILES;
+#endif
+  if (latent || num_seqs <= 0) return 1;
+  const long long rows = static_cast<long long>(num_query_rows) * (num_heads / num_kv_heads);
+  return rows >= 32LL * num_seqs ? 2 : 1;
+}
+
+// Items are (sequence, K/V head, group of row_tiles 16-row tiles, value
+// slice, partition).  Their number is bounded from host-known sizes: the
+// tile groups of a call are at most ceil(T*G/(16*row_tiles)) + S (a
+// sequence's partial group adds at most one), partitions at most
+// ceil(W*BS / part_tokens).  partition_size 0 splits the context only when
+// the unsplit items would not fill the GPU, into partitions of 1024 keys (512
+// for the latent cache; fewer, larger ones beyond 64 partitions).
 PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_query_rows, int32_t num_heads,
                          int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t block_size,
-                         int32_t partition_size, int32_t v_per_item, int32_t slices) {
+                         int32_t partition_size, int32_t v_per_item, int32_t slices, int32_t row_tiles) {
   PrefillPlan p{PA_OK, 0, 0, 0, {0, 0, 0, 0}};
   if (num_seqs < 0 || num_query_rows < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
       num_heads % num_kv_heads != 0 || max_blocks_per_seq <= 0 ||
@@ -216,18 +237,18 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_query_rows, int32_t num_h
   }
   const long long ctx = static_cast<long long>(max_blocks_per_seq) * block_size;
   const long long group = num_heads / num_kv_heads;
-  const long long tiles = (static_cast<long long>(num_query_rows) * group + 15) / 16 + num_seqs;
+  const long long group_rows = 16LL * row_tiles;
+  const long long tiles = (static_cast<long long>(num_query_rows) * group + group_rows - 1) / group_rows + num_seqs;
   const long long base = tiles * num_kv_heads * slices;
   if (partition_size == 0) {
-    long long parts = 1;
-    if (base > 0 && base < kPfTargetItems) {
-      parts = (kPfTargetItems + base - 1) / base;
-      const long long most = (ctx + kPfMinPartTokens - 1) / kPfMinPartTokens;
-      parts = parts < most ? parts : most;
-      parts = parts < 1 ? 1 : parts;
+    if (base >= kPfTargetItems) {
+      p.part_tokens = static_cast<int>((ctx + 31) / 32 * 32);  // one partition
+    } else {
+      const long long spread = (ctx + kPfMaxDefaultParts - 1) / kPfMaxDefaultParts;
+      const long long dflt = slices > 1 ? kPfPartTokensLatent : kPfPartTokens;
+      const long long per = spread > dflt ? spread : dflt;
+      p.part_tokens = static_cast<int>((per + 31) / 32 * 32);
     }
-    const long long per = (ctx + parts - 1) / parts;
-    p.part_tokens = static_cast<int>((per + 15) / 16 * 16);
   } else {
     if (partition_size < 0 || partition_size % 16 != 0) {
       p.status = PA_ERR_INVALID_ARG;
@@ -241,11 +262,12 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_query_rows, int32_t num_h
     p.status = PA_ERR_INVALID_ARG;
     return p;
   }
-  const long long wg = (p.max_items + 3) / 4;
-  p.workgroups = static_cast<int>(wg < 1 ? 1 : (wg > pa::kPfMaxWorkgroups ? pa::kPfMaxWorkgroups : wg));
+  // a multiple of 8 workgroups: the kernel gives each XCD an equal share
+  const long long wg = ((p.max_items + 3) / 4 + 7) / 8 * 8;
+  p.workgroups = static_cast<int>(wg < 8 ? 8 : (wg > pa::kPfMaxWorkgroups ? pa::kPfMaxWorkgroups : wg));
   if (max_parts > 1)
-    p.ws = pa::workspace_layout(static_cast<size_t>(p.max_items), static_cast<size_t>(p.max_items) * 16,
-                                v_per_item);
+    p.ws = pa::workspace_layout(static_cast<size_t>(p.max_items),
+                                static_cast<size_t>(p.max_items) * group_rows, v_per_item);
   return p;
 }
 
@@ -262,9 +284,11 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const voi
   if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
   const int v_per_item = latent ? pa::kMlaVSlice : head_dim;
   const int slices = latent ? pa::kMlaVDim / pa::kMlaVSlice : 1;
+  if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  const int row_tiles = prefill_row_tiles(num_seqs, num_query_rows, num_heads, num_kv_heads, latent);
   const PrefillPlan plan = plan_prefill(num_seqs, num_query_rows, num_heads, num_kv_heads,
                                         max_blocks_per_seq, block_size, partition_size,
-                                        v_per_item, slices);
+                                        v_per_item, slices, row_tiles);
   if (plan.status != PA_OK) return plan.status;
   if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0 || num_query_rows == 0) return PA_OK;
@@ -293,6 +317,7 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const voi
   a.dtype = dtype;
   a.latent = latent;
   a.part_tokens = plan.part_tokens;
+  a.row_tiles = row_tiles;
   a.max_items = static_cast<int>(plan.max_items);
   a.workgroups = plan.workgroups;
   if (plan.ws.total > 0) {
@@ -555,8 +580,11 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_query_tokens, int
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                                  int32_t block_size, int32_t partition_size) {
   if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32)) return 0;
+  if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return 0;
   const PrefillPlan p = plan_prefill(num_seqs, num_query_tokens, num_heads, num_kv_heads,
-                                     max_blocks_per_seq, block_size, partition_size, head_dim, 1);
+                                     max_blocks_per_seq, block_size, partition_size, head_dim, 1,
+                                     prefill_row_tiles(num_seqs, num_query_tokens, num_heads, num_kv_heads,
+                                                       false));
   return p.status == PA_OK ? p.ws.total : 0;
 }
 
@@ -579,7 +607,7 @@ size_t pa_decode_mla_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t
                                     int32_t block_size, int32_t partition_size) {
   if (block_size != 16 && block_size != 32) return 0;
   const PrefillPlan p = plan_prefill(num_seqs, num_seqs, num_heads, 1, max_blocks_per_seq, block_size,
-                                     partition_size, pa::kMlaVSlice, pa::kMlaVDim / pa::kMlaVSlice);
+                                     partition_size, pa::kMlaVSlice, pa::kMlaVDim / pa::kMlaVSlice, 1);
   return p.status == PA_OK ? p.ws.total : 0;
 }
 

@@ -157,11 +157,12 @@ struct PrefillArgs {
   int dtype;        // PA_DTYPE_F16 or PA_DTYPE_BF16
   bool latent;
   int part_tokens;  // keys per context partition (multiple of 16)
+  int row_tiles;    // 16-row tiles per wave (1 or 2; latent: 1)
   int max_items;    // workspace capacity in items; the kernel never goes past it
   int workgroups;
   uint32_t* counters;  // [max_items] (null when no row can be split)
-  float* ws_ml;        // [max_items][16][2]
-  float* ws_acc;       // [max_items][16][value elements per item: DV, or kMlaVSlice]
+  float* ws_ml;        // [max_items][16 * row_tiles][2]
+  float* ws_acc;       // [max_items][16 * row_tiles][value elements per item: DV, or kMlaVSlice]
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

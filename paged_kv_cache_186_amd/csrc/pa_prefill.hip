@@ -97,40 +97,89 @@ struct Mfma<BF16> {
   }
 };
 
-// Element e (< 4) of a lane's 8-byte slice, in the low 16 bits.
-__device__ __forceinline__ uint32_t half_of(u32x2 v, int e) {
-  const uint32_t w = (e < 2) ? v.x : v.y;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+// One operand word of V^T: element e (< 4) of slice a in the low half and
+// element e of slice b in the high half (one v_perm_b32: result bytes pick
+// bytes of wa (selector values 0-3) and wb (4-7)).
+__device__ __forceinline__ uint32_t col_pair(u32x2 a, u32x2 b, int e) {
+  const uint32_t wa = (e < 2) ? a.x : a.y;
+  const uint32_t wb = (e < 2) ? b.x : b.y;
+  return __builtin_amdgcn_perm(wb, wa, (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
+// Deferred rescaling: the running sums keep the reference max m until some
+// row's scores exceed it by more than 2^kRescaleLog2 (then every row moves to
+// its new max).  Until then probabilities are at most 2^kRescaleLog2 = 256,
+// well inside fp32 and the 16-bit types the P.V products take; the final
+// ratio sum / weight does not depend on the reference, so only the number of
+// rescalings changes (rare after the first chunks of a row).
+constexpr float kRescaleLog2 = 8.f;
+
 constexpr int kPfWaves = 4;
-constexpr int kPfRows = 16;      // query rows per item (MFMA N of S^T)
-constexpr int kPfChunk = 16;     // keys per step (MFMA M of S^T)
+constexpr int kXcds = 8;     // MI355X: 8 XCDs of 32 CUs
+constexpr int kPfRows = 16;  // query rows per tile (MFMA N of S^T)
+
+// Operand words of the P.V products.  With KB = 2 key blocks of 16 per chunk
+// the product is 16x16x32 and its K index 8*(l/16) + j of lane l stands for
+// key 4*(l/16) + j (j < 4) of block 0 and key 16 + 4*(l/16) + j - 4 of block
+// 1 — any labelling of the summed index works as long as both operands use
+// it; with KB = 1 it is 16x16x16 over keys 4*(l/16) + j.
+template <typename T, int KB>
+struct PvOps;
+
+template <typename T>
+struct PvOps<T, 1> {
+  using word_t = u32x2;
+  static __device__ __forceinline__ f4_t mma(word_t a, word_t b, f4_t c) { return Mfma<T>::pv(a, b, c); }
+};
+
+template <>
+struct PvOps<F16, 2> {
+  using word_t = u32x4;
+  static __device__ __forceinline__ f4_t mma(word_t a, word_t b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c,
+                                                  0, 0, 0);
+  }
+};
+
+template <>
+struct PvOps<BF16, 2> {
+  using word_t = u32x4;
+  static __device__ __forceinline__ f4_t mma(word_t a, word_t b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, a), __builtin_bit_cast(b8_t, b), c,
+                                                   0, 0, 0);
+  }
+};
 
 // T: storage of q, pools and out (F16 or BF16).  DQK: elements of a query /
 // key row; DV: elements of a value row; DVS: value elements one item
 // produces (DV, or a slice of it: the 512-element latent values are split in
 // two items of 256 that share the scores, so that one wave's registers hold
-// the query, two chunks in flight and the accumulators without spilling);
-// KV_STRIDE: elements between consecutive value rows of the V pool (DV for a
-// separate V pool; DQK when values are the first DV elements of the key rows,
-// v_pool == k_pool).
-template <typename T, int DQK, int DV, int DVS, int KV_STRIDE, int BS>
-__global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 ? 1 : 2)) void prefill_kernel(
+// the query, two chunks in flight and the accumulators); KV_STRIDE: elements
+// between consecutive value rows of the V pool (DV for a separate V pool; DQK
+// when values are the first DV elements of the key rows, v_pool == k_pool).
+// KB: 16-key blocks per chunk (2: the P.V products run at the full 16x16x32
+// rate).  NT: 16-row tiles per wave; every K/V operand a wave loads serves
+// all NT tiles (more matrix work per byte when a sequence has many rows).
+template <typename T, int DQK, int DV, int DVS, int KV_STRIDE, int BS, int KB, int NT>
+__global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) void prefill_kernel(
     typename T::storage* __restrict__ out, const typename T::storage* __restrict__ q,
     const char* __restrict__ k_pool, const char* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     const int32_t* __restrict__ query_start, uint32_t* __restrict__ counters, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, float qk_scale, int num_seqs, int num_rows, int num_heads, int num_kv_heads,
-    int group, int num_blocks, int max_blocks, int part_tokens, int max_items) {
+    int group, int num_blocks, int max_blocks, int part_tokens, int max_items, uint32_t q_sign_bits) {
   static_assert(DQK % 32 == 0 && DVS % 64 == 0 && DV % DVS == 0, "MFMA slices");
-  static_assert(BS % kPfChunk == 0, "a chunk never crosses a block");
+  static_assert(BS % 16 == 0, "a 16-key block never crosses a cache block");
   using S16 = typename T::storage;
   using M = Mfma<T>;
-  constexpr int kQK = DQK / 32;   // S^T products per chunk
+  using PV = PvOps<T, KB>;
+  using pw_t = typename PV::word_t;
+  constexpr int kQK = DQK / 32;   // S^T products per 16 keys
   constexpr int kDq = DVS / 64;   // 64-element value slices of an item
   constexpr int kSlices = DV / DVS;
-  constexpr int kMergeBatch = DVS <= 128 ? 4 : 1;  // partials loaded at once while merging
+  constexpr int kChunk = 16 * KB;
+  constexpr int kGroupRows = kPfRows * NT;
+  constexpr int kMergeBatch = DVS <= 128 ? 4 : 2;  // partials loaded at once while merging (<= 128 VGPRs)
   constexpr int kThreads = kPfWaves * kWave;
   constexpr int kPer = (kPfMaxSeqs + kThreads - 1) / kThreads;
   __shared__ int s_off[kPfMaxSeqs + 1];  // items of all sequences before s
@@ -159,7 +208,7 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 ? 1 : 2)) void prefill_
     int c = 0;
     if (s < S) {
       const int rows = max(s_q0[s + 1] - s_q0[s], 0) * group;
-      const int tiles = rows > 0 ? (rows + kPfRows - 1) / kPfRows : 0;
+      const int tiles = rows > 0 ? (rows + kGroupRows - 1) / kGroupRows : 0;
       const int parts = max(1, (s_len[s] + part_tokens - 1) / part_tokens);
       c = HKV * tiles * kSlices * parts;
     }
@@ -195,12 +244,22 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 ? 1 : 2)) void prefill_
   // contract (overlapping ranges) could ask for more: those items are dropped
   total = min(__builtin_amdgcn_readfirstlane(total), max_items);
 
-  const int col = lane % 16;  // query row of the tile / key of a chunk (A rows)
+  const u32x4 q_sign = {q_sign_bits, q_sign_bits, q_sign_bits, q_sign_bits};
+  const int col = lane % 16;  // query row of a tile / key of a 16-key block (A rows)
   const int g4 = lane / 16;   // lane group: 8-element slice of S^T's K dim, key quad of P
   const int NH = num_heads;
 
-  for (int item = blockIdx.x * kPfWaves + wave; item < total; item += gridDim.x * kPfWaves) {
-    // 2. which (sequence, K/V head, tile, partition)
+  // XCD-aware item order: workgroups are dispatched to the 8 XCDs round
+  // robin (workgroup i on XCD i % 8), and each XCD has its own L2.  The items
+  // are cut into 8 contiguous ranges, one per XCD, so that the row tiles and
+  // partitions of one (sequence, K/V head) — which read the same keys and
+  // values — run on one XCD and share its L2 (the grid is a multiple of 8).
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int x_end = min(total, (xcd + 1) * per_xcd);
+  const int x_step = (gridDim.x / kXcds) * kPfWaves;
+  for (int item = xcd * per_xcd + (blockIdx.x / kXcds) * kPfWaves + wave; item < x_end; item += x_step) {
+    // 2. which (sequence, K/V head, tile group, value slice, partition)
     int lo = 0;
     int hi = S - 1;
     while (lo < hi) {
@@ -215,156 +274,208 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 ? 1 : 2)) void prefill_
     const int q0 = __builtin_amdgcn_readfirstlane(s_q0[s]);
     const int Tq = max(__builtin_amdgcn_readfirstlane(s_q0[s + 1]) - q0, 0);
     const int Mrows = Tq * group;
-    const int tiles = (Mrows + kPfRows - 1) / kPfRows;
+    const int tiles = (Mrows + kGroupRows - 1) / kGroupRows;
     const int parts = max(1, (L + part_tokens - 1) / part_tokens);
+    // value slices fastest (the slices of one partition read the same key
+    // rows: adjacent waves, mostly of one workgroup, so the second read
+    // hits the cache), then partitions
     const int local = item - __builtin_amdgcn_readfirstlane(s_off[s]);
-    const int part = local % parts;
-    const int rest = local / parts;
-    const int slice = rest % kSlices;
-    const int rest2 = rest / kSlices;
-    const int tile = rest2 % tiles;
+    const int slice = local % kSlices;
+    const int rest = local / kSlices;
+    const int part = rest % parts;
+    const int rest2 = rest / parts;
+    const int tg = rest2 % tiles;
     const int hk = rest2 / tiles;
     const int v_off = slice * DVS;  // first value element of the item
 
-    // this lane's query row
-    const int r = tile * kPfRows + col;
-    const bool row_ok = r < Mrows;
-    const int ti = row_ok ? r / group : 0;
-    const int h = hk * group + (row_ok ? r % group : 0);
-    const int pos = row_ok ? L - Tq + ti : -1;  // keys 0..pos are visible
+    // this lane's query row in each tile
+    bool row_ok[NT];
+    int ti[NT], h[NT], pos[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r = (tg * NT + t) * kPfRows + col;
+      row_ok[t] = r < Mrows;
+      ti[t] = row_ok[t] ? r / group : 0;
+      h[t] = hk * group + (row_ok[t] ? r % group : 0);
+      pos[t] = row_ok[t] ? L - Tq + ti[t] : -1;  // keys 0..pos are visible
+    }
     // wave-uniform key range of the item
-    const int r_last = min(Mrows, (tile + 1) * kPfRows) - 1;
+    const int r_last = min(Mrows, (tg + 1) * kGroupRows) - 1;
     const int pos_max = L - Tq + r_last / group;
-    const int pos_min = L - Tq + (tile * kPfRows) / group;
+    const int pos_min = L - Tq + (tg * kGroupRows) / group;
     const int k_begin = part * part_tokens;
     const int k_end = min(min(k_begin + part_tokens, L), pos_max + 1);
 
     // query slices (B operand of S^T): lane holds elements 32j + 8*g4 .. +7
-    u32x4 qv[kQK];
-    {
-      const S16* qrow = q + (static_cast<size_t>(q0 + ti) * NH + h) * DQK + 8 * g4;
+    u32x4 qv[NT][kQK];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const S16* qrow = q + (static_cast<size_t>(q0 + ti[t]) * NH + h[t]) * DQK + 8 * g4;
 #pragma unroll
       for (int j = 0; j < kQK; ++j) {
-        const u32x4 v = load16(qrow + 32 * j);
-        qv[j] = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 v = load16(qrow + 32 * j) ^ q_sign;  // a negative scale flips q's signs instead
+        qv[t][j] = row_ok[t] ? v : u32x4{0u, 0u, 0u, 0u};
       }
     }
 
-    float m = -INFINITY;  // running max of row `col` (same in its 4 lanes)
-    float lsum = 0.f;     // this lane's share of the row's running sum
-    f4_t acc[kDq][4];     // O^T products: [slice][column label e]
+    float m[NT];     // running max of row `col` of tile t (same in its 4 lanes)
+    float lsum[NT];  // this lane's share of that row's running sum
+    f4_t acc[NT][kDq][4];  // O^T products: [tile][slice][column label e]
 #pragma unroll
-    for (int dq = 0; dq < kDq; ++dq)
+    for (int t = 0; t < NT; ++t) {
+      m[t] = -INFINITY;
+      lsum[t] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[dq][e] = f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][dq][e] = f4_t{0.f, 0.f, 0.f, 0.f};
+    }
     int bad = 0;
 
     struct Stage {
-      u32x4 k[kQK];
-      u32x2 v[kDq][4];
+      u32x4 k[KB][kQK];
+      u32x2 v[KB][kDq][4];
       int c;  // first key of the chunk
       int bad;
     };
     const int32_t* tbl = block_tables + static_cast<size_t>(s) * max_blocks;
     auto load_chunk = [&](Stage& st, int c) __attribute__((always_inline)) {
       st.c = c;
-      int phys = tbl[c / BS];
       st.bad = 0;
-      if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
-        st.bad = 1;  // never dereference an id outside the pool
-        phys = 0;
-      }
-      const size_t row0 = (static_cast<size_t>(phys) * HKV + hk) * BS + (c % BS);
-      const char* kb = k_pool + ((row0 + col) * DQK + 8 * g4) * sizeof(S16);
 #pragma unroll
-      for (int j = 0; j < kQK; ++j) st.k[j] = load16(kb + 32 * j * sizeof(S16));
-#pragma unroll
-      for (int dq = 0; dq < kDq; ++dq)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const char* vb = v_pool + ((row0 + 4 * g4 + e) * KV_STRIDE + v_off + 64 * dq + 4 * col) * sizeof(S16);
-          st.v[dq][e] = *reinterpret_cast<const u32x2*>(vb);
+      for (int kb = 0; kb < KB; ++kb) {
+        // a 16-key block wholly past the item's keys (tail chunk) reads the
+        // chunk's first block again instead — its table entry may not exist,
+        // and a block the item does not need must not poison it: its keys
+        // are masked (and values past the context zeroed) like any other
+        const int key0 = (c + 16 * kb < k_end) ? c + 16 * kb : c;
+        int phys = tbl[key0 / BS];
+        if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
+          st.bad = 1;  // never dereference an id outside the pool
+          phys = 0;
         }
+        const size_t row0 = (static_cast<size_t>(phys) * HKV + hk) * BS + (key0 % BS);
+        const char* kb_ptr = k_pool + ((row0 + col) * DQK + 8 * g4) * sizeof(S16);
+#pragma unroll
+        for (int j = 0; j < kQK; ++j) st.k[kb][j] = load16(kb_ptr + 32 * j * sizeof(S16));
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const char* vb =
+                v_pool + ((row0 + 4 * g4 + e) * KV_STRIDE + v_off + 64 * dq + 4 * col) * sizeof(S16);
+            st.v[kb][dq][e] = *reinterpret_cast<const u32x2*>(vb);
+          }
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
 
     auto attend_chunk = [&](Stage& st) __attribute__((always_inline)) {
       bad |= st.bad;
-      f4_t sc = {0.f, 0.f, 0.f, 0.f};
+      if (st.c + kChunk > L) {  // value rows past the context may hold anything: zero
 #pragma unroll
-      for (int j = 0; j < kQK; ++j) sc = M::qk(st.k[j], qv[j], sc);
-      const int key0 = st.c + 4 * g4;  // key of sc[0]
-      float z[4];
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = sc[i] * qk_scale;
-      if (st.c + kPfChunk - 1 > pos_min) {  // some key is after some row's position
+          for (int e = 0; e < 4; ++e)
+            if (st.c + 16 * kb + 4 * g4 + e >= L)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) z[i] = (key0 + i <= pos) ? z[i] : -INFINITY;
+              for (int dq = 0; dq < kDq; ++dq) st.v[kb][dq][e] = u32x2{0u, 0u};
       }
-      if (st.c + kPfChunk > L) {  // value rows past the context: zero
+      const bool masked = (st.c + kChunk - 1 > pos_min) || (st.c + kChunk > k_end);
+      pw_t pw[NT];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (key0 + e >= L)
+      for (int t = 0; t < NT; ++t) {
+        // raw scores <q, k> (the softmax scale is folded into the exponent)
+        float z[KB][4];
 #pragma unroll
-            for (int dq = 0; dq < kDq; ++dq) st.v[dq][e] = u32x2{0u, 0u};
+        for (int kb = 0; kb < KB; ++kb) {
+          f4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < kQK; ++j) sc = M::qk(st.k[kb][j], qv[t][j], sc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[kb][i] = sc[i];
+          if (masked) {
+            const int key0 = st.c + 16 * kb + 4 * g4;  // key of z[kb][0]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[kb][i] = (key0 + i <= pos[t] && key0 + i < k_end) ? z[kb][i] : -INFINITY;
+          }
+        }
+        float cm = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) cm = fmaxf(cm, fmaxf(fmaxf(z[kb][0], z[kb][1]), fmaxf(z[kb][2], z[kb][3])));
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        const float cms = (cm == -INFINITY) ? -INFINITY : cm * qk_scale;  // qk_scale > 0
+        const float mn = fmaxf(m[t], cms);
+        if (__builtin_amdgcn_ballot_w64(mn > m[t] + kRescaleLog2) != 0) {
+          const float alpha = (m[t] == -INFINITY) ? 0.f : fast_exp2(m[t] - mn);
+          lsum[t] *= alpha;
+#pragma unroll
+          for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t][dq][e] *= alpha;
+          m[t] = mn;
+        }
+        // p = 2^(scale*log2e*z - m); in a fully visible chunk every row has a
+        // finite reference by now, so no masked term needs a guard there
+        const float nm = -m[t];
+        float p[KB][4];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
+            p[kb][i] = (masked && z[kb][i] == -INFINITY) ? 0.f : x;
+            lsum[t] += p[kb][i];
+          }
+        if constexpr (KB == 1) {
+          pw[t] = pw_t{M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3])};
+        } else {
+          pw[t] = pw_t{M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3]), M::pack2(p[1][0], p[1][1]),
+                       M::pack2(p[1][2], p[1][3])};
+        }
       }
-      float cm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      cm = fmaxf(cm, __shfl_xor(cm, 16));
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
-      const float mn = fmaxf(m, cm);
-      if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
-        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
-        lsum *= alpha;
-#pragma unroll
-        for (int dq = 0; dq < kDq; ++dq)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[dq][e] *= alpha;
-        m = mn;
-      }
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = (z[i] == -INFINITY) ? 0.f : fast_exp2(z[i] - m);
-      lsum += (p[0] + p[1]) + (p[2] + p[3]);
-      const u32x2 pw = {M::pack2(p[0], p[1]), M::pack2(p[2], p[3])};
 #pragma unroll
       for (int dq = 0; dq < kDq; ++dq)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // column e of this slice for the lane's 4 keys: rows 4*g4 .. +3 of V
-          const u32x2 a = {half_of(st.v[dq][0], e) | (half_of(st.v[dq][1], e) << 16),
-                           half_of(st.v[dq][2], e) | (half_of(st.v[dq][3], e) << 16)};
-          acc[dq][e] = M::pv(a, pw, acc[dq][e]);
+          // column e of this slice for the lane's keys (rows 4*g4 .. +3 of each block)
+          pw_t a;
+          if constexpr (KB == 1) {
+            a = pw_t{col_pair(st.v[0][dq][0], st.v[0][dq][1], e), col_pair(st.v[0][dq][2], st.v[0][dq][3], e)};
+          } else {
+            a = pw_t{col_pair(st.v[0][dq][0], st.v[0][dq][1], e), col_pair(st.v[0][dq][2], st.v[0][dq][3], e),
+                     col_pair(st.v[1][dq][0], st.v[1][dq][1], e), col_pair(st.v[1][dq][2], st.v[1][dq][3], e)};
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t][dq][e] = PV::mma(a, pw[t], acc[t][dq][e]);
         }
     };
 
     // 3. the chunks of the item, two in flight
-    const int c_first = k_begin;
-    const int n_chunks = k_end > k_begin ? (k_end - k_begin + kPfChunk - 1) / kPfChunk : 0;
+    const int n_chunks = k_end > k_begin ? (k_end - k_begin + kChunk - 1) / kChunk : 0;
     if (n_chunks > 0) {
       Stage a, b;
-      load_chunk(a, c_first);
-      int t = 0;
-      for (; t + 2 < n_chunks; t += 2) {
-        load_chunk(b, c_first + (t + 1) * kPfChunk);
+      load_chunk(a, k_begin);
+      int c = 0;
+      for (; c + 2 < n_chunks; c += 2) {
+        load_chunk(b, k_begin + (c + 1) * kChunk);
         attend_chunk(a);
-        load_chunk(a, c_first + (t + 2) * kPfChunk);
+        load_chunk(a, k_begin + (c + 2) * kChunk);
         attend_chunk(b);
       }
-      if (t + 1 < n_chunks) {
-        load_chunk(b, c_first + (t + 1) * kPfChunk);
+      if (c + 1 < n_chunks) {
+        load_chunk(b, k_begin + (c + 1) * kChunk);
         attend_chunk(a);
         attend_chunk(b);
       } else {
         attend_chunk(a);
       }
     }
-    float lrow = lsum + __shfl_xor(lsum, 16);
-    lrow += __shfl_xor(lrow, 32);
-    if (bad) lrow = __builtin_nanf("");
 
-    // lane holds, for row `col`, output elements 64*dq + 16*g4 + 4*i + e
-    auto write_row = [&](const float (&o)[kDq][16]) __attribute__((always_inline)) {
-      S16* orow = out + (static_cast<size_t>(q0 + ti) * NH + h) * DV + v_off + 16 * g4;
+    // lane holds, for row `col` of tile t, output elements 64*dq + 16*g4 + 4*i + e
+    auto write_row = [&](int t, const float (&o)[kDq][16]) __attribute__((always_inline)) {
+      S16* orow = out + (static_cast<size_t>(q0 + ti[t]) * NH + h[t]) * DV + v_off + 16 * g4;
 #pragma unroll
       for (int dq = 0; dq < kDq; ++dq) {
         uint32_t w[8];
@@ -375,119 +486,141 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 ? 1 : 2)) void prefill_
       }
     };
 
+    float lrow[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      lrow[t] = lsum[t] + __shfl_xor(lsum[t], 16);
+      lrow[t] += __shfl_xor(lrow[t], 32);
+      if (bad) lrow[t] = __builtin_nanf("");
+    }
+
     if (parts == 1) {
-      if (row_ok) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (!row_ok[t]) continue;
         float o[kDq][16];
-        const float inv = (lrow == 0.f) ? 0.f : 1.f / lrow;  // no visible key (empty context): zeros
+        const float inv = (lrow[t] == 0.f) ? 0.f : 1.f / lrow[t];  // no visible key (empty context): zeros
 #pragma unroll
         for (int dq = 0; dq < kDq; ++dq)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[dq][4 * i + e] = acc[dq][e][i] * inv;
-        write_row(o);
+            for (int e = 0; e < 4; ++e) o[dq][4 * i + e] = acc[t][dq][e][i] * inv;
+        write_row(t, o);
       }
       continue;
     }
 
-    // 4. a partial of a split row: slot `item`, 16 rows of (max, sum) and DVS sums
-    {
-      float* ml = ws_ml + (static_cast<size_t>(item) * kPfRows + col) * 2;
-      float* av = ws_acc + (static_cast<size_t>(item) * kPfRows + col) * DVS + 16 * g4;
-      if (g4 == 0) store_coherent_u64(ml, m, lrow);
+    // 4. a partial of a split row group: slot `item`, NT x 16 rows of
+    //    (max, sum) and DVS sums
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t row = (static_cast<size_t>(item) * NT + t) * kPfRows + col;
+      float* av = ws_acc + row * DVS + 16 * g4;
+      if (g4 == 0) store_coherent_u64(ws_ml + row * 2, m[t], lrow[t]);
 #pragma unroll
       for (int dq = 0; dq < kDq; ++dq)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          store_coherent_u64(av + 64 * dq + 4 * i, acc[dq][0][i], acc[dq][1][i]);
-          store_coherent_u64(av + 64 * dq + 4 * i + 2, acc[dq][2][i], acc[dq][3][i]);
+          store_coherent_u64(av + 64 * dq + 4 * i, acc[t][dq][0][i], acc[t][dq][1][i]);
+          store_coherent_u64(av + 64 * dq + 4 * i + 2, acc[t][dq][2][i], acc[t][dq][3][i]);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partial stores before the ticket
-    const int item0 = item - part;
+    const int item0 = item - part * kSlices;  // the partition-0 item of this tile group and slice
     uint32_t ticket = 0;
     if (lane == 0)
       ticket = __hip_atomic_fetch_add(&counters[item0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ticket = __builtin_amdgcn_readfirstlane(ticket);
     if (ticket != static_cast<uint32_t>(parts - 1)) continue;
 
-    // 5. last arrival: merge the row tile's partials (slots item0 .. item0+parts-1)
-    float Mx = -INFINITY;
-    float den = 0.f;
-    float num[kDq][16];
+    // 5. last arrival: merge the partials of each tile (slots item0 + p*kSlices, p < parts)
 #pragma unroll
-    for (int dq = 0; dq < kDq; ++dq)
-#pragma unroll
-      for (int k2 = 0; k2 < 16; ++k2) num[dq][k2] = 0.f;
-    for (int p0 = 0; p0 < parts; p0 += kMergeBatch) {
-      uint64_t pml[kMergeBatch];
-      uint64_t pv[kMergeBatch][kDq][8];
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const size_t slot = static_cast<size_t>(item0 + min(p0 + u, parts - 1)) * kPfRows + col;
-        pml[u] = load_coherent_u64(ws_ml + slot * 2);
-#pragma unroll
-        for (int dq = 0; dq < kDq; ++dq)
-#pragma unroll
-          for (int k2 = 0; k2 < 8; ++k2)
-            pv[u][dq][k2] = load_coherent_u64(ws_acc + slot * DVS + 64 * dq + 16 * g4 + 2 * k2);
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        if (p0 + u >= parts) break;
-        const float mu = lo_float(pml[u]);
-        if (mu == -INFINITY) continue;  // an empty partition
-        const float mn = fmaxf(Mx, mu);
-        const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
-        const float b = fast_exp2(mu - mn);
-        den = den * a + hi_float(pml[u]) * b;
-#pragma unroll
-        for (int dq = 0; dq < kDq; ++dq)
-#pragma unroll
-          for (int k2 = 0; k2 < 8; ++k2) {
-            num[dq][2 * k2] = num[dq][2 * k2] * a + lo_float(pv[u][dq][k2]) * b;
-            num[dq][2 * k2 + 1] = num[dq][2 * k2 + 1] * a + hi_float(pv[u][dq][k2]) * b;
-          }
-        Mx = mn;
-      }
-    }
-    if (row_ok) {
-      float o[kDq][16];
-      const float inv = (den == 0.f) ? 0.f : 1.f / den;
+    for (int t = 0; t < NT; ++t) {
+      float Mx = -INFINITY;
+      float den = 0.f;
+      float num[kDq][16];
 #pragma unroll
       for (int dq = 0; dq < kDq; ++dq)
 #pragma unroll
-        for (int k2 = 0; k2 < 16; ++k2) o[dq][k2] = num[dq][k2] * inv;
-      write_row(o);
+        for (int k2 = 0; k2 < 16; ++k2) num[dq][k2] = 0.f;
+      for (int p0 = 0; p0 < parts; p0 += kMergeBatch) {
+        uint64_t pml[kMergeBatch];
+        uint64_t pv[kMergeBatch][kDq][8];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const size_t slot = static_cast<size_t>(item0) + static_cast<size_t>(min(p0 + u, parts - 1)) * kSlices;
+          const size_t row = (slot * NT + t) * kPfRows + col;
+          pml[u] = load_coherent_u64(ws_ml + row * 2);
+#pragma unroll
+          for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+            for (int k2 = 0; k2 < 8; ++k2)
+              pv[u][dq][k2] = load_coherent_u64(ws_acc + row * DVS + 64 * dq + 16 * g4 + 2 * k2);
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          if (p0 + u >= parts) break;
+          const float mu = lo_float(pml[u]);
+          if (mu == -INFINITY) continue;  // an empty partition
+          const float mn = fmaxf(Mx, mu);
+          const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
+          const float b = fast_exp2(mu - mn);
+          den = den * a + hi_float(pml[u]) * b;
+#pragma unroll
+          for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+            for (int k2 = 0; k2 < 8; ++k2) {
+              num[dq][2 * k2] = num[dq][2 * k2] * a + lo_float(pv[u][dq][k2]) * b;
+              num[dq][2 * k2 + 1] = num[dq][2 * k2 + 1] * a + hi_float(pv[u][dq][k2]) * b;
+            }
+          Mx = mn;
+        }
+      }
+      if (row_ok[t]) {
+        float o[kDq][16];
+        const float inv = (den == 0.f) ? 0.f : 1.f / den;
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int k2 = 0; k2 < 16; ++k2) o[dq][k2] = num[dq][k2] * inv;
+        write_row(t, o);
+      }
     }
     if (lane == 0)  // ready for the next call
       __hip_atomic_store(&counters[item0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-template <typename T, int DQK, int DV, int DVS, int KV_STRIDE, int BS>
+template <typename T, int DQK, int DV, int DVS, int KV_STRIDE, int BS, int KB, int NT>
 hipError_t run_prefill(const PrefillArgs& a, hipStream_t stream) {
   using S16 = typename T::storage;
-  hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, DVS, KV_STRIDE, BS>), dim3(a.workgroups), dim3(kPfWaves * kWave), 0,
-                     stream, static_cast<S16*>(a.out), static_cast<const S16*>(a.q),
+  hipLaunchKernelGGL((prefill_kernel<T, DQK, DV, DVS, KV_STRIDE, BS, KB, NT>), dim3(a.workgroups),
+                     dim3(kPfWaves * kWave), 0, stream, static_cast<S16*>(a.out), static_cast<const S16*>(a.q),
                      static_cast<const char*>(a.k_pool), static_cast<const char*>(a.v_pool), a.block_tables,
-                     a.context_lens, a.query_start, a.counters, a.ws_ml, a.ws_acc, a.scale * kLog2e, a.num_seqs,
-                     a.num_query_rows, a.num_heads, a.num_kv_heads, a.num_heads / a.num_kv_heads, a.num_blocks,
-                     a.max_blocks_per_seq, a.part_tokens, a.max_items);
+                     a.context_lens, a.query_start, a.counters, a.ws_ml, a.ws_acc, fabsf(a.scale) * kLog2e,
+                     a.num_seqs, a.num_query_rows, a.num_heads, a.num_kv_heads, a.num_heads / a.num_kv_heads,
+                     a.num_blocks, a.max_blocks_per_seq, a.part_tokens, a.max_items,
+                     a.scale < 0.f ? 0x80008000u : 0u);
   return hipGetLastError();
 }
 
-template <typename T, int DQK, int DV, int DVS, int KV_STRIDE>
+template <typename T, int DQK, int DV, int DVS, int KV_STRIDE, int KB, int NT>
 hipError_t run_prefill_bs(const PrefillArgs& a, hipStream_t stream) {
-  return a.block_size == 16 ? run_prefill<T, DQK, DV, DVS, KV_STRIDE, 16>(a, stream)
-                            : run_prefill<T, DQK, DV, DVS, KV_STRIDE, 32>(a, stream);
+  return a.block_size == 16 ? run_prefill<T, DQK, DV, DVS, KV_STRIDE, 16, KB, NT>(a, stream)
+                            : run_prefill<T, DQK, DV, DVS, KV_STRIDE, 32, KB, NT>(a, stream);
+}
+
+template <typename T, int D>
+hipError_t run_prefill_nt(const PrefillArgs& a, hipStream_t stream) {
+  return a.row_tiles == 2 ? run_prefill_bs<T, D, D, D, D, 2, 2>(a, stream)
+                          : run_prefill_bs<T, D, D, D, D, 2, 1>(a, stream);
 }
 
 template <typename T>
 hipError_t run_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  if (a.latent) return run_prefill_bs<T, kMlaQkDim, kMlaVDim, kMlaVSlice, kMlaQkDim>(a, stream);
-  return a.head_dim == 64 ? run_prefill_bs<T, 64, 64, 64, 64>(a, stream)
-                          : run_prefill_bs<T, 128, 128, 128, 128>(a, stream);
+  if (a.latent) return run_prefill_bs<T, kMlaQkDim, kMlaVDim, kMlaVSlice, kMlaQkDim, 1, 1>(a, stream);
+  return a.head_dim == 64 ? run_prefill_nt<T, 64>(a, stream) : run_prefill_nt<T, 128>(a, stream);
 }
 
 }  // namespace

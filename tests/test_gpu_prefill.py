@@ -43,20 +43,21 @@ class Case:
         self.qs = np.concatenate([[0], np.cumsum(self.tq)]).astype(np.int32)
         self.q = W.normal((int(self.qs[-1]), H, D), dtype, DEV, g)
 
-    def run(self, partition_size=0, tables=None, q=None):
+    def run(self, partition_size=0, tables=None, q=None, scale=None):
         w = self.w
         q = self.q if q is None else q
         out = torch.empty_like(q)
         bt = w.block_tables().to(DEV) if tables is None else tables
         pa.pa_prefill(out, q, w.k_pool, w.v_pool, bt, w.context_lens().to(DEV),
-                      torch.from_numpy(self.qs).to(DEV), w.scale, w.block_size, partition_size=partition_size)
+                      torch.from_numpy(self.qs).to(DEV), w.scale if scale is None else scale, w.block_size,
+                      partition_size=partition_size)
         torch.cuda.synchronize()
         return out
 
-    def oracle(self):
+    def oracle(self, scale=None):
         w = self.w
         return prefill_ref(self.q.cpu(), w.k_pool.cpu(), w.v_pool.cpu(), w.block_tables_np(),
-                           w.context_lens_np(), self.qs, w.scale, w.block_size)
+                           w.context_lens_np(), self.qs, w.scale if scale is None else scale, w.block_size)
 
 
 # (context length, query tokens): whole prompts, prompt chunks, drafted
@@ -163,10 +164,21 @@ def test_repeat_calls_are_bit_identical_and_counters_return_to_zero():
         assert torch.equal(bits(o), bits(outs[0]))
     from paged_kv_cache_186_amd.binding import PagedAttnError
     # the ticket counters (one uint32 per item, first in the workspace, then
-    # 16 (max, sum) pairs and 16 x D sums per item) are back at zero
-    items = (need - 768) // (4 + 16 * 2 * 4 + 16 * D * 4)
+    # 16 or 32 rows of (max, sum) and D sums per item) are back at zero; a
+    # lower bound on the number of items keeps the check inside the counters
+    items = (need - 768) // (4 + 32 * 2 * 4 + 32 * D * 4)
     assert items > 0 and int(ws.view(torch.int32)[:items].count_nonzero()) == 0
     with pytest.raises(PagedAttnError):
         pa.pa_prefill(torch.empty_like(c.q), c.q, w.k_pool, w.v_pool, w.block_tables().to(DEV),
                       w.context_lens().to(DEV), torch.from_numpy(c.qs).to(DEV), w.scale, w.block_size,
                       partition_size=64, workspace=ws[:256])
+
+
+@pytest.mark.parametrize("scale", [-0.15, 0.0, 0.4])
+def test_negative_zero_and_large_scales(scale):
+    """A negative scale (handled by flipping the query's signs), zero (every
+    visible key weighs the same) and a scale that makes scores span a wide
+    range (the deferred rescaling of the running sums must still settle)."""
+    announce(f"prefill scale={scale}")
+    c = Case([200, 70, 1], [50, 70, 1], 16, 4, 128, 16, torch.float16, 87)
+    assert_close(c.run(scale=scale), c.oracle(scale=scale), torch.float16, f"scale={scale}")
