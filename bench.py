@@ -425,7 +425,8 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
     mfma_bound = op == "prefill"
     digest = kernel_source_digest(PF_SOURCES)
     tag = op + (f"_h{H}" if heads else "") + (f"_p{partition}" if partition else "")
-    traffic = traffic_from_profile(digest, os.path.join(PROFILES, f"prefill_kernel_{tag}_traffic.txt"))
+    kernel = "mla_split_kernel" if mla else "prefill_kernel"
+    traffic = traffic_from_profile(digest, os.path.join(PROFILES, f"{kernel}_{tag}_traffic.txt"))
     metric = {"prefill": "chunked prefill over the paged cache (pa_prefill): achieved TFLOP/s, 1 MI355X",
               "verify": "speculative verification over the paged cache (pa_prefill): achieved HBM GB/s, 1 MI355X",
               "verify1": "one-token queries through pa_prefill: achieved HBM GB/s, 1 MI355X",
@@ -447,12 +448,12 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
         "us_per_step": round(ms * 1e3, 3),
         "flops_per_step": flops, "bytes_per_step": bytes_,
         "achieved": {"TFLOP/s": round(tflops, 2), "GB/s": round(gbs, 2)},
-        "roofline": ({"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tflops, 2),
+        "roofline": ({"bound": "mfma", "kernel": kernel, "achieved": round(tflops, 2),
                       "peak": PEAK_MFMA_16BIT_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(tflops / PEAK_MFMA_16BIT_TFLOPS, 4), "traffic": traffic,
                       "kernel_source_sha": digest}
                      if mfma_bound else
-                     {"bound": "hbm", "kernel": "prefill_kernel", "achieved": round(gbs, 2),
+                     {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 2),
                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                       "traffic": traffic, "kernel_source_sha": digest}),
     }

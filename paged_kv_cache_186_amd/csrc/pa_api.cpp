@@ -199,10 +199,11 @@ struct PrefillPlan {
 constexpr long long kPfTargetItems = 2048;  // ~2 waves per SIMD of a 256-CU GPU
 // Default partition when contexts are split (measured on 64 sequences of
 // log-normal lengths, 4 query tokens, 8 K/V heads: 256 keys 86 us, 512 keys
-// 90 us, 1024 keys 70 us, 2048 keys 101 us; the latent cache, whose items
-// take 16 keys per step, did best at 512)
+// 90 us, 1024 keys 70 us, 2048 keys 101 us; the latent kernel on 32
+// sequences of 1024..8192 tokens, 16 heads: 512 keys 150 us, 768 keys 96 us,
+// 1024 keys 102 us, 2048 keys 156 us)
 constexpr int kPfPartTokens = 1024;
-constexpr int kPfPartTokensLatent = 512;
+constexpr int kPfPartTokensLatent = 768;
 constexpr int kPfMaxDefaultParts = 64;     // ... but no row merges more partials than this
 
 // 16-row tiles per wave: two when the sequences have at least 32 query rows
@@ -223,11 +224,12 @@ int prefill_row_tiles(int32_t num_seqs, int32_t num_query_rows, int32_t num_head
 // tile groups of a call are at most ceil(T*G/(16*row_tiles)) + S (a
 // sequence's partial group adds at most one), partitions at most
 // ceil(W*BS / part_tokens).  partition_size 0 splits the context only when
-// the unsplit items would not fill the GPU, into partitions of 1024 keys (512
+// the unsplit items would not fill the GPU, into partitions of 1024 keys (768
 // for the latent cache; fewer, larger ones beyond 64 partitions).
 PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_query_rows, int32_t num_heads,
                          int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t block_size,
-                         int32_t partition_size, int32_t v_per_item, int32_t slices, int32_t row_tiles) {
+                         int32_t partition_size, int32_t v_per_item, int32_t slices, int32_t row_tiles,
+                         bool wg_items = false) {
   PrefillPlan p{PA_OK, 0, 0, 0, {0, 0, 0, 0}};
   if (num_seqs < 0 || num_query_rows < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
       num_heads % num_kv_heads != 0 || max_blocks_per_seq <= 0 ||
@@ -240,12 +242,14 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_query_rows, int32_t num_h
   const long long group_rows = 16LL * row_tiles;
   const long long tiles = (static_cast<long long>(num_query_rows) * group + group_rows - 1) / group_rows + num_seqs;
   const long long base = tiles * num_kv_heads * slices;
+  // an item of the latent kernel is a whole workgroup: a quarter as many fill the GPU
+  const long long target = wg_items ? kPfTargetItems / 4 : kPfTargetItems;
   if (partition_size == 0) {
-    if (base >= kPfTargetItems) {
+    if (base >= target) {
       p.part_tokens = static_cast<int>((ctx + 31) / 32 * 32);  // one partition
     } else {
       const long long spread = (ctx + kPfMaxDefaultParts - 1) / kPfMaxDefaultParts;
-      const long long dflt = slices > 1 ? kPfPartTokensLatent : kPfPartTokens;
+      const long long dflt = wg_items ? kPfPartTokensLatent : kPfPartTokens;
       const long long per = spread > dflt ? spread : dflt;
       p.part_tokens = static_cast<int>((per + 31) / 32 * 32);
     }
@@ -263,7 +267,7 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_query_rows, int32_t num_h
     return p;
   }
   // a multiple of 8 workgroups: the kernel gives each XCD an equal share
-  const long long wg = ((p.max_items + 3) / 4 + 7) / 8 * 8;
+  const long long wg = ((wg_items ? p.max_items : (p.max_items + 3) / 4) + 7) / 8 * 8;
   p.workgroups = static_cast<int>(wg < 8 ? 8 : (wg > pa::kPfMaxWorkgroups ? pa::kPfMaxWorkgroups : wg));
   if (max_parts > 1)
     p.ws = pa::workspace_layout(static_cast<size_t>(p.max_items),
@@ -282,13 +286,12 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const voi
                          int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
                          bool latent, void* workspace, size_t workspace_bytes, void* stream) {
   if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
-  const int v_per_item = latent ? pa::kMlaVSlice : head_dim;
-  const int slices = latent ? pa::kMlaVDim / pa::kMlaVSlice : 1;
+  const int v_per_item = latent ? pa::kMlaVDim : head_dim;
   if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   const int row_tiles = prefill_row_tiles(num_seqs, num_query_rows, num_heads, num_kv_heads, latent);
   const PrefillPlan plan = plan_prefill(num_seqs, num_query_rows, num_heads, num_kv_heads,
                                         max_blocks_per_seq, block_size, partition_size,
-                                        v_per_item, slices, row_tiles);
+                                        v_per_item, 1, row_tiles, latent);
   if (plan.status != PA_OK) return plan.status;
   if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0 || num_query_rows == 0) return PA_OK;
@@ -337,7 +340,9 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const voi
               static_cast<size_t>(s0) * num_heads * (latent ? pa::kMlaVDim : head_dim) * 2;
       a.num_query_rows = a.num_seqs;
     }
-    if (pa::launch_prefill(a, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_HIP;
+    const hipError_t e = latent ? pa::launch_mla_split(a, static_cast<hipStream_t>(stream))
+                                : pa::launch_prefill(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;
 }
@@ -607,7 +612,7 @@ size_t pa_decode_mla_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t
                                     int32_t block_size, int32_t partition_size) {
   if (block_size != 16 && block_size != 32) return 0;
   const PrefillPlan p = plan_prefill(num_seqs, num_seqs, num_heads, 1, max_blocks_per_seq, block_size,
-                                     partition_size, pa::kMlaVSlice, pa::kMlaVDim / pa::kMlaVSlice, 1);
+                                     partition_size, pa::kMlaVDim, 1, 1, true);
   return p.status == PA_OK ? p.ws.total : 0;
 }
 

@@ -141,7 +141,6 @@ constexpr int kPfMaxSeqs = 2048;
 constexpr int kPfMaxWorkgroups = 1024;
 constexpr int kMlaQkDim = 576;  // latent 512 + rotary 64 (DeepSeek-V2/V3)
 constexpr int kMlaVDim = 512;
-constexpr int kMlaVSlice = 256;  // value elements per work item (two items per row tile)
 
 struct PrefillArgs {
   void* out;                    // [T][H][DV]
@@ -162,9 +161,12 @@ struct PrefillArgs {
   int workgroups;
   uint32_t* counters;  // [max_items] (null when no row can be split)
   float* ws_ml;        // [max_items][16 * row_tiles][2]
-  float* ws_acc;       // [max_items][16 * row_tiles][value elements per item: DV, or kMlaVSlice]
+  float* ws_acc;       // [max_items][16 * row_tiles][DV]
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// the latent cache: one workgroup per (sequence, 16 heads, partition), the
+// 576 elements of a row split across its four waves
+hipError_t launch_mla_split(const PrefillArgs& a, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                                     const int32_t* slot_mapping, int num_tokens, int num_heads,

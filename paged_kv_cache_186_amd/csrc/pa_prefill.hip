@@ -619,11 +619,398 @@ hipError_t run_prefill_nt(const PrefillArgs& a, hipStream_t stream) {
 
 template <typename T>
 hipError_t run_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-  if (a.latent) return run_prefill_bs<T, kMlaQkDim, kMlaVDim, kMlaVSlice, kMlaQkDim, 1, 1>(a, stream);
+  if (a.latent) return hipErrorInvalidValue;  // the latent cache has its own kernel (mla_split_kernel)
   return a.head_dim == 64 ? run_prefill_nt<T, 64>(a, stream) : run_prefill_nt<T, 128>(a, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Decode over the latent (MLA) cache with the head dimension split across the
+// four waves of a workgroup.  A latent row is 576 elements: wave w owns latent
+// elements [128w, 128w + 128) — its share of the scores and its 128-element
+// slice of the values — and waves 0 and 1 also one 32-element half of the
+// 64-element rotary part.  Per 32-key step each wave loads only its slice of
+// the key rows (so the workgroup reads every latent row once), computes the
+// partial scores S^T over its elements with the 16x16x32 products, and the
+// four partials are summed through LDS (double-buffered: one barrier per
+// step); every wave then runs the same softmax on the full scores and
+// accumulates O^T += V^T P^T for its own value slice (whose rows it loads in
+// the transposed-operand layout; the lines are the ones it just read for its
+// scores).  A work item is (sequence, context partition, 16 heads).
+constexpr int kMlaWaves = 4;
+constexpr int kMlaOwn = kMlaVDim / kMlaWaves;  // latent elements per wave (128)
+
+template <typename T, int BS>
+__global__ __launch_bounds__(kMlaWaves* kWave, 2) void mla_split_kernel(
+    typename T::storage* __restrict__ out, const typename T::storage* __restrict__ q,
+    const char* __restrict__ kv_pool, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, uint32_t* __restrict__ counters, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc, float qk_scale, int num_seqs, int num_heads, int num_blocks, int max_blocks,
+    int part_tokens, int max_items, uint32_t q_sign_bits) {
+  using S16 = typename T::storage;
+  using M = Mfma<T>;
+  using PV = PvOps<T, 2>;
+  using pw_t = typename PV::word_t;
+  constexpr int kThreads = kMlaWaves * kWave;
+  constexpr int kPer = (kPfMaxSeqs + kThreads - 1) / kThreads;
+  constexpr int kJ = 5;       // 32-element score slices a wave may own (4 latent + 1 rotary)
+  constexpr int kDq = kMlaOwn / 64;
+  constexpr int kRowB = kMlaQkDim * 2;
+  __shared__ int s_off[kPfMaxSeqs + 1];
+  __shared__ int s_len[kPfMaxSeqs];
+  __shared__ int s_wsum[kMlaWaves];
+  __shared__ uint32_t s_ticket;
+  __shared__ f4_t s_sc[2][kMlaWaves][2][kWave];  // partial scores of the last two steps
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int S = num_seqs;
+  const int cap = max_blocks * BS;
+  const int tiles = (num_heads + kPfRows - 1) / kPfRows;
+
+  // 1. lengths and the prefix sum of items (tiles x partitions) per sequence
+  for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);
+  __syncthreads();
+  int cnt[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    cnt[i] = s < S ? tiles * max(1, (s_len[s] + part_tokens - 1) / part_tokens) : 0;
+    mine += cnt[i];
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kMlaWaves; ++w) {
+    const int v = s_wsum[w];
+    before += (w < wave) ? v : 0;
+    total += v;
+  }
+  int run = before + incl - mine;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    if (s < S) s_off[s] = run;
+    run += cnt[i];
+  }
+  if (tid == 0) s_off[S] = total;
+  __syncthreads();
+  total = min(__builtin_amdgcn_readfirstlane(total), max_items);
+
+  const u32x4 q_sign = {q_sign_bits, q_sign_bits, q_sign_bits, q_sign_bits};
+  const int col = lane % 16;
+  const int g4 = lane / 16;
+  const int nj = wave < 2 ? 5 : 4;  // waves 0 and 1 also take a rotary half
+  // element offset of score slice j of this wave
+  auto dim_of = [&](int j) __attribute__((always_inline)) {
+    return j < 4 ? kMlaOwn * wave + 32 * j : kMlaVDim + 32 * wave;
+  };
+  const int own0 = kMlaOwn * wave;  // first value element of this wave
+
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int x_end = min(total, (xcd + 1) * per_xcd);
+  const int x_step = gridDim.x / kXcds;
+  int parity = 0;
+  for (int item = xcd * per_xcd + blockIdx.x / kXcds; item < x_end; item += x_step) {
+    int lo = 0;
+    int hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= item)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(lo);
+    const int L = __builtin_amdgcn_readfirstlane(s_len[s]);
+    const int parts = max(1, (L + part_tokens - 1) / part_tokens);
+    // head tiles fastest: the tiles of one partition read the same latent
+    // rows, in adjacent workgroups of one XCD, so all but the first read hit L2
+    const int local = item - __builtin_amdgcn_readfirstlane(s_off[s]);
+    const int tile = local % tiles;
+    const int part = local / tiles;
+    const int h = tile * kPfRows + col;
+    const bool row_ok = h < num_heads;
+    const int k_begin = part * part_tokens;
+    const int k_end = min(k_begin + part_tokens, L);
+
+    u32x4 qv[kJ];
+    {
+      const S16* qrow = q + (static_cast<size_t>(s) * num_heads + (row_ok ? h : 0)) * kMlaQkDim + 8 * g4;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const u32x4 v = (j < nj) ? (load16(qrow + dim_of(j)) ^ q_sign) : u32x4{0u, 0u, 0u, 0u};
+        qv[j] = row_ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    float m = -INFINITY, lsum = 0.f;
+    f4_t acc[kDq][4];
+#pragma unroll
+    for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[dq][e] = f4_t{0.f, 0.f, 0.f, 0.f};
+    int bad = 0;
+
+    struct Stage {
+      u32x4 k[2][kJ];
+      u32x2 v[2][kDq][4];
+      int c, bad;
+    };
+    const int32_t* tbl = block_tables + static_cast<size_t>(s) * max_blocks;
+    auto load_step = [&](Stage& st, int c) __attribute__((always_inline)) {
+      st.c = c;
+      st.bad = 0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key0 = (c + 16 * kb < k_end) ? c + 16 * kb : c;
+        int phys = tbl[key0 / BS];
+        if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
+          st.bad = 1;
+          phys = 0;
+        }
+        const char* rows = kv_pool + (static_cast<size_t>(phys) * BS + key0 % BS) * kRowB;
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+          st.k[kb][j] = (j < nj) ? load16(rows + col * kRowB + (dim_of(j) + 8 * g4) * 2) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st.v[kb][dq][e] =
+                *reinterpret_cast<const u32x2*>(rows + (4 * g4 + e) * kRowB + (own0 + 64 * dq + 4 * col) * 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto attend_step = [&](Stage& st) __attribute__((always_inline)) {
+      bad |= st.bad;
+      if (st.c + 32 > L) {  // value rows past the context may hold anything: zero
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (st.c + 16 * kb + 4 * g4 + e >= L)
+#pragma unroll
+              for (int dq = 0; dq < kDq; ++dq) st.v[kb][dq][e] = u32x2{0u, 0u};
+      }
+      // partial scores over this wave's elements, summed across the waves
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kJ; ++j)
+          if (j < nj) sc = M::qk(st.k[kb][j], qv[j], sc);
+        s_sc[parity][wave][kb][lane] = sc;
+      }
+      __syncthreads();
+      float z[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f4_t t = s_sc[parity][0][kb][lane];
+#pragma unroll
+        for (int w = 1; w < kMlaWaves; ++w) t += s_sc[parity][w][kb][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[kb][i] = t[i];
+      }
+      parity ^= 1;
+      const bool masked = st.c + 32 > k_end;
+      if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            z[kb][i] = (st.c + 16 * kb + 4 * g4 + i < k_end) ? z[kb][i] : -INFINITY;
+      }
+      float cm = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      const float cms = (cm == -INFINITY) ? -INFINITY : cm * qk_scale;
+      const float mn = fmaxf(m, cms);
+      if (__builtin_amdgcn_ballot_w64(mn > m + kRescaleLog2) != 0) {
+        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[dq][e] *= alpha;
+        m = mn;
+      }
+      const float nm = -m;
+      float p[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
+          p[kb][i] = (masked && z[kb][i] == -INFINITY) ? 0.f : x;
+          lsum += p[kb][i];
+        }
+      const pw_t pw = {M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3]), M::pack2(p[1][0], p[1][1]),
+                       M::pack2(p[1][2], p[1][3])};
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const pw_t a = {col_pair(st.v[0][dq][0], st.v[0][dq][1], e), col_pair(st.v[0][dq][2], st.v[0][dq][3], e),
+                          col_pair(st.v[1][dq][0], st.v[1][dq][1], e), col_pair(st.v[1][dq][2], st.v[1][dq][3], e)};
+          acc[dq][e] = PV::mma(a, pw, acc[dq][e]);
+        }
+    };
+
+    const int n_steps = k_end > k_begin ? (k_end - k_begin + 31) / 32 : 0;
+    if (n_steps > 0) {
+      Stage a, b;
+      load_step(a, k_begin);
+      int c = 0;
+      for (; c + 2 < n_steps; c += 2) {
+        load_step(b, k_begin + (c + 1) * 32);
+        attend_step(a);
+        load_step(a, k_begin + (c + 2) * 32);
+        attend_step(b);
+      }
+      if (c + 1 < n_steps) {
+        load_step(b, k_begin + (c + 1) * 32);
+        attend_step(a);
+        attend_step(b);
+      } else {
+        attend_step(a);
+      }
+    }
+    float lrow = lsum + __shfl_xor(lsum, 16);
+    lrow += __shfl_xor(lrow, 32);
+    if (bad) lrow = __builtin_nanf("");
+
+    auto write_row = [&](const float (&o)[kDq][16]) __attribute__((always_inline)) {
+      S16* orow = out + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + own0 + 16 * g4;
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq) {
+        uint32_t w[8];
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) w[k2] = M::pack2(o[dq][2 * k2], o[dq][2 * k2 + 1]);
+        store16(orow + 64 * dq, u32x4{w[0], w[1], w[2], w[3]});
+        store16(orow + 64 * dq + 8, u32x4{w[4], w[5], w[6], w[7]});
+      }
+    };
+    if (parts == 1) {
+      if (row_ok) {
+        float o[kDq][16];
+        const float inv = (lrow == 0.f) ? 0.f : 1.f / lrow;
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[dq][4 * i + e] = acc[dq][e][i] * inv;
+        write_row(o);
+      }
+      continue;
+    }
+    // partial of a split item: slot `item`, 16 rows x (max, sum) and 512 sums
+    {
+      const size_t row = static_cast<size_t>(item) * kPfRows + col;
+      if (wave == 0 && g4 == 0) store_coherent_u64(ws_ml + row * 2, m, lrow);
+      float* av = ws_acc + row * kMlaVDim + own0 + 16 * g4;
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          store_coherent_u64(av + 64 * dq + 4 * i, acc[dq][0][i], acc[dq][1][i]);
+          store_coherent_u64(av + 64 * dq + 4 * i + 2, acc[dq][2][i], acc[dq][3][i]);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int item0 = item - part * tiles;  // this tile's partition-0 item; its partitions are tiles apart
+    if (tid == 0)
+      s_ticket = __hip_atomic_fetch_add(&counters[item0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_ticket != static_cast<uint32_t>(parts - 1)) continue;
+    // last arrival: each wave merges its value slice of the 16 rows
+    float Mx = -INFINITY, den = 0.f;
+    float num[kDq][16];
+#pragma unroll
+    for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+      for (int k2 = 0; k2 < 16; ++k2) num[dq][k2] = 0.f;
+    constexpr int kB = 4;
+    for (int p0 = 0; p0 < parts; p0 += kB) {
+      uint64_t pml[kB];
+      uint64_t pvv[kB][kDq][8];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const size_t row = (static_cast<size_t>(item0) + static_cast<size_t>(min(p0 + u, parts - 1)) * tiles) *
+                               kPfRows + col;
+        pml[u] = load_coherent_u64(ws_ml + row * 2);
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int k2 = 0; k2 < 8; ++k2)
+            pvv[u][dq][k2] = load_coherent_u64(ws_acc + row * kMlaVDim + own0 + 64 * dq + 16 * g4 + 2 * k2);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (p0 + u >= parts) break;
+        const float mu = lo_float(pml[u]);
+        if (mu == -INFINITY) continue;
+        const float mn = fmaxf(Mx, mu);
+        const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
+        const float b = fast_exp2(mu - mn);
+        den = den * a + hi_float(pml[u]) * b;
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int k2 = 0; k2 < 8; ++k2) {
+            num[dq][2 * k2] = num[dq][2 * k2] * a + lo_float(pvv[u][dq][k2]) * b;
+            num[dq][2 * k2 + 1] = num[dq][2 * k2 + 1] * a + hi_float(pvv[u][dq][k2]) * b;
+          }
+        Mx = mn;
+      }
+    }
+    if (row_ok) {
+      float o[kDq][16];
+      const float inv = (den == 0.f) ? 0.f : 1.f / den;
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int k2 = 0; k2 < 16; ++k2) o[dq][k2] = num[dq][k2] * inv;
+      write_row(o);
+    }
+    if (tid == 0) __hip_atomic_store(&counters[item0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <typename T, int BS>
+hipError_t run_mla(const PrefillArgs& a, hipStream_t stream) {
+  using S16 = typename T::storage;
+  hipLaunchKernelGGL((mla_split_kernel<T, BS>), dim3(a.workgroups), dim3(kMlaWaves * kWave), 0, stream,
+                     static_cast<S16*>(a.out), static_cast<const S16*>(a.q), static_cast<const char*>(a.k_pool),
+                     a.block_tables, a.context_lens, a.counters, a.ws_ml, a.ws_acc, fabsf(a.scale) * kLog2e,
+                     a.num_seqs, a.num_heads, a.num_blocks, a.max_blocks_per_seq, a.part_tokens, a.max_items,
+                     a.scale < 0.f ? 0x80008000u : 0u);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_mla_t(const PrefillArgs& a, hipStream_t stream) {
+  return a.block_size == 16 ? run_mla<T, 16>(a, stream) : run_mla<T, 32>(a, stream);
+}
+
 }  // namespace
+
+hipError_t launch_mla_split(const PrefillArgs& a, hipStream_t stream) {
+  return a.dtype == PA_DTYPE_BF16 ? run_mla_t<BF16>(a, stream) : run_mla_t<F16>(a, stream);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   return a.dtype == PA_DTYPE_BF16 ? run_prefill_t<BF16>(a, stream) : run_prefill_t<F16>(a, stream);
