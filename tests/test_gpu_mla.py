@@ -90,3 +90,14 @@ def test_out_of_pool_table_id_poisons_only_its_sequence():
     assert torch.isnan(out[1]).all()
     ref = c.oracle()
     assert_close(out[[0, 2]], ref[[0, 2]], torch.float16, "other sequences")
+
+
+def test_more_sequences_than_one_launch_holds():
+    """2100 sequences: the library launches once per 2048 (the per-sequence
+    offsets live in LDS); the second launch must pick up q, out and the
+    tables at the right sequence."""
+    announce("mla 2100 sequences")
+    rng = np.random.default_rng(98)
+    lens = rng.integers(0, 40, size=2100).tolist()
+    c = LatentCase(lens, 16, 16, torch.bfloat16, 98)
+    assert_close(c.run(), c.oracle(), torch.bfloat16, "2100 sequences")

@@ -182,3 +182,14 @@ def test_negative_zero_and_large_scales(scale):
     announce(f"prefill scale={scale}")
     c = Case([200, 70, 1], [50, 70, 1], 16, 4, 128, 16, torch.float16, 87)
     assert_close(c.run(scale=scale), c.oracle(scale=scale), torch.float16, f"scale={scale}")
+
+
+def test_more_sequences_than_one_launch_holds():
+    """2100 sequences with 1 or 2 query tokens: two launches, the second
+    addressing q and out through the absolute query_start values."""
+    announce("prefill 2100 sequences")
+    rng = np.random.default_rng(88)
+    lens = rng.integers(2, 30, size=2100).tolist()
+    tq = rng.integers(1, 3, size=2100).tolist()
+    c = Case(lens, tq, 8, 4, 64, 16, torch.float16, 88)
+    assert_close(c.run(), c.oracle(), torch.float16, "2100 sequences")
