@@ -75,6 +75,7 @@ struct Mfma<F16> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a), __builtin_bit_cast(h4_t, b), c,
                                                  0, 0, 0);
   }
+  static constexpr uint32_t kOnes = 0x3C003C00u;  // two f16 1.0
   // two fp32 values -> one word of two f16 (round to nearest even)
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(lo))) |
@@ -92,6 +93,7 @@ struct Mfma<BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a), __builtin_bit_cast(s4_t, b), c,
                                                      0, 0, 0);
   }
+  static constexpr uint32_t kOnes = 0x3F803F80u;  // two bf16 1.0
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return static_cast<uint32_t>(BF16::pack(lo)) | (static_cast<uint32_t>(BF16::pack(hi)) << 16);
   }
@@ -318,13 +320,14 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
       }
     }
 
-    float m[NT];     // running max of row `col` of tile t (same in its 4 lanes)
-    float lsum[NT];  // this lane's share of that row's running sum
+    float m[NT];      // running max of row `col` of tile t (same in its 4 lanes)
+    f4_t lacc[NT];    // running row sums: the P.V product with every value 1
+                      // (each of the 4 elements holds row col's sum)
     f4_t acc[NT][kDq][4];  // O^T products: [tile][slice][column label e]
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       m[t] = -INFINITY;
-      lsum[t] = 0.f;
+      lacc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dq = 0; dq < kDq; ++dq)
 #pragma unroll
@@ -354,18 +357,21 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
           st.bad = 1;  // never dereference an id outside the pool
           phys = 0;
         }
+        // wave-uniform 64-bit row base + a 32-bit lane offset + constant
+        // offsets per load: scalar-base addressing, no 64-bit lane arithmetic
         const size_t row0 = (static_cast<size_t>(phys) * HKV + hk) * BS + (key0 % BS);
-        const char* kb_ptr = k_pool + ((row0 + col) * DQK + 8 * g4) * sizeof(S16);
+        const char* kb_ptr = k_pool + row0 * (DQK * sizeof(S16)) +
+                             static_cast<uint32_t>((col * DQK + 8 * g4) * sizeof(S16));
 #pragma unroll
         for (int j = 0; j < kQK; ++j) st.k[kb][j] = load16(kb_ptr + 32 * j * sizeof(S16));
+        const char* vb_ptr = v_pool + row0 * (KV_STRIDE * sizeof(S16)) +
+                             static_cast<uint32_t>((4 * g4 * KV_STRIDE + v_off + 4 * col) * sizeof(S16));
 #pragma unroll
         for (int dq = 0; dq < kDq; ++dq)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const char* vb =
-                v_pool + ((row0 + 4 * g4 + e) * KV_STRIDE + v_off + 64 * dq + 4 * col) * sizeof(S16);
-            st.v[kb][dq][e] = *reinterpret_cast<const u32x2*>(vb);
-          }
+          for (int e = 0; e < 4; ++e)
+            st.v[kb][dq][e] =
+                *reinterpret_cast<const u32x2*>(vb_ptr + (e * KV_STRIDE + 64 * dq) * sizeof(S16));
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -382,18 +388,27 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
               for (int dq = 0; dq < kDq; ++dq) st.v[kb][dq][e] = u32x2{0u, 0u};
       }
       const bool masked = (st.c + kChunk - 1 > pos_min) || (st.c + kChunk > k_end);
-      pw_t pw[NT];
+      // raw scores <q, k> of every tile first (the softmax scale is folded
+      // into the exponent): the matrix unit then works on the later tiles'
+      // products while the vector unit runs the first tile's softmax
+      f4_t scs[NT][KB];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        // raw scores <q, k> (the softmax scale is folded into the exponent)
-        float z[KB][4];
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int t = 0; t < NT; ++t) {
           f4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int j = 0; j < kQK; ++j) sc = M::qk(st.k[kb][j], qv[t][j], sc);
+          scs[t][kb] = sc;
+        }
+      pw_t pw[NT];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) z[kb][i] = sc[i];
+      for (int t = 0; t < NT; ++t) {
+        float z[KB][4];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[kb][i] = scs[t][kb][i];
           if (masked) {
             const int key0 = st.c + 16 * kb + 4 * g4;  // key of z[kb][0]
 #pragma unroll
@@ -409,25 +424,28 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
         const float mn = fmaxf(m[t], cms);
         if (__builtin_amdgcn_ballot_w64(mn > m[t] + kRescaleLog2) != 0) {
           const float alpha = (m[t] == -INFINITY) ? 0.f : fast_exp2(m[t] - mn);
-          lsum[t] *= alpha;
+          lacc[t] *= alpha;
 #pragma unroll
           for (int dq = 0; dq < kDq; ++dq)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[t][dq][e] *= alpha;
           m[t] = mn;
         }
-        // p = 2^(scale*log2e*z - m); in a fully visible chunk every row has a
-        // finite reference by now, so no masked term needs a guard there
+        // p = 2^(scale*log2e*z - m); masked scores (-inf) are set to 0
+        // explicitly, in the steps that have any (a zero scale would make
+        // -inf * scale a NaN)
         const float nm = -m[t];
         float p[KB][4];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
-            p[kb][i] = (masked && z[kb][i] == -INFINITY) ? 0.f : x;
-            lsum[t] += p[kb][i];
-          }
+          for (int i = 0; i < 4; ++i) p[kb][i] = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
+        if (masked) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[kb][i] = (z[kb][i] == -INFINITY) ? 0.f : p[kb][i];
+        }
         if constexpr (KB == 1) {
           pw[t] = pw_t{M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3])};
         } else {
@@ -450,6 +468,12 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
 #pragma unroll
           for (int t = 0; t < NT; ++t) acc[t][dq][e] = PV::mma(a, pw[t], acc[t][dq][e]);
         }
+      // row sums of the rounded probabilities the products used
+      pw_t ones;
+#pragma unroll
+      for (int w = 0; w < static_cast<int>(sizeof(pw_t) / 4); ++w) ones[w] = M::kOnes;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) lacc[t] = PV::mma(ones, pw[t], lacc[t]);
     };
 
     // 3. the chunks of the item, two in flight
@@ -488,11 +512,7 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
 
     float lrow[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      lrow[t] = lsum[t] + __shfl_xor(lsum[t], 16);
-      lrow[t] += __shfl_xor(lrow[t], 32);
-      if (bad) lrow[t] = __builtin_nanf("");
-    }
+    for (int t = 0; t < NT; ++t) lrow[t] = bad ? __builtin_nanf("") : lacc[t][0];
 
     if (parts == 1) {
 #pragma unroll
