@@ -211,9 +211,6 @@ constexpr int kPfMaxDefaultParts = 64;     // ... but no row merges more partial
 // else one.  The latent cache always takes one (register budget).
 int prefill_row_tiles(int32_t num_seqs, int32_t num_query_rows, int32_t num_heads, int32_t num_kv_heads,
                       bool latent) {
-#ifdef PA_PF_FORCE_ROW_TILES
-  if (!latent) return PA_PF_FORCE_ROW_TILES;
-#endif
   if (latent || num_seqs <= 0) return 1;
   const long long rows = static_cast<long long>(num_query_rows) * (num_heads / num_kv_heads);
   return rows >= 32LL * num_seqs ? 2 : 1;
