@@ -145,19 +145,57 @@ __device__ __forceinline__ void attend_tile_heads(const u32x4 (&kv)[Tile<T, D, B
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i) p[g][i] = ok[i] ? fast_exp2(sc[g][i] - m[g]) : 0.f;
   }
+  if constexpr (__is_same(T, F16) && C::kLoads % 2 == 0) {
+    // fp16 cache: the weighted sums by packed dot products over PAIRS of
+    // rows — loads i and i+1 hold rows 4 apart in the same lanes, so byte
+    // permutes turn their words into (row i, row i+1) pairs per element, and
+    // each head's two weights are rounded to fp16 (relative error <= 2^-11)
+    // into one word: half the multiply-adds of the per-row form.  The row
+    // sums take the same rounded weights (a dot product with (1, 1)).  A
+    // bf16 cache keeps the fp32 weights (bf16 would round them to 2^-8).
 #pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    float vf[T::kElems];
-    T::unpack(vv[i], vf);
+    for (int i = 0; i < C::kLoads; i += 2) {
+      uint32_t a[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+      uint32_t b[4] = {vv[i + 1].x, vv[i + 1].y, vv[i + 1].z, vv[i + 1].w};
+      if constexpr (kMasked) {
 #pragma unroll
-    for (int e = 0; e < T::kElems; ++e) vf[e] = ok[i] ? vf[e] : 0.f;
+        for (int w = 0; w < 4; ++w) {
+          a[w] = ok[i] ? a[w] : 0u;
+          b[w] = ok[i + 1] ? b[w] : 0u;
+        }
+      }
+      uint32_t lo[4], hi[4];
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      l[g] += p[g][i];
-      float pv = p[g][i];
-      if constexpr (T::kScaled) pv *= sv;
+      for (int w = 0; w < 4; ++w) {
+        lo[w] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);  // element 2w of both rows
+        hi[w] = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);  // element 2w + 1
+      }
 #pragma unroll
-      for (int e = 0; e < T::kElems; ++e) acc[g][e] = fmaf(pv, vf[e], acc[g][e]);
+      for (int g = 0; g < GW; ++g) {
+        const uint32_t pp = T::pack_pair(p[g][i], p[g][i + 1]);
+        l[g] = T::dot2(pp, T::kOnePair, l[g]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc[g][2 * w] = T::dot2(pp, lo[w], acc[g][2 * w]);
+          acc[g][2 * w + 1] = T::dot2(pp, hi[w], acc[g][2 * w + 1]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+      float vf[T::kElems];
+      T::unpack(vv[i], vf);
+#pragma unroll
+      for (int e = 0; e < T::kElems; ++e) vf[e] = ok[i] ? vf[e] : 0.f;
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        l[g] += p[g][i];
+        float pv = p[g][i];
+        if constexpr (T::kScaled) pv *= sv;
+#pragma unroll
+        for (int e = 0; e < T::kElems; ++e) acc[g][e] = fmaf(pv, vf[e], acc[g][e]);
+      }
     }
   }
 }

@@ -49,6 +49,7 @@ struct F16 {
   static constexpr int kElems = 8;
   static constexpr bool kScaled = false;
   static constexpr bool kDot2 = true;
+  static constexpr uint32_t kOnePair = 0x3C003C00u;  // (1.0, 1.0)
   static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
   }
@@ -65,6 +66,11 @@ struct F16 {
   }
   // v_cvt_f16_f32 rounds to nearest even in the default rounding mode.
   static __device__ __forceinline__ storage pack(float x) { return static_cast<_Float16>(x); }
+  // two fp32 values -> one word of two (round to nearest even)
+  static __device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, pack(lo))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, pack(hi))) << 16);
+  }
 };
 
 struct BF16 {
@@ -72,6 +78,7 @@ struct BF16 {
   static constexpr int kElems = 8;
   static constexpr bool kScaled = false;
   static constexpr bool kDot2 = true;
+  static constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0)
   static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
                                            false);
@@ -92,6 +99,9 @@ struct BF16 {
     if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return static_cast<uint16_t>(u >> 16);
+  }
+  static __device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+    return static_cast<uint32_t>(pack(lo)) | (static_cast<uint32_t>(pack(hi)) << 16);
   }
 };
 
