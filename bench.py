@@ -321,23 +321,7 @@ def swap_bench(pa, dev, steps: int, warmup: int) -> dict:
 
 PEAK_MFMA_16BIT_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak (published)
 
-# multi-token query workloads (pa_prefill) and the latent cache (pa_decode_mla)
-QUERY_OPS = {
-    # a prompt chunk per sequence: 4 sequences whose last 1024 of 4096 tokens
-    # are new (chunked prefill), 32 query / 8 K/V heads, D=128, BS=16, fp16
-    "prefill": dict(S=4, lens="4096", tq=1024, H=32, Hkv=8, D=128, bs=16, dtype=torch.float16),
-    # speculative verification: 64 sequences with lengths as in continuous
-    # batching (log-normal, median 512, clipped to [32, 4096]), 4 drafted
-    # tokens each, 32 query / 8 K/V heads, D=128, BS=32, fp16
-    "verify": dict(S=64, lens="lognormal", tq=4, H=32, Hkv=8, D=128, bs=32, dtype=torch.float16),
-    # the same batch with one query token each: grouped-query decode through
-    # the matrix-core kernel (compare pa_decode_gqa on continuous batching)
-    "verify1": dict(S=64, lens="lognormal", tq=1, H=32, Hkv=8, D=128, bs=32, dtype=torch.float16),
-    # MLA decode: 32 sequences, lengths uniform in [1024, 8192], 16 heads (a
-    # 128-head model split over 8 GPUs by heads), 576-element latent rows,
-    # BS=32, bf16
-    "mla": dict(S=32, lens="uniform", tq=1, H=16, Hkv=1, D=576, bs=32, dtype=torch.bfloat16),
-}
+from paged_kv_cache_186_amd.workloads import QUERY_OPS  # noqa: E402
 
 
 def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: int, cpu: bool,
@@ -345,40 +329,16 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
     """One call of pa_prefill / pa_decode_mla per step, cold cache (pool
     replicas rotated), HIP-graph replays timed with HIP events."""
     from paged_kv_cache_186_amd import workloads as W
-    cfg = dict(QUERY_OPS[op])
-    if heads:
-        cfg["H"] = heads
-    S, H, Hkv, D, bs, dtype, tq = cfg["S"], cfg["H"], cfg["Hkv"], cfg["D"], cfg["bs"], cfg["dtype"], cfg["tq"]
-    mla = op == "mla"
-    Dv = pa.binding.MLA_V_DIM if mla else D
     calibration_copy(pa, dev)
-    rng = np.random.default_rng(seed)
-    if cfg["lens"] == "4096":
-        lens = np.full(S, 4096, dtype=np.int64)
-    elif cfg["lens"] == "lognormal":
-        lens = np.clip(np.rint(rng.lognormal(math.log(512.0), 1.0, S)), 32, 4096).astype(np.int64)
-    else:
-        lens = rng.integers(1024, 8192, size=S, endpoint=True)
-    nb = int(sum(-(-int(L) // bs) for L in lens)) + 8
-    m = W.BlockManager(nb, bs, free_order=rng.permutation(nb).tolist())
-    for s, L in enumerate(lens):
-        m.allocate(s)
-        m.append_slots(s, int(L))
-    width = int(max(-(-int(L) // bs) for L in lens))
-    tables_np = m.block_tables(list(range(S)), width)
+    qw = W.query_workload(op, seed, dev, heads)
+    S, H, Hkv, D, Dv, bs, dtype, tq = qw.S, qw.H, qw.Hkv, qw.D, qw.Dv, qw.bs, qw.dtype, qw.tq
+    mla = qw.mla
+    lens, tables_np, qs_np, T, width, scale = qw.lens, qw.tables_np, qw.qs_np, qw.T, qw.width, qw.scale
     tables = torch.from_numpy(tables_np).to(dev)
     clens = torch.from_numpy(lens.astype(np.int32)).to(dev)
-    tq_s = np.full(S, tq, dtype=np.int64)
-    qs_np = np.concatenate([[0], np.cumsum(tq_s)]).astype(np.int32)
-    T = int(qs_np[-1])
     qs = torch.from_numpy(qs_np).to(dev)
-    g = torch.Generator(device=dev)
-    g.manual_seed(seed * 1000003 + 29)
-    base = (W.normal((nb, bs, D), dtype, dev, g),) if mla else \
-        (W.normal((nb, Hkv, bs, D), dtype, dev, g), W.normal((nb, Hkv, bs, D), dtype, dev, g))
-    q = W.normal((T, H, D), dtype, dev, g)
+    base, q = qw.pools, qw.q
     out = torch.empty((T, H, Dv), dtype=dtype, device=dev)
-    scale = 1.0 / math.sqrt(192.0 if mla else D)
     pool_bytes = sum(t.numel() * t.element_size() for t in base)
     R = max(1, math.ceil(COLD_BYTES / pool_bytes))
     reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]

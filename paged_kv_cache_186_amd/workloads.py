@@ -26,6 +26,20 @@ contexts from the same two pages):
 * ``long_context``         batch 1 or 4 at 131072 tokens each, 32 heads, D=128,
                            block 16, fp16; 8192 randomly scattered blocks each.
 
+Multi-token and latent-cache workloads (``QUERY_OPS``, built by
+``query_workload``; lengths and blocks from a numpy generator, values from a
+seeded ``torch.Generator``):
+
+* ``prefill``   4 sequences of 4096 tokens whose last 1024 are new (a prompt
+                chunk), 32 query / 8 K/V heads, D=128, block 16, fp16.
+* ``verify``    64 sequences with the ``continuous_batching`` length mix and 4
+                drafted tokens each, 32 query / 8 K/V heads, D=128, block 32,
+                fp16.
+* ``verify1``   the same batch with one query token per sequence.
+* ``mla``       32 sequences, lengths uniform in [1024, 8192], 16 heads over a
+                576-element latent row (values are its first 512), block 32,
+                bf16.
+
 q, K and V are N(0, 1) drawn in float32 from a seeded ``torch.Generator`` on
 the target device and rounded to the storage dtype.  Pool blocks that no table
 references (and rows past a sequence's length) are filled the same way unless
@@ -300,3 +314,78 @@ BUILDERS = {
     "shared_prefix": shared_prefix,
     "long_context": long_context,
 }
+
+
+# multi-token query workloads (pa_prefill) and the latent cache (pa_decode_mla)
+QUERY_OPS = {
+    # a prompt chunk per sequence: 4 sequences whose last 1024 of 4096 tokens
+    # are new (chunked prefill), 32 query / 8 K/V heads, D=128, BS=16, fp16
+    "prefill": dict(S=4, lens="4096", tq=1024, H=32, Hkv=8, D=128, bs=16, dtype=torch.float16),
+    # speculative verification: 64 sequences with lengths as in continuous
+    # batching (log-normal, median 512, clipped to [32, 4096]), 4 drafted
+    # tokens each, 32 query / 8 K/V heads, D=128, BS=32, fp16
+    "verify": dict(S=64, lens="lognormal", tq=4, H=32, Hkv=8, D=128, bs=32, dtype=torch.float16),
+    # the same batch with one query token each: grouped-query decode through
+    # the matrix-core kernel (compare pa_decode_gqa on continuous batching)
+    "verify1": dict(S=64, lens="lognormal", tq=1, H=32, Hkv=8, D=128, bs=32, dtype=torch.float16),
+    # MLA decode: 32 sequences, lengths uniform in [1024, 8192], 16 heads (a
+    # 128-head model split over 8 GPUs by heads), 576-element latent rows,
+    # BS=32, bf16
+    "mla": dict(S=32, lens="uniform", tq=1, H=16, Hkv=1, D=576, bs=32, dtype=torch.bfloat16),
+}
+
+
+@dataclass
+class QueryWorkload:
+    """Inputs of one pa_prefill / pa_decode_mla call (see QUERY_OPS)."""
+    op: str
+    S: int
+    H: int
+    Hkv: int
+    D: int
+    Dv: int
+    bs: int
+    dtype: torch.dtype
+    tq: int
+    mla: bool
+    lens: np.ndarray        # int64 [S]
+    tables_np: np.ndarray   # int32 [S, width]
+    qs_np: np.ndarray       # int32 [S + 1]
+    T: int
+    width: int
+    scale: float
+    pools: tuple            # (k_pool, v_pool) or (latent pool,)
+    q: torch.Tensor
+
+
+def query_workload(op: str, seed: int = 0, device="cpu", heads: int = 0) -> QueryWorkload:
+    """Seeded inputs of a QUERY_OPS workload: lengths, blocks popped from a
+    shuffled free list, N(0,1) pools and queries in the workload's dtype."""
+    cfg = dict(QUERY_OPS[op])
+    if heads:
+        cfg["H"] = heads
+    S, H, Hkv, D, bs, dtype, tq = cfg["S"], cfg["H"], cfg["Hkv"], cfg["D"], cfg["bs"], cfg["dtype"], cfg["tq"]
+    mla = op == "mla"
+    dev = torch.device(device)
+    rng = np.random.default_rng(seed)
+    if cfg["lens"] == "4096":
+        lens = np.full(S, 4096, dtype=np.int64)
+    elif cfg["lens"] == "lognormal":
+        lens = np.clip(np.rint(rng.lognormal(math.log(512.0), 1.0, S)), 32, 4096).astype(np.int64)
+    else:
+        lens = rng.integers(1024, 8192, size=S, endpoint=True)
+    nb = int(sum(-(-int(L) // bs) for L in lens)) + 8
+    m = BlockManager(nb, bs, free_order=rng.permutation(nb).tolist())
+    for s, L in enumerate(lens):
+        m.allocate(s)
+        m.append_slots(s, int(L))
+    width = int(max(-(-int(L) // bs) for L in lens))
+    tables_np = m.block_tables(list(range(S)), width)
+    qs_np = np.concatenate([[0], np.cumsum(np.full(S, tq, dtype=np.int64))]).astype(np.int32)
+    T = int(qs_np[-1])
+    g = _generator(dev, seed * 1000003 + 29)
+    pools = (normal((nb, bs, D), dtype, dev, g),) if mla else \
+        (normal((nb, Hkv, bs, D), dtype, dev, g), normal((nb, Hkv, bs, D), dtype, dev, g))
+    q = normal((T, H, D), dtype, dev, g)
+    return QueryWorkload(op, S, H, Hkv, D, 512 if mla else D, bs, dtype, tq, mla, lens, tables_np, qs_np, T, width,
+                         1.0 / math.sqrt(192.0 if mla else D), pools, q)

@@ -193,3 +193,34 @@ def test_more_sequences_than_one_launch_holds():
     tq = rng.integers(1, 3, size=2100).tolist()
     c = Case(lens, tq, 8, 4, 64, 16, torch.float16, 88)
     assert_close(c.run(), c.oracle(), torch.float16, "2100 sequences")
+
+
+def test_long_context_verification():
+    """One sequence of 32768 tokens with 4 drafted tokens: 16 query rows of a
+    K/V head in one tile, the context split into many partitions."""
+    announce("prefill long-context verification 32768 x 4")
+    c = Case([32768], [4], 32, 8, 128, 16, torch.float16, 89)
+    ref = c.oracle()
+    for part in (0, 2048):
+        assert_close(c.run(part), ref, torch.float16, f"partition={part}")
+
+
+def test_more_query_tokens_than_context():
+    """Tq_s > L_s breaks the contract; the library's documented answer: rows
+    that would sit before position 0 see no key and come out zero, the others
+    are the causal rows of the L_s tokens."""
+    announce("prefill Tq > L")
+    lens, tq = [3, 40, 0], [5, 45, 2]
+    c = Case(lens, tq, 8, 2, 64, 16, torch.float16, 90)
+    w = c.w
+    tables = w.block_tables_np()
+    for part in (0, 16):
+        out = c.run(part)
+        for s, L in enumerate(lens):
+            r0, r1 = int(c.qs[s]), int(c.qs[s + 1])
+            before = r0 + tq[s] - L   # rows at positions < 0
+            assert torch.count_nonzero(out[r0:before]) == 0, f"seq {s}: rows before position 0"
+            if L:
+                ref = prefill_ref(c.q[before:r1].cpu(), w.k_pool.cpu(), w.v_pool.cpu(), tables[s:s + 1],
+                                  np.array([L]), np.array([0, L], np.int32), w.scale, w.block_size)
+                assert_close(out[before:r1], ref, torch.float16, f"seq {s} partition={part}")
