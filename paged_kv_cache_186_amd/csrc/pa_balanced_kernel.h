@@ -10,15 +10,18 @@
 // "Flash-Dec" milestone named on the "PagedAttention MLX：为Apple Silicon打造的
 // 高吞吐量LLM推理引擎" page).  Only the distribution of work differs.
 //
-// Work decomposition (our design): all (sequence, head, block) tiles are laid
+// Work decomposition (our design): all (sequence, head, block) units are laid
 // out in one sequence — sequence-major, then head, then logical block — and
-// W = min(waves of a fixed grid, T) waves take equal contiguous shares of it:
-// wave k takes tiles [floor(k*T/W), floor((k+1)*T/W)), never an empty share.  Every wave therefore moves the same
-// number of bytes (+-1 tile) whatever the mix of context lengths, every
-// workgroup starts at once, and consecutive shares — which land on different
-// XCDs — read every head.  Each workgroup rebuilds the per-sequence tile
-// offsets in LDS from context_lens (an exclusive prefix sum), so the host
-// needs no knowledge of the lengths.
+// W = min(waves of a fixed grid, T) waves take shares of equal cost: a unit
+// costs kBalancedCostUnit and each row (sequence, head) kBalancedCostRow more,
+// the measured time of a row change, so a wave whose share crosses many short
+// rows gets fewer units.  Each share is a contiguous run of units (possibly
+// none, for a share that falls between two rows' units).  Every wave moves
+// about the same bytes whatever the mix of context lengths, every workgroup
+// starts at once, and consecutive shares — which land on different XCDs —
+// read every head.  Each workgroup rebuilds the per-sequence unit and cost
+// offsets in LDS from context_lens (exclusive prefix sums), so the host needs
+// no knowledge of the lengths.
 //
 // A wave walks its share with the same two-stage load pipeline and per-lane-
 // group online softmax as the partitioned kernel.  When the row (sequence,
@@ -44,6 +47,12 @@ namespace pa {
 namespace {
 
 constexpr int kWaveMergeBatch = 8;  // partials in flight per lane group while merging
+
+// Cost of one row of `units` units in the balanced split (kBalancedCostUnit,
+// kBalancedCostRow: pa_internal.h).
+constexpr int kCostUnit = kBalancedCostUnit;
+constexpr int kCostRow = kBalancedCostRow;
+__device__ __forceinline__ int row_cost(int units) { return units > 0 ? kCostRow + kCostUnit * units : 0; }
 
 // One pipeline stage: one tile's K/V, its row's query slice, and its place.
 // A unit is R consecutive rows of one (block, head) tile, at most
@@ -83,9 +92,25 @@ struct BStage {
   int newrow;           // the unit opens a row segment of this wave (q is loaded)
 };
 
-// The wave whose share holds tile x: the largest k with floor(k*T/W) <= x.
-__device__ __forceinline__ long long wave_of_tile(long long x, long long T, long long W) {
-  return ((x + 1) * W - 1) / T;
+// floor(a / b) for 0 <= a <= 2^53 and b >= 1, given rb = 1.0 / b in fp64.  A
+// 64-bit integer division expands to a long software sequence on this GPU
+// (it sat in every row change of the walk below); here the fp64 quotient
+// a * rb (a is exact in fp64, rb and the product are correctly rounded) lies
+// within 2^-51 * (a / b) < 1 of a / b, so its truncation is off by at most
+// one, and one integer step makes it exact.
+__device__ __forceinline__ long long floor_div(long long a, long long b, double rb) {
+  long long c = static_cast<long long>(static_cast<double>(a) * rb);
+  if (c * b > a)
+    --c;
+  else if ((c + 1) * b <= a)
+    ++c;
+  return c;
+}
+
+// The wave whose share holds position x: the largest k with
+// floor(k*T/W) <= x (rT = 1.0 / T).
+__device__ __forceinline__ long long wave_of_tile(long long x, long long T, long long W, double rT) {
+  return floor_div((x + 1) * W - 1, T, rT);
 }
 
 // Log-sum-exp merge of one row's partials by a single wave (64 lanes), for
@@ -134,8 +159,7 @@ __device__ __forceinline__ void merge_row_wave(typename T::storage* __restrict__
 #pragma unroll
       for (int u = 0; u < B; ++u)
         if (i0 + u * kG + gl < nparts) bm = fmaxf(bm, lo_float(pr[h][u]));
-#pragma unroll
-      for (int off = kChunks; off < kWave; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+      bm = fold_max<kChunks>(bm);
       const float Mn = fmaxf(M[h], bm);
       const float rs = (M[h] == -INFINITY) ? 0.f : fast_exp2(M[h] - Mn);
       den[h] *= rs;
@@ -155,12 +179,9 @@ __device__ __forceinline__ void merge_row_wave(typename T::storage* __restrict__
   }
 #pragma unroll
   for (int h = 0; h < GW; ++h) {
+    den[h] = fold_sum<kChunks>(den[h]);
 #pragma unroll
-    for (int off = kChunks; off < kWave; off <<= 1) {
-      den[h] += __shfl_xor(den[h], off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) num[h][e] += __shfl_xor(num[h][e], off);
-    }
+    for (int e = 0; e < 4; ++e) num[h][e] = fold_sum<kChunks>(num[h][e]);
     if (gl == 0)
 #pragma unroll
       for (int e = 0; e < 4; ++e) out_row[h * D + 4 * c + e] = T::pack(num[h][e] / den[h]);
@@ -194,9 +215,11 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   constexpr int E = KT::kElems;
   constexpr int kThreads = NW * kWave;
   constexpr int kPer = (kBalancedMaxSeqs + kThreads - 1) / kThreads;  // sequences per thread
-  __shared__ int s_off[kBalancedMaxSeqs + 1];  // units of all sequences before s
+  __shared__ int s_off[kBalancedMaxSeqs + 1];   // units of all sequences before s (per head)
+  __shared__ int s_coff[kBalancedMaxSeqs + 1];  // cost of all sequences before s (per head)
   __shared__ int s_len[kBalancedMaxSeqs];
   __shared__ int s_wsum[NW];
+  __shared__ int s_wcost[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -207,81 +230,154 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   const int HKV = num_kv_heads;
   const int cap = max_blocks * BS;
 
-  // 1. clamped lengths and the exclusive prefix sum of units per sequence;
-  //    thread t owns sequences [t*kPer, (t+1)*kPer)
+  // 1. clamped lengths and the exclusive prefix sums of units and of cost per
+  //    sequence (one row's cost: kCostRow + kCostUnit per unit, nothing for an
+  //    empty row); thread t owns sequences [t*kPer, (t+1)*kPer)
   for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);  // coalesced
   __syncthreads();
   int nbl[kPer];
   int mine = 0;
+  int mine_c = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int s = tid * kPer + i;
     nbl[i] = s < S ? (s_len[s] + R - 1) / R : 0;  // units of sequence s (per head)
     mine += nbl[i];
+    mine_c += row_cost(nbl[i]);
   }
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
+  const int incl = wave_prefix_sum(mine);
+  const int incl_c = wave_prefix_sum(mine_c);
+  if (lane == kWave - 1) {
+    s_wsum[wave] = incl;
+    s_wcost[wave] = incl_c;
   }
-  if (lane == kWave - 1) s_wsum[wave] = incl;
   __syncthreads();
   int before = 0;
   int total = 0;
+  int before_c = 0;
+  int total_c = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     const int v = s_wsum[w];
+    const int vc = s_wcost[w];
     before += (w < wave) ? v : 0;
+    before_c += (w < wave) ? vc : 0;
     total += v;
+    total_c += vc;
   }
   int run = before + incl - mine;
+  int run_c = before_c + incl_c - mine_c;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int s = tid * kPer + i;
-    if (s < S) s_off[s] = run;
+    if (s < S) {
+      s_off[s] = run;
+      s_coff[s] = run_c;
+    }
     run += nbl[i];
+    run_c += row_cost(nbl[i]);
   }
-  if (tid == 0) s_off[S] = total;
+  if (tid == 0) {
+    s_off[S] = total;
+    s_coff[S] = total_c;
+  }
   __syncthreads();
   total = __builtin_amdgcn_readfirstlane(total);
+  total_c = __builtin_amdgcn_readfirstlane(total_c);
 
   // 2. empty contexts give zero rows (spread over the workgroups)
   for (int s = blockIdx.x; s < S; s += gridDim.x)
     if (s_len[s] == 0)
       for (int i = tid; i < NH * D; i += kThreads) out[static_cast<size_t>(s) * NH * D + i] = QT::pack(0.f);
 
-  // 3. this wave's share of the T units (no workgroup barrier after this point)
-  // Wn = min(waves in the grid, T): with at most one wave per unit no share is
-  // empty, so the waves kf..kl covering a row each store exactly one partial.
+  // 3. this wave's share (no workgroup barrier after this point).  Work is
+  // laid out as rows (sequence-major, then head), each a row cost kCostRow
+  // followed by its units at kCostUnit each; unit x starts at cost position
+  // C(x).  Wave k owns the units whose cost start lies in
+  // [floor(k*C_all/Wn), floor((k+1)*C_all/Wn)): a contiguous run of units,
+  // and equal cost per wave charges each row segment for the time a row
+  // change takes.  Wn = min(waves in the grid, T): a share is then at least
+  // kCostUnit long, so every wave between the owners of a row's first and
+  // last units owns some of that row, and stores exactly one partial of it.
   const long long T_all = static_cast<long long>(H) * total;
+  const long long C_all = static_cast<long long>(H) * total_c;
   const long long Wn = min(static_cast<long long>(gridDim.x) * NW, T_all);
   const long long k = static_cast<long long>(blockIdx.x) * NW + wave;
   if (k >= Wn) return;
-  const long long t0 = k * T_all / Wn;
-  const long long t1 = (k + 1) * T_all / Wn;
-  const int nt = static_cast<int>(t1 - t0);
-
-  // walker: the largest s with H*off[s] <= t0 has units (off[s+1] > off[s])
-  int lo = 0;
-  int hi = S - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (static_cast<long long>(H) * s_off[mid] <= t0)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  int w_s = __builtin_amdgcn_readfirstlane(lo);
+  // C_all < 2^43 (the host bounds it) and Wn <= 2^10, so every dividend
+  // below stays within floor_div's 2^53
+  const double rC = 1.0 / static_cast<double>(C_all);
+  const double rW = 1.0 / static_cast<double>(Wn);
+  // cost start of the first unit of row (s, h)
+  auto row_start = [&](int s, int h) __attribute__((always_inline)) {
+    const int nb = __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]);
+    return static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_coff[s]) +
+           static_cast<long long>(h) * row_cost(nb) + kCostRow;
+  };
+  // the first unit whose cost start is >= c: its sequence, head and index in
+  // the row, and its place in the unit order (T_all and s = S past the end)
+  auto first_unit_at = [&](long long c, int& s, int& h, int& j) __attribute__((always_inline)) {
+    if (c >= C_all) {
+      s = S;
+      h = j = 0;
+      return T_all;
+    }
+    // the largest s with H*coff[s] <= c (its cost range holds c, so it has
+    // units): the lanes test 64 candidates at once, evenly spaced over all
+    // sequences, then the 64 (or fewer) that follow the last one that passed
+    int base = 0;
+    int span = S;
+    if (S > kWave) {
+      const int stride = (S + kWave - 1) / kWave;
+      const int cand = lane * stride;
+      const uint64_t pass = __builtin_amdgcn_ballot_w64(cand < S && static_cast<long long>(H) * s_coff[cand] <= c);
+      base = (63 - __builtin_clzll(pass)) * stride;  // lane 0 always passes (coff[0] = 0)
+      span = min(stride, S - base);
+    }
+    const uint64_t pass =
+        __builtin_amdgcn_ballot_w64(lane < span && static_cast<long long>(H) * s_coff[base + min(lane, span - 1)] <= c);
+    s = base + (63 - __builtin_clzll(pass));
+    const int nb = __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]);
+    const int rc = row_cost(nb);
+    const long long local = c - static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_coff[s]);
+    h = static_cast<int>(floor_div(local, rc, 1.0 / static_cast<double>(rc)));
+    const int o = static_cast<int>(local - static_cast<long long>(h) * rc);  // in [0, rc)
+    j = o <= kCostRow ? 0 : (o - kCostRow + kCostUnit - 1) / kCostUnit;   // in [0, nb]
+    if (j == nb) {  // past the row's last unit start: the next row's first unit
+      j = 0;
+      if (++h == H) {
+        h = 0;
+        do {
+          ++s;
+        } while (s < S && __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]) == 0);
+        if (s == S) return T_all;
+      }
+    }
+    const int nbs = __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]);
+    return static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_off[s]) +
+           static_cast<long long>(h) * nbs + j;
+  };
+  int w_s, w_h, w_j;
+  const long long c1 = floor_div((k + 1) * C_all, Wn, rW);
+  const long long t0 = first_unit_at(floor_div(k * C_all, Wn, rW), w_s, w_h, w_j);
+  // a share that falls between two rows' units holds none: nothing to do
+  if (w_s == S || row_start(w_s, w_h) + static_cast<long long>(kCostUnit) * w_j >= c1) return;
+  // the share's end is found after its first loads are issued (below)
+  long long t1 = 0;
   int w_nb = __builtin_amdgcn_readfirstlane(s_off[w_s + 1] - s_off[w_s]);
-  const long long u0 = t0 - static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_off[w_s]);
-  int w_h = static_cast<int>(u0 / w_nb);
-  int w_j = static_cast<int>(u0 % w_nb);
+  // the K/V head of the row's query heads, updated only when the row changes
+  // (no division when each work row is one whole group, as in plain MHA)
+  auto kv_head = [&](int h) __attribute__((always_inline)) { return group == GW ? h : (h * GW) / group; };
+  int w_kvh = kv_head(w_h);
   auto advance = [&]() __attribute__((always_inline)) {
     if (++w_j < w_nb) return;
     w_j = 0;
-    if (++w_h < H) return;
+    if (++w_h < H) {
+      w_kvh = kv_head(w_h);
+      return;
+    }
     w_h = 0;
+    w_kvh = 0;
     do {
       ++w_s;
     } while (w_s < S && __builtin_amdgcn_readfirstlane(s_off[w_s + 1] - s_off[w_s]) == 0);
@@ -319,7 +415,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
       st.bad = 1;  // never dereference an id outside the pool
       phys = 0;
     }
-    const int kvh = (w_h * GW) / group;  // the K/V head of this row's query heads
+    const int kvh = w_kvh;  // the K/V head of this row's query heads
     const size_t tile = ((static_cast<size_t>(phys) * HKV + kvh) * BS + sub * R) * C::kRowBytes;
     const char* kb = k_pool + tile + lane * kVecBytes;
     const char* vb = v_pool + tile + lane * kVecBytes;
@@ -365,6 +461,8 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   // rows whose partial is stored and whose ticket is still to be taken (<= 2)
   int pend = 0;
   size_t pend_row[2] = {0, 0};
+  int pend_s[2] = {0, 0};
+  int pend_h[2] = {0, 0};
   int pend_n[2] = {0, 0};
   size_t pend_slot0[2] = {0, 0};
 
@@ -372,28 +470,24 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     const int nb = __builtin_amdgcn_readfirstlane(s_off[cur_s + 1] - s_off[cur_s]);
     const int off_s = __builtin_amdgcn_readfirstlane(s_off[cur_s]);
     const long long first = static_cast<long long>(H) * off_s + static_cast<long long>(cur_h) * nb;
-    const long long kf = wave_of_tile(first, T_all, Wn);
-    const long long kl = wave_of_tile(first + nb - 1, T_all, Wn);
+    // the whole row lies in this share: final, no partial to merge
+    const bool whole = first >= t0 && first + nb <= t1;
     const size_t row = static_cast<size_t>(cur_s) * H + cur_h;
     const size_t slot = static_cast<size_t>(k) + row;
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
       // fold the lane groups of the wave into one state
       float M = m[g];
-#pragma unroll
-      for (int off = C::kLanesPerRow; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      M = fold_max<C::kLanesPerRow>(M);
       const float sc = (m[g] == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
       float lt = l[g] * sc;
       float a[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) a[e] = acc[g][e] * sc;
+      lt = fold_sum<C::kLanesPerRow>(lt);
 #pragma unroll
-      for (int off = C::kLanesPerRow; off < kWave; off <<= 1) {
-        lt += __shfl_xor(lt, off);
-#pragma unroll
-        for (int e = 0; e < E; ++e) a[e] += __shfl_xor(a[e], off);
-      }
-      if (kf == kl) {  // the whole row is in this share: final
+      for (int e = 0; e < E; ++e) a[e] = fold_sum<C::kLanesPerRow>(a[e]);
+      if (whole) {
         if (grp == 0) {
           float o[E];
           const float inv = 1.f / lt;
@@ -409,13 +503,20 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
         if (lane == 0) store_coherent_u64(ws_ml + sg * 2, M, seg_bad ? __builtin_nanf("") : lt);
       }
     }
-    if (kf != kl) {
+    if (!whole) {  // the waves kf..kl cover the row: the owners of its first and last units
+      const long long cf = row_start(cur_s, cur_h);
+      const long long kf = wave_of_tile(cf, C_all, Wn, rC);
+      const long long kl = wave_of_tile(cf + static_cast<long long>(kCostUnit) * (nb - 1), C_all, Wn, rC);
       if (pend == 0) {
         pend_row[0] = row;
+        pend_s[0] = cur_s;
+        pend_h[0] = cur_h;
         pend_n[0] = static_cast<int>(kl - kf + 1);
         pend_slot0[0] = static_cast<size_t>(kf) + row;
       } else {
         pend_row[1] = row;
+        pend_s[1] = cur_s;
+        pend_h[1] = cur_h;
         pend_n[1] = static_cast<int>(kl - kf + 1);
         pend_slot0[1] = static_cast<size_t>(kf) + row;
       }
@@ -469,6 +570,11 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   // loads, then a one- or two-stage epilogue), then the last segment
   St a, b;
   load_stage(a);
+  {
+    int e_s, e_h, e_j;
+    t1 = first_unit_at(c1, e_s, e_h, e_j);
+  }
+  const int nt = static_cast<int>(t1 - t0);  // >= 1
   int st = 0;
   for (; st + 2 < nt; st += 2) {
     load_stage(b);
@@ -499,8 +605,8 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   for (int p = 0; p < 2; ++p) {
     if (p >= pend) break;
     if (tk[p] == static_cast<uint32_t>(pend_n[p] - 1)) {
-      const size_t rs = pend_row[p] / H;  // sequence and head group of the row
-      const size_t rh = pend_row[p] % H;
+      const size_t rs = pend_s[p];  // sequence and head group of the row
+      const size_t rh = pend_h[p];
       merge_row_wave<QT, D, GW>(out + (rs * NH + rh * GW) * D, ws_ml + pend_slot0[p] * GW * 2,
                                 ws_acc + pend_slot0[p] * GW * D, pend_n[p], lane);
       if (lane == 0)  // ready for the next call

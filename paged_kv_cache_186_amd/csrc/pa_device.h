@@ -209,8 +209,82 @@ __device__ __forceinline__ float dpp_row_half_mirror(float x) {
 __device__ __forceinline__ float dpp_row_mirror(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float swizzle_xor16(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+
+// Exchanges between lane groups without the LDS crossbar (__shfl_xor becomes
+// ds_bpermute, an LDS round trip of ~100+ cycles per value).
+//  * row_ror<N>: each lane reads lane (i - N) mod 16 of its 16-lane row (DPP);
+//  * swap_pair<16> / swap_pair<32>: v_permlane16_swap (v_permlane32_swap),
+//    given x in both operands, leaves x of the lower lane of each pair
+//    (l, l ^ 16) (or (l, l ^ 32)) in the first register and x of the upper
+//    lane in the second, in both lanes of the pair, so sums and maxima of the
+//    two end with the same bits in both lanes.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  static_assert(N == 4 || N == 8, "rotations by 4 or 8 lanes");
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + N, 0xF, 0xF, true));
+}
+template <int OFF>
+__device__ __forceinline__ void swap_pair(float x, float& lo, float& hi) {
+  static_assert(OFF == 16 || OFF == 32, "lane swaps across 16 or 32 lanes");
+  // Written out: this compiler's __builtin_amdgcn_permlane{16,32}_swap hands
+  // back the first register of the pair in both result elements.  b is a copy
+  // of x; the two wait states cover the VALU writes of both operands before
+  // the swap reads them (as the compiler itself places them).
+  uint32_t a = __builtin_bit_cast(uint32_t, x);
+  uint32_t b;
+  if constexpr (OFF == 16)
+    asm("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
+  else
+    asm("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+
+// Inclusive prefix sum of x over the 64 lanes of a wave, in DPP steps (no
+// LDS round trips): sums within each 16-lane row by shifts of 1, 2, 4 and 8
+// lanes (a lane shifted in from outside the row reads 0), then the total of
+// row 0 added to row 1 and of row 2 to row 3 (row_bcast:15, rows 1 and 3
+// written), then the total of rows 0-1 to rows 2 and 3 (row_bcast:31).  All
+// 64 lanes must be active.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Sum / maximum of x over the lanes that share lane % G (G = 4, 8, 16 or 32):
+// the lane groups of a wave folded into one.  The maximum is the same in
+// every lane; the sum is complete in every lane (for G >= 8 also bit-identical
+// across lanes; for G = 4 the first two steps associate differently per lane).
+template <int G>
+__device__ __forceinline__ float fold_sum(float x) {
+  static_assert(G == 4 || G == 8 || G == 16 || G == 32, "fold over groups of 4, 8, 16 or 32 lanes");
+  if constexpr (G == 4) x += row_ror<4>(x);
+  if constexpr (G <= 8) x += row_ror<8>(x);
+  float lo, hi;
+  if constexpr (G <= 16) {
+    swap_pair<16>(x, lo, hi);
+    x = lo + hi;
+  }
+  swap_pair<32>(x, lo, hi);
+  return lo + hi;
+}
+template <int G>
+__device__ __forceinline__ float fold_max(float x) {
+  static_assert(G == 4 || G == 8 || G == 16 || G == 32, "fold over groups of 4, 8, 16 or 32 lanes");
+  if constexpr (G == 4) x = fmaxf(x, row_ror<4>(x));
+  if constexpr (G <= 8) x = fmaxf(x, row_ror<8>(x));
+  float lo, hi;
+  if constexpr (G <= 16) {
+    swap_pair<16>(x, lo, hi);
+    x = fmaxf(lo, hi);
+  }
+  swap_pair<32>(x, lo, hi);
+  return fmaxf(lo, hi);
 }
 
 template <int G>
@@ -220,7 +294,11 @@ __device__ __forceinline__ float group_sum(float x) {
   x += dpp_quad_xor2(x);
   if constexpr (G >= 8) x += dpp_row_half_mirror(x);
   if constexpr (G >= 16) x += dpp_row_mirror(x);
-  if constexpr (G >= 32) x += swizzle_xor16(x);
+  if constexpr (G >= 32) {
+    float lo, hi;
+    swap_pair<16>(x, lo, hi);
+    x = lo + hi;
+  }
   return x;
 }
 

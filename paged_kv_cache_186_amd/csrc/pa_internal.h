@@ -112,6 +112,20 @@ inline int default_partition_blocks(int num_seqs, int num_heads, int max_blocks,
 // kBalancedMinTiles tiles each.  The per-sequence prefix sums live in LDS,
 // hence the sequence limit.
 constexpr int kBalancedMaxSeqs = 2048;
+// Cost model of the balanced split: a unit costs kBalancedCostUnit, and each
+// row segment a wave walks costs kBalancedCostRow more.  Measured: a row
+// change takes about two thirds of a unit's time (layer-shape and
+// continuous-batching workloads: with the same number of units, a wave that
+// walked six rows took ~2 us longer than one that walked one).
+constexpr int kBalancedCostUnit = 3;
+constexpr int kBalancedCostRow = 2;
+// Cost positions stay within int per head and within 2^43 over all rows (a
+// block holds at most 8 units of any balanced kernel).
+inline bool balanced_cost_fits(long long num_seqs, long long rows, long long max_blocks) {
+  constexpr long long kMaxUnitsPerBlock = 8;
+  constexpr long long c = (kBalancedCostUnit + kBalancedCostRow) * kMaxUnitsPerBlock;
+  return num_seqs * max_blocks * c < (1LL << 31) && rows * max_blocks * c < (1LL << 43);
+}
 constexpr int kBalancedWaves = PA_BALANCED_WAVES;
 constexpr int kBalancedWorkgroups = PA_BALANCED_WORKGROUPS;
 constexpr int kBalancedMinTiles = PA_BALANCED_MIN_TILES;

@@ -217,12 +217,7 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
     cnt[i] = c;
     mine += c;
   }
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_prefix_sum(mine);
   if (lane == kWave - 1) s_wsum[wave] = incl;
   __syncthreads();
   int before = 0;
@@ -418,8 +413,7 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
         float cm = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) cm = fmaxf(cm, fmaxf(fmaxf(z[kb][0], z[kb][1]), fmaxf(z[kb][2], z[kb][3])));
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        cm = fold_max<16>(cm);  // the row's four lanes: l, l ^ 16, l ^ 32, l ^ 48
         const float cms = (cm == -INFINITY) ? -INFINITY : cm * qk_scale;  // qk_scale > 0
         const float mn = fmaxf(m[t], cms);
         if (__builtin_amdgcn_ballot_w64(mn > m[t] + kRescaleLog2) != 0) {
@@ -699,12 +693,7 @@ __global__ __launch_bounds__(kMlaWaves* kWave, 2) void mla_split_kernel(
     cnt[i] = s < S ? tiles * max(1, (s_len[s] + part_tokens - 1) / part_tokens) : 0;
     mine += cnt[i];
   }
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_prefix_sum(mine);
   if (lane == kWave - 1) s_wsum[wave] = incl;
   __syncthreads();
   int before = 0;
@@ -853,8 +842,7 @@ __global__ __launch_bounds__(kMlaWaves* kWave, 2) void mla_split_kernel(
       }
       float cm = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
                        fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
-      cm = fmaxf(cm, __shfl_xor(cm, 16));
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      cm = fold_max<16>(cm);  // the row's four lanes: l, l ^ 16, l ^ 32, l ^ 48
       const float cms = (cm == -INFINITY) ? -INFINITY : cm * qk_scale;
       const float mn = fmaxf(m, cms);
       if (__builtin_amdgcn_ballot_w64(mn > m + kRescaleLog2) != 0) {
@@ -907,8 +895,7 @@ __global__ __launch_bounds__(kMlaWaves* kWave, 2) void mla_split_kernel(
         attend_step(a);
       }
     }
-    float lrow = lsum + __shfl_xor(lsum, 16);
-    lrow += __shfl_xor(lrow, 32);
+    float lrow = fold_sum<16>(lsum);
     if (bad) lrow = __builtin_nanf("");
 
     auto write_row = [&](const float (&o)[kDq][16]) __attribute__((always_inline)) {
