@@ -314,6 +314,37 @@ def test_balanced_split_with_empty_and_tiny_rows(dtype, bs):
         assert torch.equal(out[s].cpu(), torch.zeros_like(out[s].cpu()))
 
 
+# batch sizes chosen so that the units about match the 1024 waves of the grid
+# (between 400 and 1900 units over 3 heads): then tens of shares fall between
+# two rows' units
+@pytest.mark.parametrize("dtype,D,bs,size", [(torch.float32, 128, 32, 100), (torch.float16, 64, 16, 200),
+                                              (torch.bfloat16, 128, 16, 200), (torch.float16, 128, 32, 150)])
+@pytest.mark.parametrize("seed", [3, 4])
+def test_balanced_split_shares_between_rows(dtype, D, bs, size, seed):
+    """Many short rows and about as many units as waves: the cost-weighted
+    split then gives some waves a share that falls between two rows' units
+    (no work) and many waves several row segments; the balanced kernel must
+    still cover every unit once, merge every split row, and leave its
+    counters at zero (a second call gives the same bits)."""
+    announce(f"decode balanced shares between rows dtype={dtype} D={D} bs={bs} size={size} seed={seed}")
+    rng = np.random.default_rng(seed)
+    lens = rng.choice([0, 1, 3, 8, bs + 1, 2 * bs + 5], size=size).tolist()
+    w = _ragged_workload(lens, 3, D, bs, dtype, seed)
+    S, H = w.num_seqs, w.num_heads
+    need = pa.pa_decode_workspace_size(S, H, D, w.table_width, bs, 0)
+    ws = pa.new_workspace(need, DEV)
+    bt, cl = w.block_tables().to(DEV), w.context_lens().to(DEV)
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(w.q)
+        pa.pa_decode(out, w.q, w.k_pool, w.v_pool, bt, cl, w.scale, bs, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[: 4 * S * H].view(torch.int32).abs().sum()) == 0, "counters left non-zero"
+        outs.append(out)
+    assert_close(outs[0], oracle_decode(w), dtype, "shares between rows")
+    assert torch.equal(bits(outs[1]), bits(outs[0])), "second call differs"
+
+
 def test_more_sequences_than_the_balanced_limit_use_partitions():
     announce("decode 2100 sequences (partitioned default)")
     rng = np.random.default_rng(5)

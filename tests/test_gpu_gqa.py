@@ -159,3 +159,17 @@ def test_one_workspace_serves_grouped_plain_and_partitioned_calls():
         torch.cuda.synchronize()
         assert int(ws[: 4 * S * H].view(torch.int32).abs().sum()) == 0, f"counters after call {it}"
         assert_close(out, ref, torch.float16, f"call {it} ({kind})")
+
+
+@pytest.mark.parametrize("Hkv", [4, 2, 1])
+def test_grouped_split_shares_between_rows(Hkv):
+    """Grouped heads with many short rows and about as many units as waves
+    (shares that fall between rows' units, waves walking many row segments)."""
+    announce(f"decode gqa shares between rows Hkv={Hkv}")
+    rng = np.random.default_rng(21)
+    lens = rng.choice([0, 1, 5, 16, 17, 40, 130], size=400).tolist()
+    w = _gqa_workload(lens, 8, Hkv, 128, 16, torch.float16, 21)
+    ref = _oracle(w)
+    first = _run(w)
+    assert_close(first, ref, torch.float16, f"gqa shares between rows Hkv={Hkv}")
+    assert torch.equal(bits(_run(w)), bits(first)), "second call differs"
