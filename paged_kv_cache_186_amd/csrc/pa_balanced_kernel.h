@@ -71,6 +71,18 @@ constexpr int kUnitLoads = PA_UNIT_LOADS;
 #define PA_UNIT_LOADS_GROUPED 4
 #endif
 constexpr int kUnitLoadsGrouped = PA_UNIT_LOADS_GROUPED;
+// Grouped kernels use at most T / kGroupedMinUnits(GW) waves: their units
+// are few and arithmetic-heavy on small batches, and splitting a row over
+// many waves made the split rows' tickets (many waves' atomics on one row
+// counter) and merges (GW heads' partials from each wave) the bulk of the
+// time.  Measured on the layer shape (8 sequences, 32 query heads): with 16,
+// 8 and 4 K/V heads, 20.5 -> 17.9 us (GW 2, at least 8 units per wave),
+// 24.9 -> 23.0 us (GW 4, at least 4) and 51.5 -> 41.0 us (GW 8, at least 4);
+// large batches keep every wave busy either way.
+template <int GW>
+constexpr long long grouped_min_units() {
+  return GW >= 4 ? 4 : 8;
+}
 
 template <typename T, int D, int BS, int GW>
 struct Unit {
@@ -301,7 +313,8 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   // last units owns some of that row, and stores exactly one partial of it.
   const long long T_all = static_cast<long long>(H) * total;
   const long long C_all = static_cast<long long>(H) * total_c;
-  const long long Wn = min(static_cast<long long>(gridDim.x) * NW, T_all);
+  const long long Wn = min(static_cast<long long>(gridDim.x) * NW,
+                           GW > 1 ? max(1LL, T_all / grouped_min_units<GW>()) : T_all);
   const long long k = static_cast<long long>(blockIdx.x) * NW + wave;
   if (k >= Wn) return;
   // C_all < 2^43 (the host bounds it) and Wn <= 2^10, so every dividend
