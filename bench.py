@@ -604,6 +604,18 @@ def main() -> int:
     warm_ms = time_graph(warm_graph, n_rep, stream) / R
     n_steps = n_rep * R
 
+    # the shared-prefix workload's copy-on-write (pa_copy_blocks of the pairs
+    # that made the last shared block private), cold, one call per replica
+    cow = None
+    if getattr(w, "cow_pairs", None) and not fp8 and not gqa:
+        pairs = torch.tensor(w.cow_pairs, dtype=torch.int32, device=dev)
+        cow_graph = capture(lambda: [pa.pa_copy_blocks(*reps[i % R][:2], pairs) for i in range(R)])
+        cow_ms = time_graph(cow_graph, n_rep, stream) / R
+        b_cow = 2 * 2 * len(w.cow_pairs) * bs * Hkv * D * e  # K and V, read + write
+        cow = {"pairs": len(w.cow_pairs), "bytes_per_call": b_cow, "us_per_call": round(cow_ms * 1e3, 3),
+               "GB/s": round(b_cow / (cow_ms * 1e-3) / 1e9, 2),
+               "timing": "HIP graph of one call per pool replica, HIP events around the replays"}
+
     b_dec = decode_bytes(lens, H, D, e, bs, e_kv, Hkv)
     b_res = reshape_bytes(S, Hkv, D, e, e_kv)
     step_s = step_ms * 1e-3
@@ -655,6 +667,8 @@ def main() -> int:
                      "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel_source_sha": digest},
     }
+    if cow is not None:
+        result["copy_blocks"] = cow
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s on one host thread")
         host.update({"q": q.cpu(), "tables": w.block_tables_np(), "lens": lens, "scale": w.scale,
