@@ -40,7 +40,7 @@ COLD_BYTES = 2 << 30           # replica footprint that defeats the 256 MB last-
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_decode_balanced.hip", "pa_decode_balanced_gqa2.hip",
-                            "pa_decode_balanced_gqa4.hip", "pa_decode_balanced_gqa8.hip",
+                            "pa_decode_balanced_gqa4.hip",
                             "pa_balanced_kernel.h", "pa_attend.h", "pa_device.h", "pa_internal.h",
                             "pa_api.cpp")]
 

@@ -188,9 +188,9 @@ pa_status_t pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapp
  * for F16 / BF16 queries, an 8-bit format (then k_scales / v_scales are
  * required, else ignored).  num_heads must be a multiple of num_kv_heads.
  * With the default split (partition_size 0, num_seqs <= 2048) and 16-bit
- * queries, one K/V tile load serves 8, 4 or 2 query heads of a group (the
- * largest dividing the group size; at most 4 with an 8-bit cache); otherwise
- * every query head reads its K/V head's tiles itself.  Workspace: pa_decode_gqa_workspace_size() for the
+ * queries, one K/V tile load serves 4 or 2 query heads of a group (the
+ * largest dividing the group size; a larger group is served 4 heads at a
+ * time); otherwise every query head reads its K/V head's tiles itself.  Workspace: pa_decode_gqa_workspace_size() for the
  * same arguments; same contract as pa_decode_workspace_size().
  */
 size_t pa_decode_gqa_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

@@ -71,14 +71,14 @@ constexpr int kUnitLoads = PA_UNIT_LOADS;
 #define PA_UNIT_LOADS_GROUPED 4
 #endif
 constexpr int kUnitLoadsGrouped = PA_UNIT_LOADS_GROUPED;
-// Grouped kernels use at most T / kGroupedMinUnits(GW) waves: their units
+// Grouped kernels use at most T / grouped_min_units<GW>() waves: their units
 // are few and arithmetic-heavy on small batches, and splitting a row over
 // many waves made the split rows' tickets (many waves' atomics on one row
 // counter) and merges (GW heads' partials from each wave) the bulk of the
-// time.  Measured on the layer shape (8 sequences, 32 query heads): with 16,
-// 8 and 4 K/V heads, 20.5 -> 17.9 us (GW 2, at least 8 units per wave),
-// 24.9 -> 23.0 us (GW 4, at least 4) and 51.5 -> 41.0 us (GW 8, at least 4);
-// large batches keep every wave busy either way.
+// time.  Measured on the layer shape (8 sequences, 32 query heads): with 16
+// and 8 K/V heads, 20.5 -> 17.9 us (GW 2, at least 8 units per wave) and
+// 24.9 -> 23.0 us (GW 4, at least 4); large batches keep every wave busy
+// either way.
 template <int GW>
 constexpr long long grouped_min_units() {
   return GW >= 4 ? 4 : 8;

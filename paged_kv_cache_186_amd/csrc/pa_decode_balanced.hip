@@ -11,8 +11,6 @@ hipError_t launch_decode_balanced(const DecodeArgs& a, hipStream_t stream) {
       return launch_decode_balanced_gqa2(a, stream);
     case 4:
       return launch_decode_balanced_gqa4(a, stream);
-    case 8:
-      return launch_decode_balanced_gqa8(a, stream);
     default:
       break;
   }

@@ -52,7 +52,7 @@ struct DecodeArgs {
   int num_seqs;
   int num_heads;         // query heads
   int num_kv_heads;      // K/V heads (divides num_heads)
-  int group_width;       // kBalanced: query heads per K/V tile load (1, 2, 4 or 8)
+  int group_width;       // kBalanced: query heads per K/V tile load (1, 2 or 4)
   int head_dim;
   int num_blocks;
   int max_blocks_per_seq;
@@ -139,10 +139,9 @@ inline int balanced_workgroups(int num_seqs, int num_heads, int max_blocks) {
 
 hipError_t launch_decode_partitioned(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced(const DecodeArgs& a, hipStream_t stream);
-// group_width 2, 4, 8 (8: 16-bit caches only)
+// group_width 2, 4
 hipError_t launch_decode_balanced_gqa2(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced_gqa4(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_balanced_gqa8(const DecodeArgs& a, hipStream_t stream);
 
 // Attention of several query rows per (sequence, K/V head) on the matrix
 // cores: multi-token queries (pa_prefill) and decode over an MLA latent cache

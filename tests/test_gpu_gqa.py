@@ -1,7 +1,7 @@
 """GPU parity of grouped-query decode (pa_decode_gqa) against the float64
 oracle (decode_gqa_ref), through the C ABI: every group width the kernels
-build (tile loads shared by 8, 4, 2 query heads, and 1 — each head reads its
-own K/V head), multi-query (one K/V head), 16-bit and 8-bit caches, the
+build (tile loads shared by 4 or 2 query heads — groups of 8 and more 4 at a
+time — and 1: each head reads its own K/V head), multi-query (one K/V head), 16-bit and 8-bit caches, the
 default split and explicit partitions, ragged NaN-poisoned batches."""
 
 import numpy as np
