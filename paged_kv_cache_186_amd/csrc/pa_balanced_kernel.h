@@ -1,6 +1,6 @@
 // Balanced-split decode kernel template (gfx950), included by
 // pa_decode_balanced.hip (one query head per K/V head) and
-// pa_decode_balanced_gqa.hip (grouped-query heads).
+// pa_decode_balanced_gqa{2,4}.hip (grouped-query heads, 2 or 4 per K/V load).
 //
 // Same computation as the partitioned kernel (pa_decode.hip): single-query
 // softmax attention per (sequence, head) over K/V rows found through the block
@@ -140,7 +140,10 @@ __device__ __forceinline__ void merge_row_wave(typename T::storage* __restrict__
                                                const float* __restrict__ acc, int nparts, int lane) {
   constexpr int kChunks = D / 4;       // 16-byte slices of a partial row
   constexpr int kG = kWave / kChunks;  // partials read side by side
-  constexpr int B = GW <= 2 ? kWaveMergeBatch : (4 * kWaveMergeBatch) / GW;  // <= 48 loads per lane
+  // B partials per lane group and batch: 3 loads each per head, GW*B*3 <= 48
+  // per lane, within the 63 loads a wave can have in flight, so that a batch
+  // is one memory round trip
+  constexpr int B = GW <= 2 ? kWaveMergeBatch : (2 * kWaveMergeBatch) / GW;
   const int c = lane % kChunks;
   const int gl = lane / kChunks;
   float M[GW];       // running max per head (identical in every lane)
