@@ -345,6 +345,21 @@ def test_balanced_split_shares_between_rows(dtype, D, bs, size, seed):
     assert torch.equal(bits(outs[1]), bits(outs[0])), "second call differs"
 
 
+def test_balanced_split_at_its_sequence_limit():
+    """2048 sequences (the balanced split's limit): the sequence of a cost
+    position is found by a two-level wave ballot (64 candidates 32 apart,
+    then 32 consecutive ones); short ragged contexts with empty ones among
+    them, so that shares also fall between rows' units."""
+    announce("decode balanced 2048 sequences")
+    rng = np.random.default_rng(8)
+    lens = rng.integers(0, 41, size=2048).tolist()
+    w = _ragged_workload(lens, 2, 64, 16, torch.float16, 8)
+    out = gpu_decode(w)
+    assert_close(out, oracle_decode(w), torch.float16, "2048 sequences")
+    for s in [i for i, L in enumerate(lens) if L == 0][:20]:
+        assert torch.equal(out[s].cpu(), torch.zeros_like(out[s].cpu()))
+
+
 def test_more_sequences_than_the_balanced_limit_use_partitions():
     announce("decode 2100 sequences (partitioned default)")
     rng = np.random.default_rng(5)
