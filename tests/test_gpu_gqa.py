@@ -112,11 +112,41 @@ def test_layer_shape_with_8_kv_heads():
     assert_close(_run(w), _oracle(w), torch.float16, "layer shape gqa")
 
 
+@pytest.mark.parametrize("Hkv", [8, 1])
+def test_continuous_batching_with_grouped_heads(Hkv):
+    """The continuous-batching workload (64 sequences, log-normal lengths,
+    block 32, fp16) with 32 query heads over 8 K/V heads or one (multi-query),
+    whole output against the oracle."""
+    announce(f"gqa continuous batching 32/{Hkv}")
+    w = W.continuous_batching(0, device=DEV, poison=True)
+    w.k_pool = w.k_pool[:, :Hkv].contiguous()
+    w.v_pool = w.v_pool[:, :Hkv].contiguous()
+    assert_close(_run(w), _oracle(w), torch.float16, f"continuous batching gqa {Hkv}")
+
+
+def test_long_context_with_8_kv_heads_sampled_heads():
+    """One 131072-token context (8192 scattered blocks, fp16) with 32 query
+    heads over 8 K/V heads, the benchmark's size and launch: sampled query
+    heads of every group position against the oracle (one K/V head each)."""
+    announce("gqa long context 32/8")
+    w = W.long_context(0, batch=1, device=DEV)
+    w.k_pool = w.k_pool[:, :8].contiguous()
+    w.v_pool = w.v_pool[:, :8].contiguous()
+    torch.cuda.empty_cache()
+    out = _run(w)
+    tables, lens = w.block_tables_np(), w.context_lens_np()
+    for h in (0, 5, 14, 27, 31):  # group positions 0, 1, 2, 3, 3
+        hk = h // 4
+        ref = decode_gqa_ref(w.q[:, h:h + 1].cpu(), w.k_pool[:, hk:hk + 1].cpu(), w.v_pool[:, hk:hk + 1].cpu(),
+                             tables, lens, w.scale, w.block_size)
+        assert_close(out[:, h:h + 1], ref, torch.float16, f"long context gqa head {h}")
+
+
 def test_gqa_agrees_with_mha_on_repeated_kv_heads():
-    """The grouped kernel (tile loads shared by 8 heads) and plain multi-head
-    decode over K/V heads repeated 8 times compute the same attention; their
-    splits differ (rows of 8 heads vs single heads), so they agree within the
-    tolerance, not bit for bit, and both match the oracle."""
+    """The grouped kernel (groups of 8 served 4 heads per tile load) and plain
+    multi-head decode over K/V heads repeated 8 times compute the same
+    attention; their splits differ (rows of 4 heads vs single heads), so they
+    agree within the tolerance, not bit for bit, and both match the oracle."""
     announce("gqa vs repeated-head mha")
     w = _gqa_workload(LENS, 32, 4, 128, 16, torch.float16, 90, poison=False)
     gqa = _run(w)
