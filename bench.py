@@ -192,6 +192,29 @@ def check_graph_replays(g, decode, R: int, out) -> None:
     torch.cuda.synchronize()
 
 
+def copy_ceiling(dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """GB/s of a plain device-to-device copy of nbytes (read + write bytes
+    counted), HIP events around `reps` back-to-back copies: the bandwidth this
+    box's HBM actually delivers to a simple stream, reported beside the
+    nominal peak."""
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (start.elapsed_time(end) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def calibration_copy(pa, dev) -> None:
     """pa_copy_blocks over a known byte count (3 calls of 256 blocks of 128 KiB
     per pool: 64 MiB read and 64 MiB written each), so that counter runs carry
@@ -669,6 +692,7 @@ def main() -> int:
     }
     if cow is not None:
         result["copy_blocks"] = cow
+    result["roofline"]["achievable_copy_GB/s"] = round(copy_ceiling(dev), 1)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s on one host thread")
         host.update({"q": q.cpu(), "tables": w.block_tables_np(), "lens": lens, "scale": w.scale,
