@@ -181,7 +181,11 @@ __global__ __launch_bounds__(kPfWaves* kWave, (DQK > 128 || NT > 1 ? 1 : 2)) voi
   constexpr int kSlices = DV / DVS;
   constexpr int kChunk = 16 * KB;
   constexpr int kGroupRows = kPfRows * NT;
-  constexpr int kMergeBatch = DVS <= 128 ? 4 : 2;  // partials loaded at once while merging (<= 128 VGPRs)
+  // partials loaded at once while merging: 1 + 8*kDq loads each per lane, at
+  // most 60 in all (a wave has at most 63 loads in flight; past that a batch
+  // costs two memory round trips), at most 4 (register budget)
+  constexpr int kMergeBatch = 60 / (1 + 8 * kDq) < 4 ? 60 / (1 + 8 * kDq) : 4;
+  static_assert(kMergeBatch >= 1, "one partial per batch at least");
   constexpr int kThreads = kPfWaves * kWave;
   constexpr int kPer = (kPfMaxSeqs + kThreads - 1) / kThreads;
   __shared__ int s_off[kPfMaxSeqs + 1];  // items of all sequences before s
@@ -950,7 +954,7 @@ __global__ __launch_bounds__(kMlaWaves* kWave, 2) void mla_split_kernel(
     for (int dq = 0; dq < kDq; ++dq)
 #pragma unroll
       for (int k2 = 0; k2 < 16; ++k2) num[dq][k2] = 0.f;
-    constexpr int kB = 4;
+    constexpr int kB = 60 / (1 + 8 * kDq);  // partials per batch: at most 60 loads per lane in flight
     for (int p0 = 0; p0 < parts; p0 += kB) {
       uint64_t pml[kB];
       uint64_t pvv[kB][kDq][8];
