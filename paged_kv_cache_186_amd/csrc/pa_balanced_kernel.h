@@ -76,12 +76,13 @@ constexpr int kUnitLoadsGrouped = PA_UNIT_LOADS_GROUPED;
 // many waves made the split rows' tickets (many waves' atomics on one row
 // counter) and merges (GW heads' partials from each wave) the bulk of the
 // time.  Measured on the layer shape (8 sequences, 32 query heads): with 16
-// and 8 K/V heads, 20.5 -> 17.9 us (GW 2, at least 8 units per wave) and
-// 24.9 -> 23.0 us (GW 4, at least 4); large batches keep every wave busy
-// either way.
+// K/V heads (GW 2) 20.5 us with every wave, 17.9 us with at least 8 units per
+// wave; with 8, 4 or 1 K/V heads (GW 4) at least 2 / 3 / 4 / 6 / 8 / 10 units:
+// 25.7 / 23.9 / 22.1 / 21.2 / 22.9 / 25.1 us (8 K/V heads); large batches
+// keep every wave busy either way.
 template <int GW>
 constexpr long long grouped_min_units() {
-  return GW >= 4 ? 4 : 8;
+  return GW >= 4 ? 6 : 8;
 }
 
 template <typename T, int D, int BS, int GW>
