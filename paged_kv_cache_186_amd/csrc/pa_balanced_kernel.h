@@ -48,11 +48,14 @@ namespace {
 
 constexpr int kWaveMergeBatch = 8;  // partials in flight per lane group while merging
 
-// Cost of one row of `units` units in the balanced split (kBalancedCostUnit,
-// kBalancedCostRow: pa_internal.h).
+// Cost of one row of `units` units in the balanced split, with a row charge
+// RC (kBalancedCostUnit, kBalancedCostRow / kBalancedCostRowWide:
+// pa_internal.h).
 constexpr int kCostUnit = kBalancedCostUnit;
-constexpr int kCostRow = kBalancedCostRow;
-__device__ __forceinline__ int row_cost(int units) { return units > 0 ? kCostRow + kCostUnit * units : 0; }
+template <int RC>
+__device__ __forceinline__ int row_cost(int units) {
+  return units > 0 ? RC + kCostUnit * units : 0;
+}
 
 // One pipeline stage: one tile's K/V, its row's query slice, and its place.
 // A unit is R consecutive rows of one (block, head) tile, at most
@@ -231,6 +234,12 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   constexpr int E = KT::kElems;
   constexpr int kThreads = NW * kWave;
   constexpr int kPer = (kBalancedMaxSeqs + kThreads - 1) / kThreads;  // sequences per thread
+  // the row charge of the cost model: the wide one where a row change folds
+  // more state (grouped heads, or 16 elements per lane over an 8-bit cache);
+  // the host's range bound assumes at most 2 units per block for it, 8 else
+  constexpr int kCostRow = (GW > 1 || KT::kScaled) ? kBalancedCostRowWide : kBalancedCostRow;
+  static_assert(Unit<KT, D, BS, GW>::kPerBlock <= (kCostRow == kBalancedCostRow ? 8 : 2),
+                "units per block within the host's cost bound");
   __shared__ int s_off[kBalancedMaxSeqs + 1];   // units of all sequences before s (per head)
   __shared__ int s_coff[kBalancedMaxSeqs + 1];  // cost of all sequences before s (per head)
   __shared__ int s_len[kBalancedMaxSeqs];
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     const int s = tid * kPer + i;
     nbl[i] = s < S ? (s_len[s] + R - 1) / R : 0;  // units of sequence s (per head)
     mine += nbl[i];
-    mine_c += row_cost(nbl[i]);
+    mine_c += row_cost<kCostRow>(nbl[i]);
   }
   const int incl = wave_prefix_sum(mine);
   const int incl_c = wave_prefix_sum(mine_c);
@@ -291,7 +300,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
       s_coff[s] = run_c;
     }
     run += nbl[i];
-    run_c += row_cost(nbl[i]);
+    run_c += row_cost<kCostRow>(nbl[i]);
   }
   if (tid == 0) {
     s_off[S] = total;
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   auto row_start = [&](int s, int h) __attribute__((always_inline)) {
     const int nb = __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]);
     return static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_coff[s]) +
-           static_cast<long long>(h) * row_cost(nb) + kCostRow;
+           static_cast<long long>(h) * row_cost<kCostRow>(nb) + kCostRow;
   };
   // the first unit whose cost start is >= c: its sequence, head and index in
   // the row, and its place in the unit order (T_all and s = S past the end)
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
         __builtin_amdgcn_ballot_w64(lane < span && static_cast<long long>(H) * s_coff[base + min(lane, span - 1)] <= c);
     s = base + (63 - __builtin_clzll(pass));
     const int nb = __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]);
-    const int rc = row_cost(nb);
+    const int rc = row_cost<kCostRow>(nb);
     const long long local = c - static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_coff[s]);
     h = static_cast<int>(floor_div(local, rc, 1.0 / static_cast<double>(rc)));
     const int o = static_cast<int>(local - static_cast<long long>(h) * rc);  // in [0, rc)

@@ -113,17 +113,28 @@ inline int default_partition_blocks(int num_seqs, int num_heads, int max_blocks,
 // hence the sequence limit.
 constexpr int kBalancedMaxSeqs = 2048;
 // Cost model of the balanced split: a unit costs kBalancedCostUnit, and each
-// row segment a wave walks costs kBalancedCostRow more.  Measured: a row
-// change takes about two thirds of a unit's time (layer-shape and
+// row segment a wave walks costs kBalancedCostRow more for the kernels with
+// one head per load over a 16-bit or fp32 cache, kBalancedCostRowWide for
+// those whose row change folds more state (grouped heads, or 16 elements per
+// lane over an 8-bit cache).  Measured: a row change takes about two thirds
+// of a 4 KiB unit's time (fp16, D = 128; layer-shape and
 // continuous-batching workloads: with the same number of units, a wave that
-// walked six rows took ~2 us longer than one that walked one).
+// walked six rows took ~2 us longer than one that walked one); for the
+// others a charge of 6 was fastest (8-bit layer shape 18.6 / 17.3 /
+// 17.0 / 16.8 us with charges 0 / 2 / 4 / 6; grouped heads on continuous
+// batching 54.0 / 53.1 / 52.9 / 52.2 us), while the 16-bit kernel is best at
+// 2 (153.7 us against 154.5 / 154.8 / 154.0).
 constexpr int kBalancedCostUnit = 3;
 constexpr int kBalancedCostRow = 2;
-// Cost positions stay within int per head and within 2^43 over all rows (a
-// block holds at most 8 units of any balanced kernel).
+constexpr int kBalancedCostRowWide = 6;
+// Cost positions stay within int per head and within 2^43 over all rows.  Per
+// block the cost is at most (unit + row charge) x units per block: up to 8
+// units (fp32, D = 128, BS = 32) at 3 + 2, or up to 2 units (16 or 32 rows)
+// at 3 + 6 — the kernel asserts the units per block.
 inline bool balanced_cost_fits(long long num_seqs, long long rows, long long max_blocks) {
-  constexpr long long kMaxUnitsPerBlock = 8;
-  constexpr long long c = (kBalancedCostUnit + kBalancedCostRow) * kMaxUnitsPerBlock;
+  constexpr long long c8 = (kBalancedCostUnit + kBalancedCostRow) * 8LL;
+  constexpr long long c16 = (kBalancedCostUnit + kBalancedCostRowWide) * 2LL;
+  constexpr long long c = c8 > c16 ? c8 : c16;
   return num_seqs * max_blocks * c < (1LL << 31) && rows * max_blocks * c < (1LL << 43);
 }
 constexpr int kBalancedWaves = PA_BALANCED_WAVES;
