@@ -120,17 +120,18 @@ constexpr int kBalancedMaxSeqs = 2048;
 // of a 4 KiB unit's time (fp16, D = 128; layer-shape and
 // continuous-batching workloads: with the same number of units, a wave that
 // walked six rows took ~2 us longer than one that walked one); for the
-// others a charge of 6 was fastest (8-bit layer shape 18.6 / 17.3 /
-// 17.0 / 16.8 us with charges 0 / 2 / 4 / 6; grouped heads on continuous
-// batching 54.0 / 53.1 / 52.9 / 52.2 us), while the 16-bit kernel is best at
-// 2 (153.7 us against 154.5 / 154.8 / 154.0).
+// others a charge of 10 was fastest (8-bit layer shape 18.6 / 17.3 / 17.0 /
+// 16.8 / 16.5 / 16.5 / 16.5 us with charges 0 / 2 / 4 / 6 / 8 / 10 / 12;
+// grouped layer shape with 8 K/V heads 20.2 / 19.4 / 19.2 / 19.4 us with
+// 6 / 8 / 10 / 12), while the 16-bit kernel is best at 2 (153.7 us against
+// 154.5 / 154.8 / 154.0 with 0 / 4 / 6).
 constexpr int kBalancedCostUnit = 3;
 constexpr int kBalancedCostRow = 2;
-constexpr int kBalancedCostRowWide = 6;
+constexpr int kBalancedCostRowWide = 10;
 // Cost positions stay within int per head and within 2^43 over all rows.  Per
 // block the cost is at most (unit + row charge) x units per block: up to 8
 // units (fp32, D = 128, BS = 32) at 3 + 2, or up to 2 units (16 or 32 rows)
-// at 3 + 6 — the kernel asserts the units per block.
+// at 3 + 10 — the kernel asserts the units per block.
 inline bool balanced_cost_fits(long long num_seqs, long long rows, long long max_blocks) {
   constexpr long long c8 = (kBalancedCostUnit + kBalancedCostRow) * 8LL;
   constexpr long long c16 = (kBalancedCostUnit + kBalancedCostRowWide) * 2LL;
