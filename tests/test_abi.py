@@ -285,8 +285,9 @@ def test_gqa_workspace_rules(lib):
     # balanced split: one row per (sequence, group of query heads a tile load serves)
     mha = lib.pa_decode_workspace_size(8, 32, 128, 128, 16, 0)
     assert lib.pa_decode_gqa_workspace_size(8, 32, 32, 128, 128, 16, 0, F16, F16) == mha
-    g8 = lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 0, F16, F16)   # 8 heads per load
-    g4 = lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 0, F16, E4M3)  # 8-bit: 4 per load
+    # groups of 8: two work rows of 4 heads each, over a 16-bit or an 8-bit cache
+    g8 = lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 0, F16, F16)
+    g4 = lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 0, F16, E4M3)
     assert g8 > 0 and g4 > 0 and g8 % 256 == 0
     assert lib.pa_decode_gqa_workspace_size(8, 32, 3, 128, 128, 16, 0, F16, F16) == 0   # invalid
     assert lib.pa_decode_gqa_workspace_size(8, 32, 4, 128, 128, 16, 0, 9, F16) == 0

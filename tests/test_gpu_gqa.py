@@ -64,7 +64,8 @@ LENS = [0, 1, 900, 2, 0, 333, 17, 2500, 1]
 @pytest.mark.parametrize("H,Hkv", [(32, 4), (32, 1), (16, 4), (8, 4), (12, 4), (8, 8)])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 def test_group_widths_16bit_cache(H, Hkv, dtype):
-    """(32,4) and (32,1): 8 heads per tile load; (16,4): 4; (8,4): 2;
+    """(32,4) and (32,1): groups of 8 and 32, served 4 heads per tile load;
+    (16,4): 4; (8,4): 2;
     (12,4): groups of 3, one head per load; (8,8): plain multi-head."""
     announce(f"gqa H={H} Hkv={Hkv} dtype={dtype}")
     w = _gqa_workload(LENS, H, Hkv, 128, 16, dtype, 50 + H + Hkv)
@@ -165,7 +166,7 @@ def test_gqa_agrees_with_mha_on_repeated_kv_heads():
 def test_one_workspace_serves_grouped_plain_and_partitioned_calls():
     """Every decode call lays out the same counter region for the same
     num_seqs * num_heads, so one zero-filled workspace serves grouped (tile
-    loads shared by 8 heads), partitioned and plain calls in any order, and
+    loads shared by 4 heads), partitioned and plain calls in any order, and
     every call leaves the counters zero."""
     announce("gqa: one workspace for grouped, partitioned and plain calls")
     w = _gqa_workload(LENS, 32, 1, 128, 16, torch.float16, 95)
