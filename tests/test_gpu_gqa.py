@@ -1,8 +1,9 @@
 """GPU parity of grouped-query decode (pa_decode_gqa) against the float64
 oracle (decode_gqa_ref), through the C ABI: every group width the kernels
 build (tile loads shared by 4 or 2 query heads — groups of 8 and more 4 at a
-time — and 1: each head reads its own K/V head), multi-query (one K/V head), 16-bit and 8-bit caches, the
-default split and explicit partitions, ragged NaN-poisoned batches."""
+time — and 1: each head reads its own K/V head), multi-query (one K/V head),
+16-bit and 8-bit caches with fp16 and bf16 queries, the default split and
+explicit partitions, ragged NaN-poisoned batches."""
 
 import numpy as np
 import pytest
@@ -86,6 +87,21 @@ def test_group_widths_8bit_cache(fmt, H, Hkv):
     ref = _oracle(w, kv, fmt)
     for part in (0, 128):
         assert_close(_run(w, kv, part), ref, torch.float16, f"{fmt} H={H} Hkv={Hkv} partition={part}")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("D,bs", [(128, 16), (128, 32), (64, 32)])
+def test_bf16_queries_over_8bit_cache(fmt, D, bs):
+    """bf16 queries and output over an 8-bit cache with groups of 8 (4 heads
+    per tile load); at D = 128 and block 32 this kernel holds part of its
+    state in scratch (the register file is full), which must not change the
+    result."""
+    announce(f"gqa bf16 over {fmt} D={D} bs={bs}")
+    w = _gqa_workload(LENS, 32, 4, D, bs, torch.bfloat16, 75 + D + bs)
+    kv = W.fp8_pools(w, fmt)
+    ref = _oracle(w, kv, fmt)
+    for part in (0, 128):
+        assert_close(_run(w, kv, part), ref, torch.bfloat16, f"bf16 {fmt} D={D} bs={bs} partition={part}")
 
 
 @pytest.mark.parametrize("D,bs", [(64, 16), (64, 32), (128, 32)])
