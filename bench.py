@@ -516,7 +516,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         return 2
 
     import paged_kv_cache_186_amd as pa
