@@ -6,7 +6,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring): only ``tests/``,
 The pages name quantization only as future work (page "mlx-paged-attention:
 Bringing vLLM-level High Throughput Inference to Apple Silicon", future
 plans); they fix no format, no scale granularity and no rounding.  The
-readings taken here (each also listed in the design doc):
+readings taken here:
 
 * formats: the two 8-bit formats of the OCP 8-bit floating point
   specification (OFP8): E4M3 — 4 exponent bits, bias 7, 3 mantissa bits, no

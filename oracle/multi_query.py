@@ -9,8 +9,7 @@ Throughput Inference to Apple Silicon" names speculative decoding as a feature
 vLLM has and the project lacks (comparison with vLLM) and as future work
 (future plans); verifying k drafted tokens — like prefilling a prompt in
 chunks — means attending with several new query tokens of a sequence at once
-over its paged cache.  The pages give no semantics; the readings taken here
-(each also listed in the design doc):
+over its paged cache.  The pages give no semantics; the readings taken here:
 
 * the new tokens are already in the cache: sequence s has context length L_s
   including them, and its Tq_s query tokens are its LAST Tq_s tokens, token i

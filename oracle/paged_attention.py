@@ -11,7 +11,7 @@ first ``ceil(L_s / block_size)`` entries are physical block ids;
 any float storage dtype (float32, float16, bfloat16); values are upcast to
 float64 exactly before any arithmetic.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 
 * softmax scale is an explicit argument (the pages give none);
 * an empty context (L = 0) yields a zero output row;
