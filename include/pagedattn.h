@@ -234,10 +234,18 @@ pa_status_t pa_decode_gqa(void* out, const void* q, const void* k_pool, const vo
  *                 query rows alone would not fill the GPU; otherwise keys per
  *                 partition, a positive multiple of 16.
  *   workspace:    pa_prefill_workspace_size() bytes for the same sizes, 0
- *                 when nothing is split (then workspace may be NULL).  Its
- *                 counters must be zero before the first call; every call
- *                 leaves them zero.  Its layout differs from pa_decode*'s:
- *                 do not hand one workspace to both kinds without zeroing it.
+ *                 when nothing is split (then workspace may be NULL).  It
+ *                 begins with arrival counters that must be zero when a call
+ *                 starts; every call leaves its own counters zero.  How many
+ *                 counters there are depends on every size argument
+ *                 (num_seqs, num_query_tokens, num_heads, num_kv_heads,
+ *                 head_dim, max_blocks_per_seq, block_size, partition_size),
+ *                 and the partials of a call follow its counters, so a call
+ *                 with fewer counters writes partials where a call with more
+ *                 keeps counters: zero the whole workspace again before a
+ *                 call whose sizes differ from those of the previous call
+ *                 that used it.  Its layout differs from pa_decode*'s: do not
+ *                 hand one workspace to both kinds without zeroing it.
  * Device-side contents never cause an access outside the arrays: lengths are
  * clamped to [0, max_blocks_per_seq * block_size], query bounds to
  * [0, num_query_tokens], and a table id outside the pool makes NaN every
@@ -274,7 +282,9 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void*
  *   dtype:    PA_DTYPE_F16 or PA_DTYPE_BF16; block_size 16 or 32.
  * Everything else (tables, lengths, partition_size, workspace from
  * pa_decode_mla_workspace_size(), error behaviour) as for pa_prefill with one
- * query token per sequence.
+ * query token per sequence; in particular zero the workspace again before a
+ * call whose sizes (num_seqs, num_heads, max_blocks_per_seq, block_size,
+ * partition_size) differ from those of the previous call that used it.
  */
 size_t pa_decode_mla_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                     int32_t block_size, int32_t partition_size);

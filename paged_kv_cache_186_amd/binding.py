@@ -61,10 +61,13 @@ MLA_V_DIM = 512
 
 _lib: Optional[ctypes.CDLL] = None
 
-# Zero-filled pa_decode workspaces kept between calls, keyed by (device, stream,
-# num_seqs*num_heads): the library leaves the arrival counters at the start of a
-# workspace at zero after every call, so a cached workspace stays valid for the
-# next call with the same number of rows on the same stream.
+# Zero-filled workspaces kept between calls.  pa_decode*: keyed by (device,
+# stream, num_seqs*num_heads): the library leaves the arrival counters at the
+# start of a workspace at zero after every call and their region depends only
+# on num_seqs*num_heads, so a cached workspace stays valid for the next call
+# with the same number of rows on the same stream.  pa_prefill / pa_decode_mla:
+# keyed by (device, stream, kind), with the sizes of the last call beside it
+# (see _query_workspace).
 _WORKSPACES: dict = {}
 
 
@@ -416,12 +419,34 @@ def pa_prefill_workspace_size(num_seqs: int, num_query_tokens: int, num_heads: i
                                                         partition_size))
 
 
-def _query_call_args(out, q, block_tables, context_lens, partition_size, workspace, stream, need):
+def _query_workspace(device, stream_handle: int, kind: str, sizes: tuple, need: int) -> torch.Tensor:
+    """Cached workspace of pa_prefill / pa_decode_mla for one (device, stream,
+    kind).  Where its arrival counters end depends on every size argument of
+    the call, so a call with other sizes than the previous one could find
+    that call's partials where its own counters sit: the buffer is zeroed
+    (a fill kernel on the call's stream) whenever the sizes change."""
+    key = (torch.device(device).index, stream_handle, kind)
+    entry = _WORKSPACES.get(key)
+    if entry is None or entry[0].numel() < need:
+        _WORKSPACES[key] = (new_workspace(need, device), sizes)
+        return _WORKSPACES[key][0]
+    ws, last = entry
+    if last != sizes:
+        if stream_handle == int(torch.cuda.current_stream(device).cuda_stream):
+            ws.zero_()
+        else:
+            with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
+                ws.zero_()
+        _WORKSPACES[key] = (ws, sizes)
+    return ws
+
+
+def _query_call_args(q, kind, sizes, workspace, stream, need):
     handle = _stream_handle(q.device, stream)
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:   # never shared with the decode calls (another layout)
-            workspace = _cached_workspace(q.device, handle, ("queries", tuple(q.shape)), need)
+            workspace = _query_workspace(q.device, handle, kind, sizes, need)
         _dev(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return ws_ptr, ws_bytes, handle
@@ -456,7 +481,7 @@ def pa_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool:
              "query_start must be int32 [num_seqs + 1]")
     Hkv, W = k_pool.shape[1], block_tables.shape[1]
     need = pa_prefill_workspace_size(S, T, H, Hkv, D, W, block_size, partition_size)
-    ws_ptr, ws_bytes, handle = _query_call_args(out, q, block_tables, context_lens, partition_size,
+    ws_ptr, ws_bytes, handle = _query_call_args(q, "prefill", (S, T, H, Hkv, D, W, block_size, partition_size),
                                                 workspace, stream, need)
     with torch.cuda.device(q.device):
         st = lib.pa_prefill(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
@@ -494,7 +519,7 @@ def pa_decode_mla(out: torch.Tensor, q: torch.Tensor, kv_pool: torch.Tensor, blo
     _require(context_lens.dtype == torch.int32 and context_lens.shape == (S,), "context_lens must be int32 [num_seqs]")
     W = block_tables.shape[1]
     need = pa_decode_mla_workspace_size(S, H, W, block_size, partition_size)
-    ws_ptr, ws_bytes, handle = _query_call_args(out, q, block_tables, context_lens, partition_size,
+    ws_ptr, ws_bytes, handle = _query_call_args(q, "mla", (S, H, W, block_size, partition_size),
                                                 workspace, stream, need)
     with torch.cuda.device(q.device):
         st = lib.pa_decode_mla(out.data_ptr(), q.data_ptr(), kv_pool.data_ptr(), block_tables.data_ptr(),

@@ -95,7 +95,6 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     return p;
   }
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads;
-  const long long tiles = static_cast<long long>(rows) * max_blocks_per_seq;
   if (partition_size == 0 && num_seqs <= pa::kBalancedMaxSeqs &&
       pa::balanced_cost_fits(num_seqs, static_cast<long long>(rows), max_blocks_per_seq)) {
     p.mode = pa::DecodeMode::kBalanced;
