@@ -4,16 +4,21 @@
 A step is the whole hot path over one batch: write each sequence's new token
 into its cache slot (pa_reshape_and_cache), then decode attention over the
 paged cache (pa_decode: block-table gather, scores, softmax, weighted V sum and
-the split-context log-sum-exp merge).  The default workload is the pages'
-layer shape: 8 sequences with context lengths uniform in [1, 2048], 32 heads,
-head_dim 128, block size 16, fp16, a 1024-block pool, blocks popped from a
-shuffled free list (seed 0).
+the split-context log-sum-exp merge).  The default workload is the largest
+decode configuration one GPU holds: 4 sequences of 131072 tokens each, 32
+heads, head_dim 128, block size 16, fp16, 8192 randomly scattered blocks per
+sequence (an 8 GiB K+V pool), under the library's default split.  The same
+run then measures, with fewer steps, the pages' layer shape (8 sequences,
+lengths uniform in [1, 2048]), continuous batching (64 sequences, log-normal
+lengths, block 32), the 128K context at batch 1, and the 4 x 128K batch with
+explicit partitions of 512 tokens (key "configs"); --no-extra skips them.
 
 Timing is cold-cache: the step rotates over enough replicas of the KV pool
 (>= 2 GiB in total) that the 256 MB last-level cache cannot hold the working
-set from one visit to the next.  A warm (no rotation) figure is reported beside
-it.  Inputs are resident in HBM before the timed region; HIP events on the
-stream the kernels run on bracket every kernel call.
+set from one visit to the next (a pool of 2 GiB or more is its own replica).
+Inputs are resident in HBM before the timed region; the steps are replayed
+from HIP graphs and HIP events on the stream the kernels run on bracket
+exactly --steps steps.
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
@@ -145,20 +150,6 @@ def capture(enqueue) -> "torch.cuda.CUDAGraph":
     return g
 
 
-def time_graph(g, n: int, stream) -> float:
-    """Milliseconds per replay of g over n back-to-back replays."""
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    g.replay()
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(n):
-        g.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / n
-
-
 def time_eager(reshape, decode, n: int, stream) -> dict:
     """Per-call HIP events around eager calls (includes host launch overhead)."""
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
@@ -228,35 +219,79 @@ def calibration_copy(pa, dev) -> None:
     del k, v
 
 
-def cpu_baseline(w_host, k_new, v_new, slots, step_bytes: int, seconds: float) -> dict:
-    """The float64 oracle, as it stands, on the host: one thread, same step."""
-    from threadpoolctl import threadpool_limits
-    from oracle import (decode_gqa_ref, decode_ref, dequant_ref, reshape_and_cache_fp8_ref,
-                        reshape_and_cache_ref)
-    torch.set_num_threads(1)
-    lens = w_host["lens"]
-    fmt = w_host["fmt"]
-    times = []
-    t_end = time.perf_counter() + seconds
-    with threadpool_limits(limits=1):
-        while True:
-            t0 = time.perf_counter()
-            dec = decode_gqa_ref if w_host["gqa"] else decode_ref
-            if fmt is None:
-                kp, vp = reshape_and_cache_ref(w_host["k"], w_host["v"], k_new, v_new, slots, w_host["bs"])
-            else:
-                kc, vc = reshape_and_cache_fp8_ref(w_host["k"], w_host["v"], w_host["ks"], w_host["vs"],
-                                                   k_new, v_new, slots, w_host["bs"], fmt)
-                kp, vp = dequant_ref(kc, w_host["ks"], fmt), dequant_ref(vc, w_host["vs"], fmt)
-            dec(w_host["q"], kp, vp, w_host["tables"], lens, w_host["scale"], w_host["bs"])
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() >= t_end and len(times) >= 1:
+def _host_threads() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def _run_rows(fn, rows, threads: int, seconds: float):
+    """Run fn(row) over rows, in batches of `threads` rows on that many host
+    threads, until the rows are done or `seconds` have passed; returns (rows
+    done, elapsed seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    done = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while done < len(rows):
+            batch = rows[done:done + threads]
+            list(ex.map(fn, batch))
+            done += len(batch)
+            if time.perf_counter() - t0 >= seconds:
                 break
-    t = float(np.median(times))
-    return {"value": round(step_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"the full default step (reshape_and_cache + decode) run {len(times)} times "
-                       f"back to back on one host thread, float64 numpy; median {t * 1e3:.1f} ms/step; "
-                       f"host has {len(os.sched_getaffinity(0))} cores available")}
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(w_host, step_bytes: int, seconds: float) -> dict:
+    """The float64 oracle, as it stands, on the host's cores: the decode of
+    the step's (sequence, query head) rows, each row one oracle call on that
+    head's slice of the pools (decode_ref; decode_gqa_ref with its K/V head;
+    decode_fp8_ref on the 8-bit codes), rows in sequence order.  Run once with
+    one host thread per core (BLAS and torch limited to one thread each, rows
+    spread over the threads) and once on a single thread, each for about
+    `seconds` or until every row is done; the rate is the step's algorithmic
+    bytes times the fraction of its context tokens covered, over the time."""
+    from threadpoolctl import threadpool_limits
+    from oracle import decode_fp8_ref, decode_gqa_ref, decode_ref
+    lens, fmt, q = w_host["lens"], w_host["fmt"], w_host["q"]
+    S, H = q.shape[0], q.shape[1]
+    G = H // w_host["k"].shape[1]
+    rows = [(s, h) for s in range(S) for h in range(H)]
+    total_tokens = float(lens.astype(np.int64).sum()) * H
+
+    def row(sh):
+        s, h = sh
+        kv = h // G
+        qa, ta, la = q[s:s + 1, h:h + 1], w_host["tables"][s:s + 1], lens[s:s + 1]
+        k, v = w_host["k"][:, kv:kv + 1], w_host["v"][:, kv:kv + 1]
+        if fmt is not None:
+            decode_fp8_ref(qa, k, v, w_host["ks"][:, kv:kv + 1], w_host["vs"][:, kv:kv + 1], ta, la,
+                           w_host["scale"], w_host["bs"], fmt)
+        elif G > 1:
+            decode_gqa_ref(qa, k, v, ta, la, w_host["scale"], w_host["bs"])
+        else:
+            decode_ref(qa, k, v, ta, la, w_host["scale"], w_host["bs"])
+
+    def rate(n, t):
+        toks = float(sum(int(lens[s]) for s, _ in rows[:n]))
+        return step_bytes * (toks / total_tokens) / t / 1e9, toks
+
+    cores = _host_threads()
+    prev = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with threadpool_limits(limits=1):
+            n_all, t_all = _run_rows(row, rows, cores, seconds)
+            n_one, t_one = _run_rows(row, rows, 1, seconds)
+    finally:
+        torch.set_num_threads(prev)
+    v_all, tok_all = rate(n_all, t_all)
+    v_one, tok_one = rate(n_one, t_one)
+    return {"value": round(v_all, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 numpy oracle over the first {n_all} of the step's {len(rows)} (sequence, head) "
+                       f"rows ({tok_all / total_tokens:.1%} of its context tokens) in {t_all:.1f} s on "
+                       f"{cores} host threads, one row per oracle call; scaled to the step's bytes"),
+            "cores_1": {"value": round(v_one, 4), "unit": "GB/s", "cores": 1,
+                        "sample": (f"the first {n_one} rows ({tok_one / total_tokens:.1%} of the context tokens) "
+                                   f"in {t_one:.1f} s on one host thread")}}
 
 
 HOST_LINK_GBS = 64.0           # PCIe 5.0 x16, per direction (published)
@@ -384,16 +419,15 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
         call(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    graph = capture(lambda: [call(i) for i in range(R)])
+    graphs = capture_steps(call, R, steps)
     call(R - 1)
     torch.cuda.synchronize()
     want = out.clone()
-    graph.replay()
+    graphs[0].replay()
     torch.cuda.synchronize()
     if not torch.equal(out.view(torch.int16), want.view(torch.int16)):
         raise RuntimeError("graph replay differs from the eager call")
-    n_rep = max(1, math.ceil(steps / R))
-    ms = time_graph(graph, n_rep, stream) / R
+    ms = time_steps(graphs, steps, stream)
 
     # algorithmic work: every (query row, visible key) pair once
     e = 2
@@ -418,7 +452,7 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
         "metric": metric,
         "value": round(tflops if mfma_bound else gbs, 2),
         "unit": "TFLOP/s" if mfma_bound else "GB/s",
-        "n_gpus": 1, "steps": n_rep * R, "warmup": warmup, "ms_per_step": round(ms, 5),
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if dtype == torch.float16 else "bf16",
         "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block layout)",
@@ -448,94 +482,113 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
 
 def queries_cpu_baseline(op, pools, q, tables_np, lens, qs_np, scale, bs, H, Hkv, D, Dv, tq, mfma_bound,
                          seconds):
-    """The float64 oracle on a bounded sample: the first sequence's query
-    rows for the first K/V head's query heads (prefill, verify) or the first
-    two sequences (MLA), on one host thread, scaled to the metric's unit."""
+    """The float64 oracle on the host's cores, on a bounded sample: units of
+    work are (sequence, K/V head) pairs for prefill / verify (the sequence's
+    query rows of that K/V head's query heads, one prefill_ref call each) and
+    sequences for MLA (one mla_decode_ref call each), in order.  Run once on
+    one host thread per core (BLAS and torch limited to one thread each) and
+    once on a single thread, each for about `seconds` or until every unit is
+    done; the rate is the work of the units done over the time, in the
+    metric's unit."""
     from threadpoolctl import threadpool_limits
     from oracle import mla_decode_ref, prefill_ref
-    torch.set_num_threads(1)
     G = H // Hkv
+    S = len(lens)
+    qh = q.cpu()
     if op == "mla":
-        n = 2
-        args = (q[:n].cpu(), pools[0].cpu(), tables_np[:n], lens[:n], scale, bs, Dv)
-        fn = mla_decode_ref
-        pairs = int(lens[:n].sum()) * H
-        work = pairs * 2 * (D + Dv) if mfma_bound else int(lens[:n].sum()) * D * 2 + n * H * (D + Dv) * 2
-        sample = f"MLA decode of the first {n} sequences, all {H} heads"
+        pool = pools[0].cpu()
+        units = list(range(S))
+
+        def run(s):
+            mla_decode_ref(qh[s:s + 1], pool, tables_np[s:s + 1], lens[s:s + 1], scale, bs, Dv)
+
+        def work(s):
+            L = int(lens[s])
+            return L * H * 2 * (D + Dv) if mfma_bound else L * D * 2 + H * (D + Dv) * 2
+        what = "sequences (one mla_decode_ref call each, all heads)"
     else:
-        rows = slice(int(qs_np[0]), int(qs_np[1]))
-        kp = pools[0][:, :1].cpu()
-        vp = pools[1][:, :1].cpu()
-        args = (q[rows, :G].cpu(), kp, vp, tables_np[:1], lens[:1], np.array([0, tq], np.int32), scale, bs)
-        fn = prefill_ref
-        L = int(lens[0])
-        pairs = sum(L - tq + i + 1 for i in range(tq)) * G
-        work = pairs * 2 * (D + Dv) if mfma_bound else L * D * 2 * 2 + tq * G * D * 2 * 2
-        sample = f"the first sequence's {tq} query rows for the {G} query heads of K/V head 0"
-    times = []
-    t_end = time.perf_counter() + seconds
-    with threadpool_limits(limits=1):
-        while True:
-            t0 = time.perf_counter()
-            fn(*args)
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() >= t_end:
-                break
-    t = float(np.median(times))
-    return {"value": round(work / t / (1e12 if mfma_bound else 1e9), 6),
-            "unit": "TFLOP/s" if mfma_bound else "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample}, run {len(times)} times on one host thread (float64 numpy), "
-                      f"median {t * 1e3:.1f} ms"}
+        kp, vp = pools[0].cpu(), pools[1].cpu()
+        units = [(s, kvh) for s in range(S) for kvh in range(Hkv)]
+
+        def run(u):
+            s, kvh = u
+            rows = slice(int(qs_np[s]), int(qs_np[s + 1]))
+            n = int(qs_np[s + 1] - qs_np[s])
+            prefill_ref(qh[rows, kvh * G:(kvh + 1) * G], kp[:, kvh:kvh + 1], vp[:, kvh:kvh + 1],
+                        tables_np[s:s + 1], lens[s:s + 1], np.array([0, n], np.int32), scale, bs)
+
+        def work(u):
+            s, _ = u
+            L, n = int(lens[s]), int(qs_np[s + 1] - qs_np[s])
+            pairs = sum(L - n + i + 1 for i in range(n)) * G
+            return pairs * 2 * (D + Dv) if mfma_bound else L * D * 2 * 2 + n * G * D * 2 * 2
+        what = "(sequence, K/V head) pairs (one prefill_ref call each over that head's query rows)"
+    cores = _host_threads()
+    prev = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with threadpool_limits(limits=1):
+            n_all, t_all = _run_rows(run, units, cores, seconds)
+            n_one, t_one = _run_rows(run, units, 1, seconds)
+    finally:
+        torch.set_num_threads(prev)
+    div = 1e12 if mfma_bound else 1e9
+    unit = "TFLOP/s" if mfma_bound else "GB/s"
+    v_all = sum(work(u) for u in units[:n_all]) / t_all / div
+    v_one = sum(work(u) for u in units[:n_one]) / t_one / div
+    return {"value": round(v_all, 6), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"float64 numpy oracle over the first {n_all} of {len(units)} {what}, "
+                      f"{t_all:.1f} s on {cores} host threads",
+            "cores_1": {"value": round(v_one, 6), "unit": unit, "cores": 1,
+                        "sample": f"the first {n_one} units in {t_one:.1f} s on one host thread"}}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="layer_shape",
-                    choices=["layer_shape", "continuous_batching", "shared_prefix",
-                             "long_context_b1", "long_context_b4", "tiny"])
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--kv", default="native", choices=["native", "e4m3", "e5m2"],
-                    help="KV cache element format: the workload's own dtype, or an 8-bit cache "
-                         "(OCP E4M3 / E5M2 with per-block, per-head scales; q and out keep their dtype)")
-    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
-    ap.add_argument("--replicas", type=int, default=0, help="KV pool replicas (0 = enough for 2 GiB)")
-    ap.add_argument("--kv-heads", type=int, default=0,
-                    help="K/V heads (0 = as many as query heads); fewer runs grouped-query decode "
-                         "(pa_decode_gqa) over the first kv-heads heads of the pools")
-    ap.add_argument("--op", default="decode", choices=["decode", "swap", "prefill", "verify", "verify1", "mla"],
-                    help="decode: the decode step (default); swap: pa_swap_blocks over the host link; "
-                         "prefill / verify: pa_prefill on a prompt-chunk / drafted-token workload; "
-                         "mla: pa_decode_mla")
-    ap.add_argument("--heads", type=int, default=0, help="query heads for --op prefill/verify/mla (0 = default)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    args = ap.parse_args()
+def capture_steps(enqueue_step, R: int, K: int):
+    """Graphs for exactly K steps: `full` holds steps 0..R-1 (one per pool
+    replica) and is replayed K // R times, `rest` holds steps 0..K % R - 1
+    (None when K is a multiple of R)."""
+    full = capture(lambda: [enqueue_step(i) for i in range(R)])
+    r = K % R
+    rest = capture(lambda: [enqueue_step(i) for i in range(r)]) if r else None
+    return full, K // R, rest
 
-    if args.gpus != 1:
-        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported "
-              "(the library has no multi-GPU path)", file=sys.stderr)
-        return 2
 
-    import paged_kv_cache_186_amd as pa
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    pa.load_library()
-    stream = torch.cuda.current_stream(dev)
+def time_steps(graphs, K: int, stream) -> float:
+    """Milliseconds per step over exactly K steps: HIP events on the kernels'
+    stream around K // R replays of the R-step graph and one replay of the
+    remainder graph."""
+    full, n_full, rest = graphs
+    full.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n_full):
+        full.replay()
+    if rest is not None:
+        rest.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / K
 
-    if args.op == "swap":
-        print(json.dumps(swap_bench(pa, dev, min(args.steps, 50), min(args.warmup, 5))), flush=True)
-        return 0
-    if args.op in QUERY_OPS:
-        print(json.dumps(queries_bench(pa, dev, args.op, args.steps, min(args.warmup, 10), args.seed, args.heads,
-                                       not args.no_cpu_baseline, args.cpu_seconds, args.partition)), flush=True)
-        return 0
 
+# The headline run also measures these decode configurations (same library
+# defaults, fewer steps) and reports them under "configs": the pages' layer
+# shape, continuous batching, the 128K context at batch 1, and the 4 x 128K
+# batch with explicit partitions of 512 tokens.
+EXTRA_CONFIGS = [("layer_shape", 0), ("continuous_batching", 0), ("long_context_b1", 0),
+                 ("long_context_b4", 512)]
+DEFAULT_WORKLOAD = "long_context_b4"
+
+
+def decode_bench(pa, dev, args, workload: str, partition: int, steps: int, warmup: int,
+                 cpu: bool, full: bool = True) -> dict:
+    """One decode step (pa_reshape_and_cache of each sequence's current token,
+    then pa_decode) on a workload, cold cache, exactly `steps` timed steps."""
     from paged_kv_cache_186_amd import workloads as W
-    log(f"building workload {args.workload} (seed {args.seed})")
-    w = build_workload(args.workload, args.seed, dev)
+    stream = torch.cuda.current_stream(dev)
+    log(f"building workload {workload} (seed {args.seed})")
+    w = build_workload(workload, args.seed, dev)
     Hkv = args.kv_heads or w.num_heads
     gqa = Hkv != w.num_heads
     if gqa:
@@ -549,11 +602,12 @@ def main() -> int:
     if fp8:
         # the 8-bit cache holds the same values, quantized (input generation)
         kc, vc, ks, vs = W.fp8_pools(w, args.kv)
-        if not args.no_cpu_baseline:
-            host = {"k": kc.cpu(), "v": vc.cpu(), "ks": ks.cpu(), "vs": vs.cpu()}
+        if cpu:
+            host = {"k": kc.cpu().view(torch.uint8).numpy(), "v": vc.cpu().view(torch.uint8).numpy(),
+                    "ks": ks.cpu().numpy(), "vs": vs.cpu().numpy()}
         w.k_pool = w.v_pool = None
         torch.cuda.empty_cache()
-    elif not args.no_cpu_baseline:
+    elif cpu:
         host = {"k": w.k_pool.cpu(), "v": w.v_pool.cpu()}
     log(describe(w) + (f", KV cache fp8 {args.kv}" if fp8 else "") + (f", {Hkv} K/V heads" if gqa else ""))
     e = w.q.element_size()
@@ -577,12 +631,13 @@ def main() -> int:
     log(f"pool K+V {pool_bytes / 2**20:.0f} MiB; {R} replica(s) for cold-cache timing")
     reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
     out = torch.empty_like(q)
-    ws_bytes = (pa.pa_decode_gqa_workspace_size(S, H, Hkv, D, w.table_width, bs, args.partition, q.dtype,
+    ws_bytes = (pa.pa_decode_gqa_workspace_size(S, H, Hkv, D, w.table_width, bs, partition, q.dtype,
                                                  base[0].dtype) if gqa
-                else pa.pa_decode_workspace_size(S, H, D, w.table_width, bs, args.partition))
+                else pa.pa_decode_workspace_size(S, H, D, w.table_width, bs, partition))
     ws = pa.new_workspace(ws_bytes, dev)
 
-    calibration_copy(pa, dev)
+    if full:
+        calibration_copy(pa, dev)
 
     def reshape(i):
         if fp8:
@@ -595,49 +650,40 @@ def main() -> int:
             kp, vp = reps[i % R][:2]
             kss, vss = (reps[i % R][2:] if fp8 else (None, None))
             pa.pa_decode_gqa(out, q, kp, vp, tables, clens, w.scale, bs, k_scales=kss, v_scales=vss,
-                             partition_size=args.partition, workspace=ws)
+                             partition_size=partition, workspace=ws)
         elif fp8:
             kp, vp, kss, vss = reps[i % R]
             pa.pa_decode_fp8(out, q, kp, vp, kss, vss, tables, clens, w.scale, bs,
-                             partition_size=args.partition, workspace=ws)
+                             partition_size=partition, workspace=ws)
         else:
             kp, vp = reps[i % R]
             pa.pa_decode(out, q, kp, vp, tables, clens, w.scale, bs,
-                         partition_size=args.partition, workspace=ws)
+                         partition_size=partition, workspace=ws)
 
-    # eager warmup, then HIP graphs: R steps (one per replica) captured once and
-    # replayed, so no host-side launch cost sits inside the timed region
-    log(f"warmup {args.warmup} steps (eager)")
-    for i in range(max(1, args.warmup)):
+    def step(i):
         reshape(i)
         decode(i)
+
+    # eager warmup, then HIP graphs of the steps (one per replica), replayed,
+    # so no host-side launch cost sits inside the timed region
+    log(f"warmup {warmup} steps (eager)")
+    for i in range(max(1, warmup)):
+        step(i)
     torch.cuda.synchronize()
-    eager = time_eager(reshape, decode, min(args.steps, 200), stream)
+    eager = time_eager(reshape, decode, min(steps, 200), stream) if full else None
 
-    step_graph = capture(lambda: [f(i) for i in range(R) for f in (reshape, decode)])
-    decode_graph = capture(lambda: [decode(i) for i in range(R)])
-    warm_graph = capture(lambda: [f(0) for _ in range(R) for f in (reshape, decode)])
-    check_graph_replays(decode_graph, decode, R, out)
+    step_graphs = capture_steps(step, R, steps)
+    decode_graphs = capture_steps(decode, R, steps)
+    check_graph_replays(decode_graphs[0], decode, R, out)
 
-    n_rep = max(1, math.ceil(args.steps / R))
-    log(f"timing {n_rep * R} cold steps ({n_rep} replays of a {R}-step graph)")
-    step_ms = time_graph(step_graph, n_rep, stream) / R
-    dec_ms = time_graph(decode_graph, n_rep, stream) / R
-    log(f"timing {n_rep * R} warm steps")
-    warm_ms = time_graph(warm_graph, n_rep, stream) / R
-    n_steps = n_rep * R
-
-    # the shared-prefix workload's copy-on-write (pa_copy_blocks of the pairs
-    # that made the last shared block private), cold, one call per replica
-    cow = None
-    if getattr(w, "cow_pairs", None) and not fp8 and not gqa:
-        pairs = torch.tensor(w.cow_pairs, dtype=torch.int32, device=dev)
-        cow_graph = capture(lambda: [pa.pa_copy_blocks(*reps[i % R][:2], pairs) for i in range(R)])
-        cow_ms = time_graph(cow_graph, n_rep, stream) / R
-        b_cow = 2 * 2 * len(w.cow_pairs) * bs * Hkv * D * e  # K and V, read + write
-        cow = {"pairs": len(w.cow_pairs), "bytes_per_call": b_cow, "us_per_call": round(cow_ms * 1e3, 3),
-               "GB/s": round(b_cow / (cow_ms * 1e-3) / 1e9, 2),
-               "timing": "HIP graph of one call per pool replica, HIP events around the replays"}
+    log(f"timing {steps} cold steps ({decode_graphs[1]} replays of a {R}-step graph"
+        + (f" and one of {steps % R} steps)" if steps % R else ")"))
+    step_ms = time_steps(step_graphs, steps, stream)
+    dec_ms = time_steps(decode_graphs, steps, stream)
+    warm_ms = None
+    if full and R > 1:
+        log(f"timing {steps} warm steps")
+        warm_ms = time_steps(capture_steps(lambda i: step(0), R, steps), steps, stream)
 
     b_dec = decode_bytes(lens, H, D, e, bs, e_kv, Hkv)
     b_res = reshape_bytes(S, Hkv, D, e, e_kv)
@@ -645,15 +691,39 @@ def main() -> int:
     value = (b_dec + b_res) / step_s / 1e9
     dec_gbs = b_dec / (dec_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
-    traffic = traffic_from_profile(digest, profile_path(args.workload, args.kv, Hkv if gqa else 0))
+    tag = workload + (f"_p{partition}" if partition else "")
+    traffic = traffic_from_profile(digest, profile_path(tag, args.kv, Hkv if gqa else 0))
+    split = "balanced (partition_size 0)" if partition == 0 else f"partitions of {partition} tokens"
+    cache = (f"cold: rotates {R} pool replicas ({R * pool_bytes / 2**30:.2f} GiB)" if R > 1 else
+             f"cold: the {pool_bytes / 2**30:.2f} GiB pool exceeds the 256 MB last-level cache")
+
+    if not full:
+        return {"workload": describe(w), "split": split, "steps": steps,
+                "us_per_step": round(step_ms * 1e3, 3), "value": round(value, 2), "unit": "GB/s",
+                "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+                "pa_decode_us": round(dec_ms * 1e3, 3), "pa_decode_bytes": b_dec,
+                "roofline_frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "cache": cache}
+
+    # the shared-prefix workload's copy-on-write (pa_copy_blocks of the pairs
+    # that made the last shared block private), cold, one call per replica
+    cow = None
+    if getattr(w, "cow_pairs", None) and not fp8 and not gqa:
+        pairs = torch.tensor(w.cow_pairs, dtype=torch.int32, device=dev)
+        cow_ms = time_steps(capture_steps(lambda i: pa.pa_copy_blocks(*reps[i % R][:2], pairs), R, steps),
+                            steps, stream)
+        b_cow = 2 * 2 * len(w.cow_pairs) * bs * Hkv * D * e  # K and V, read + write
+        cow = {"pairs": len(w.cow_pairs), "bytes_per_call": b_cow, "us_per_call": round(cow_ms * 1e3, 3),
+               "GB/s": round(b_cow / (cow_ms * 1e-3) / 1e9, 2),
+               "timing": "HIP graph of one call per pool replica, HIP events around the replays"}
 
     result = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": n_steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(step_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -668,11 +738,10 @@ def main() -> int:
             "context_tokens": int(lens.sum()),
             "kv_cache": "native" if not fp8 else f"fp8 {args.kv} + fp32 scale per (block, head)",
             "kv_heads": Hkv,
-            "split": ("balanced (partition_size 0)" if args.partition == 0
-                      else f"partitions of {args.partition} tokens"),
+            "split": split,
             "accumulate": "f32",
-            "cache": f"cold: rotates {R} pool replicas ({R * pool_bytes / 2**30:.2f} GiB)",
-            "timing": "HIP graph replays of R steps, HIP events around the replays",
+            "cache": cache,
+            "timing": "HIP graph replays of the steps, HIP events around the replays",
             "parallelism": "none (1 GPU)",
         },
         "us_per_step": round(step_ms * 1e3, 3),
@@ -682,23 +751,87 @@ def main() -> int:
         "kernels_us": {"pa_decode": round(dec_ms * 1e3, 3),
                        "pa_reshape_and_cache_and_gaps": round((step_ms - dec_ms) * 1e3, 3)},
         "eager_us": {k: round(v * 1e3, 3) for k, v in eager.items()},
-        "warm": {"value": round((b_dec + b_res) / (warm_ms * 1e-3) / 1e9, 2),
-                 "us_per_step": round(warm_ms * 1e3, 3),
-                 "note": "no replica rotation: the working set can sit in the last-level cache"},
         "roofline": {"bound": "hbm", "kernel": "pa_decode (one kernel launch per call)",
                      "achieved": round(dec_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel_source_sha": digest},
     }
+    if warm_ms is not None:
+        result["warm"] = {"value": round((b_dec + b_res) / (warm_ms * 1e-3) / 1e9, 2),
+                          "us_per_step": round(warm_ms * 1e3, 3),
+                          "note": "no replica rotation: the working set can sit in the last-level cache"}
     if cow is not None:
         result["copy_blocks"] = cow
+    del reps, base, ws
+    w.k_pool = w.v_pool = None
+    torch.cuda.empty_cache()
     result["roofline"]["achievable_copy_GB/s"] = round(copy_ceiling(dev), 1)
-    if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s on one host thread")
+    if cpu:
+        log(f"cpu baseline: oracle for ~{args.cpu_seconds:.0f} s on all host cores, then on one thread")
         host.update({"q": q.cpu(), "tables": w.block_tables_np(), "lens": lens, "scale": w.scale,
-                     "bs": bs, "fmt": args.kv if fp8 else None, "gqa": gqa})
-        result["cpu_baseline"] = cpu_baseline(host, k_new.cpu(), v_new.cpu(), slots,
-                                              b_dec + b_res, args.cpu_seconds)
+                     "bs": bs, "fmt": args.kv if fp8 else None})
+        result["cpu_baseline"] = cpu_baseline(host, b_dec + b_res, args.cpu_seconds)
+        del host
+    return result
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=["layer_shape", "continuous_batching", "shared_prefix",
+                             "long_context_b1", "long_context_b4", "tiny"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kv", default="native", choices=["native", "e4m3", "e5m2"],
+                    help="KV cache element format: the workload's own dtype, or an 8-bit cache "
+                         "(OCP E4M3 / E5M2 with per-block, per-head scales; q and out keep their dtype)")
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library default)")
+    ap.add_argument("--replicas", type=int, default=0, help="KV pool replicas (0 = enough for 2 GiB)")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="K/V heads (0 = as many as query heads); fewer runs grouped-query decode "
+                         "(pa_decode_gqa) over the first kv-heads heads of the pools")
+    ap.add_argument("--op", default="decode", choices=["decode", "swap", "prefill", "verify", "verify1", "mla"],
+                    help="decode: the decode step (default); swap: pa_swap_blocks over the host link; "
+                         "prefill / verify: pa_prefill on a prompt-chunk / drafted-token workload; "
+                         "mla: pa_decode_mla")
+    ap.add_argument("--heads", type=int, default=0, help="query heads for --op prefill/verify/mla (0 = default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="measure only --workload (the default run also measures the other decode configs)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import paged_kv_cache_186_amd as pa
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.load_library()
+
+    if args.op == "swap":
+        print(json.dumps(swap_bench(pa, dev, min(args.steps, 50), min(args.warmup, 5))), flush=True)
+        return 0
+    if args.op in QUERY_OPS:
+        print(json.dumps(queries_bench(pa, dev, args.op, args.steps, min(args.warmup, 10), args.seed, args.heads,
+                                       not args.no_cpu_baseline, args.cpu_seconds, args.partition)), flush=True)
+        return 0
+
+    result = decode_bench(pa, dev, args, args.workload, args.partition, args.steps, args.warmup,
+                          not args.no_cpu_baseline)
+    extras = (not args.no_extra and args.workload == DEFAULT_WORKLOAD and args.partition == 0
+              and args.kv == "native" and not args.kv_heads)
+    if extras:
+        result["configs"] = {}
+        for name, part in EXTRA_CONFIGS:
+            key = name + (f"_partitions_{part}" if part else "")
+            result["configs"][key] = decode_bench(pa, dev, args, name, part, min(args.steps, 200),
+                                                  min(args.warmup, 10), False, full=False)
+            torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
     return 0
 

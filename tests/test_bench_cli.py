@@ -18,3 +18,20 @@ def test_more_than_one_gpu_is_refused(n):
     assert r.returncode == 2
     assert "single GPU" in r.stderr and f"--gpus {n}" in r.stderr
     assert r.stdout == ""
+
+
+def test_cpu_baseline_reports_all_cores_and_one_thread():
+    """The host baseline runs the oracle on every host core and on one thread
+    (tiny workload, host tensors only) and reports both."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from paged_kv_cache_186_amd import workloads as W
+    w = W.tiny(0, poison=False)
+    lens = w.context_lens_np()
+    host = {"k": w.k_pool, "v": w.v_pool, "q": w.q, "tables": w.block_tables_np(), "lens": lens,
+            "scale": w.scale, "bs": w.block_size, "fmt": None}
+    b = bench.decode_bytes(lens, w.num_heads, w.head_dim, 4, w.block_size)
+    r = bench.cpu_baseline(host, b, 0.5)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert r["cores"] == len(os.sched_getaffinity(0)) and r["value"] > 0
+    assert r["cores_1"]["cores"] == 1 and r["cores_1"]["value"] > 0
