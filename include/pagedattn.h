@@ -5,7 +5,8 @@
  * tensor data is DEVICE memory owned by the caller; the library allocates
  * nothing and holds no handle (the only thing carried from one call to the
  * next is the all-zero state of the arrival counters in the caller's decode
- * workspace, see pa_decode_workspace_size).  All work is
+ * workspace, see pa_decode_workspace_size; pa_decode_noalloc keeps its own
+ * in a static device array instead).  All work is
  * enqueued asynchronously on the given stream (a hipStream_t passed as void*;
  * NULL means the default stream).
  *
@@ -72,7 +73,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1, /* null pointer, misaligned pointer, bad size, bad scale */
   PA_ERR_UNSUPPORTED = 2, /* head_dim, block_size or dtype outside what is built */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than pa_decode_workspace_size() */
-  PA_ERR_HIP = 4          /* the HIP runtime refused the launch */
+  PA_ERR_HIP = 4,         /* the HIP runtime refused the launch */
+  PA_ERR_TOO_LARGE = 5    /* pa_decode_noalloc: the call exceeds its static scratch */
 } pa_status_t;
 
 /* Version of this ABI; bumped on any incompatible change. */
@@ -142,6 +144,35 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
                       int32_t num_blocks, int32_t max_blocks_per_seq,
                       int32_t partition_size, pa_dtype_t dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (minus workspace and
+ * workspace_bytes), semantics, kernels and results as pa_decode with the same
+ * sizes and partition_size.  The arrival counters and partials live in a
+ * static device array of the library, PA_NOALLOC_SCRATCH_BYTES (32 MiB) per
+ * GPU, which each GPU the library runs this call on holds until the process
+ * ends; the call itself allocates nothing (no hipMalloc, no allocating
+ * library routine).  Its first 4*PA_NOALLOC_MAX_ROWS bytes hold the counters
+ * of every call (cleared by a fill kernel on `stream` before the first call
+ * on a device; every call leaves them zero), the partials follow.
+ * Limits: num_seqs*num_heads <= PA_NOALLOC_MAX_ROWS and a partial area that
+ * fits the rest of the array — e.g. 4 x 131072 tokens x 32 heads at
+ * head_dim 128 fits with the default split (~0.6 MB of partials) and with
+ * partitions of 512 tokens (~17 MB); otherwise PA_ERR_TOO_LARGE and nothing
+ * is launched.  Every call on one GPU shares that GPU's array: calls that
+ * may overlap in time on one GPU (other streams, other host threads) race
+ * and give wrong results; serialise them.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define PA_NOALLOC_MAX_ROWS 262144
+pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, int32_t block_size,
+                              int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t partition_size, pa_dtype_t dtype, void* stream);
 
 /*
  * Write each new token's K and V (all heads) into its cache slot:

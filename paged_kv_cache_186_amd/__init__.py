@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     pa_decode_gqa_workspace_size,
     pa_decode_mla,
     pa_decode_mla_workspace_size,
+    pa_decode_noalloc,
     pa_decode_workspace_size,
     pa_prefill,
     pa_prefill_workspace_size,

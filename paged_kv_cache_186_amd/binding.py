@@ -25,7 +25,7 @@ LIB_PATH = os.environ.get("PAGEDATTN_LIBRARY") or os.path.join(
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            "include", "pagedattn.h")
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_TOO_LARGE = range(6)
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 # 8-bit KV-cache element formats (OCP E4M3 / E5M2), held in torch's float8 dtypes
 FP8_CODES = {torch.float8_e4m3fn: 3, torch.float8_e5m2: 4}
@@ -38,6 +38,7 @@ _SIGNATURES = {
     "pa_decode_workspace_size": (_c_size, [_c_int] * 6),
     "pa_decode": (_c_int, [_c_void] * 6 + [_c_float] + [_c_int] * 6 + [_c_int, _c_int]
                   + [_c_void, _c_size, _c_void]),
+    "pa_decode_noalloc": (_c_int, [_c_void] * 6 + [_c_float] + [_c_int] * 6 + [_c_int, _c_int, _c_void]),
     "pa_reshape_and_cache": (_c_int, [_c_void] * 5 + [_c_int] * 5 + [_c_int, _c_void]),
     "pa_copy_blocks": (_c_int, [_c_void] * 3 + [_c_int] * 5 + [_c_int, _c_void]),
     "pa_decode_fp8": (_c_int, [_c_void] * 8 + [_c_float] + [_c_int] * 6 + [_c_int] * 3
@@ -203,6 +204,27 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
                            block_size, S, H, D, k_pool.shape[0], W, partition_size,
                            DTYPE_CODES[q.dtype], ws_ptr, ws_bytes, handle)
     _check("pa_decode", st)
+    return out
+
+
+def pa_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      block_size: int, *, partition_size: int = 0, stream=None) -> torch.Tensor:
+    """pa_decode without a workspace: the library's static per-GPU scratch
+    holds the partials (for callers that cannot allocate).  Calls that may
+    overlap in time on one GPU race on that scratch."""
+    lib = load_library()
+    S, H, D, W, _, _, handle = _decode_args(
+        out, q, k_pool, v_pool, block_tables, context_lens, block_size, partition_size,
+        None, stream, need_fn=lambda *a: 0)
+    _require(k_pool.shape[1] == H, "k_pool must have as many heads as q")
+    _require(k_pool.dtype == q.dtype, "q, k_pool, v_pool share one dtype")
+    with torch.cuda.device(q.device):
+        st = lib.pa_decode_noalloc(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                   block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+                                   block_size, S, H, D, k_pool.shape[0], W, partition_size,
+                                   DTYPE_CODES[q.dtype], handle)
+    _check("pa_decode_noalloc", st)
     return out
 
 

@@ -1,11 +1,13 @@
 // C ABI of libpagedattn: argument validation, sizing and dispatch.
 //
 // Every check here runs on the host before anything is enqueued; a failed
-// check returns a status and launches nothing.  No allocation, no state.
+// check returns a status and launches nothing.  No allocation; the only state
+// is the per-device address of pa_decode_noalloc's static scratch array.
 
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pa_internal.h"
 #include "pagedattn.h"
@@ -52,6 +54,8 @@ struct DecodePlan {
   int max_parts;
   int workgroups;
   int group_width;
+  size_t rows;   // arrival counters: one per (sequence, query head)
+  size_t slots;  // partial slots (each of head_dim fp32 sums and a (max, sum) pair)
   pa::WorkspaceLayout ws;
 };
 
@@ -79,7 +83,7 @@ int group_width(int num_heads, int num_kv_heads, pa_dtype_t dtype, pa_dtype_t kv
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                        int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                        int32_t partition_size, pa_dtype_t dtype, pa_dtype_t kv_dtype) {
-  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, 1, {0, 0, 0, 0}};
+  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, 1, 0, 0, {0, 0, 0, 0}};
   if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0 || num_kv_heads <= 0 ||
       num_heads % num_kv_heads != 0) {
     p.status = PA_ERR_INVALID_ARG;
@@ -108,7 +112,9 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     // every call with the same num_seqs * num_heads lays the workspace out
     // with its partials after the same counter region: calls of different
     // kinds can share one workspace without a partial landing on a counter
-    p.ws = pa::workspace_layout(rows, slots * p.group_width, head_dim);
+    p.rows = rows;
+    p.slots = slots * p.group_width;
+    p.ws = pa::workspace_layout(rows, p.slots, head_dim);
     return p;
   }
   p.part_blocks =
@@ -123,8 +129,76 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     return p;
   }
   const size_t slots = p.max_parts > 1 ? rows * p.max_parts : 0;
+  p.rows = rows;
+  p.slots = slots;
   p.ws = pa::workspace_layout(rows, slots, head_dim);
   return p;
+}
+
+// ---- static scratch of pa_decode_noalloc -----------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the partials and arrival counters live in this file-scope device
+// array instead of a caller workspace.  Each GPU holds its own copy of it for
+// the life of the process.  Its first kStaticCounterBytes hold the counters
+// of every call at a fixed place, so the partials of one call never land on
+// another call's counters; every call leaves its counters zero.
+constexpr size_t kStaticScratchBytes = size_t(PA_NOALLOC_SCRATCH_BYTES);
+constexpr size_t kStaticMaxRows = size_t(PA_NOALLOC_MAX_ROWS);
+constexpr size_t kStaticCounterBytes = kStaticMaxRows * sizeof(uint32_t);
+static_assert(kStaticCounterBytes % 256 == 0, "counter region keeps the partials 256-byte aligned");
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` on each GPU, once set up
+
+__global__ void zero_words_kernel(uint4* p, size_t n16) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Counter region fixed at the start, partials after it; total 0 when the
+// call does not fit.
+pa::WorkspaceLayout static_scratch_layout(size_t rows, size_t slots, int head_dim) {
+  pa::WorkspaceLayout w{0, 0, 0, 0};
+  if (rows > kStaticMaxRows) return w;
+  const size_t ml = kStaticCounterBytes;
+  const size_t acc = pa::align_up(ml + slots * 2 * sizeof(float), 256);
+  const size_t total = pa::align_up(acc + slots * static_cast<size_t>(head_dim) * sizeof(float), 256);
+  if (total > kStaticScratchBytes) return w;
+  w.counter_offset = 0;
+  w.ml_offset = ml;
+  w.acc_offset = acc;
+  w.total = total;
+  return w;
+}
+
+// The current device's address of `scratch`.  On the first call on a device
+// the address is looked up with hipGetSymbolAddress and the counter region is
+// cleared by a fill kernel on `stream` (ordered before the decode that
+// follows on the same stream).
+pa_status_t static_scratch_ready(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return PA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return PA_ERR_HIP;
+    }
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, stream,
+                       static_cast<uint4*>(ptr), kStaticCounterBytes / sizeof(uint4));
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
 }
 
 // Shared by pa_decode (kv_dtype == dtype, no scales) and pa_decode_fp8; the
@@ -136,11 +210,16 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void
                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                         int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
                         pa_dtype_t kv_dtype, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, bool static_scratch = false) {
   const DecodePlan plan = plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
                                       max_blocks_per_seq, block_size, partition_size, dtype,
                                       kv_dtype);
   if (plan.status != PA_OK) return plan.status;
+  pa::WorkspaceLayout layout = plan.ws;
+  if (static_scratch && plan.ws.total > 0) {
+    layout = static_scratch_layout(plan.rows, plan.slots, head_dim);
+    if (layout.total == 0) return PA_ERR_TOO_LARGE;
+  }
   if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
@@ -150,8 +229,15 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_INVALID_ARG;
-  if (plan.ws.total > 0) {
-    if (!workspace || workspace_bytes < plan.ws.total) return PA_ERR_WORKSPACE;
+  if (static_scratch && plan.ws.total > 0) {
+    void* scratch_ptr = nullptr;
+    const pa_status_t st = static_scratch_ready(static_cast<hipStream_t>(stream), &scratch_ptr);
+    if (st != PA_OK) return st;
+    workspace = scratch_ptr;
+    workspace_bytes = kStaticScratchBytes;
+  }
+  if (layout.total > 0) {
+    if (!workspace || workspace_bytes < layout.total) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
   }
 
@@ -179,11 +265,11 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void
   a.partition_blocks = plan.part_blocks;
   a.max_partitions = plan.max_parts;
   a.workgroups = plan.workgroups;
-  if (plan.ws.total > 0) {
+  if (layout.total > 0) {
     char* ws = static_cast<char*>(workspace);
-    a.counters = reinterpret_cast<uint32_t*>(ws + plan.ws.counter_offset);
-    a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
-    a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
+    a.counters = reinterpret_cast<uint32_t*>(ws + layout.counter_offset);
+    a.ws_ml = reinterpret_cast<float*>(ws + layout.ml_offset);
+    a.ws_acc = reinterpret_cast<float*>(ws + layout.acc_offset);
   }
   const hipError_t e = plan.mode == pa::DecodeMode::kBalanced
                            ? pa::launch_decode_balanced(a, static_cast<hipStream_t>(stream))
@@ -419,6 +505,9 @@ const char* pa_status_string(pa_status_t status) {
       return "PA_ERR_WORKSPACE: workspace missing or smaller than pa_decode_workspace_size()";
     case PA_ERR_HIP:
       return "PA_ERR_HIP: the HIP runtime rejected a kernel launch";
+    case PA_ERR_TOO_LARGE:
+      return "PA_ERR_TOO_LARGE: pa_decode_noalloc needs more than its static scratch holds "
+             "(PA_NOALLOC_MAX_ROWS (sequence, head) rows, PA_NOALLOC_SCRATCH_BYTES bytes)";
     default:
       return "unknown pa_status_t";
   }
@@ -453,6 +542,19 @@ pa_status_t pa_decode(void* out, const void* q, const void* k_pool, const void* 
                      block_size, num_seqs, num_heads, num_heads, head_dim, num_blocks,
                      max_blocks_per_seq, partition_size, dtype, dtype, workspace, workspace_bytes,
                      stream);
+}
+
+pa_status_t pa_decode_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, int32_t block_size, int32_t num_seqs,
+                              int32_t num_heads, int32_t head_dim, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t partition_size,
+                              pa_dtype_t dtype, void* stream) {
+  if (elem_bytes(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  return decode_impl(out, q, k_pool, v_pool, nullptr, nullptr, block_tables, context_lens, scale,
+                     block_size, num_seqs, num_heads, num_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, partition_size, dtype, dtype, nullptr, 0, stream,
+                     /*static_scratch=*/true);
 }
 
 pa_status_t pa_decode_fp8(void* out, const void* q, const void* k_pool, const void* v_pool,

@@ -29,7 +29,7 @@ def test_every_declared_function_is_exported(lib):
                              "pa_decode_fp8", "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8",
                              "pa_swap_blocks", "pa_decode_gqa", "pa_decode_gqa_workspace_size",
                              "pa_prefill", "pa_prefill_workspace_size", "pa_decode_mla",
-                             "pa_decode_mla_workspace_size"}
+                             "pa_decode_mla_workspace_size", "pa_decode_noalloc"}
     raw = ctypes.CDLL(B.LIB_PATH)
     for name in declared:
         assert hasattr(raw, name), name
@@ -38,7 +38,7 @@ def test_every_declared_function_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.pa_abi_version() == 3
-    for st in range(5):
+    for st in range(6):
         s = B.status_string(st)
         assert s.startswith("PA_")
     assert "unknown" in B.status_string(99)
@@ -362,3 +362,32 @@ def _mla(lib, **kw):
 ])
 def test_decode_mla_rejects_before_launch(lib, kw, status):
     assert _mla(lib, **kw) == status
+
+
+def _noalloc(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, scale=0.125, bs=16, S=4, H=4,
+             D=64, N=16, W=3, P=0, dt=0)
+    a.update(kw)
+    return lib.pa_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["scale"], a["bs"],
+                                 a["S"], a["H"], a["D"], a["N"], a["W"], a["P"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), UNSUPPORTED),
+    (dict(dt=3), UNSUPPORTED),             # 8-bit caches go through pa_decode_fp8
+    (dict(S=-1), INVALID),
+    (dict(P=24), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(out=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(q=MISALIGNED), INVALID),
+    # beyond the static scratch: more (sequence, head) rows than its counter
+    # region holds, or partials that do not fit its 32 MiB
+    (dict(S=2048, H=200, W=64, P=16), B.PA_ERR_TOO_LARGE),
+    (dict(S=64, H=32, D=128, W=8192, P=16), B.PA_ERR_TOO_LARGE),
+    (dict(S=0, out=None, q=None, k=None, v=None, bt=None, cl=None), OK),   # no-op
+])
+def test_noalloc_rejects_before_launch(lib, kw, status):
+    """pa_decode_noalloc checks everything on the host before it touches the
+    GPU (its static scratch is set up only after every check passed)."""
+    assert _noalloc(lib, **kw) == status
