@@ -21,24 +21,25 @@
 // of the grid in turn; each workgroup rebuilds the per-sequence item offsets
 // in LDS from context_lens and query_start.
 //
-// One 16-token chunk of one item, per wave:
-//   S^T = K Q^T   with v_mfma_f32_16x16x32_{f16,bf16}: A = 16 keys x 32
-//                 head elements (lane l: key l%16, elements 8*(l/16)..+7 of
-//                 the slice — four lanes read 64 contiguous bytes of a key
-//                 row), B = the same elements of the 16 query rows;
-//                 the result gives lane l the scores of keys 4*(l/16)+i,
-//                 i < 4, for query row l%16;
-//   softmax       per query row: the lane's four scores, then across the
-//                 four lanes of the row (two cross-lane maxima); the running
-//                 sum stays a per-lane partial until the end;
-//   O^T += V^T P^T with v_mfma_f32_16x16x16_{f16,bf16}: B = the
-//                 probabilities exactly as the scores came out (lane l: keys
-//                 4*(l/16)+i of row l%16, rounded to the 16-bit type), A =
-//                 V transposed — lane l reads 8 bytes (4 elements) of each of
-//                 its 4 keys, 16 lanes cover a 128-byte line, and byte
-//                 permutes regroup the elements by column; the column labels
-//                 of the 4 products of a 64-element slice are chosen so that
-//                 lane l ends with 16 consecutive output elements of row l%16.
+// One 32-key chunk (two 16-key blocks) of one item, per wave:
+//   S^T = K Q^T   per block, with v_mfma_f32_16x16x32_{f16,bf16}: A = 16 keys
+//                 x 32 head elements (lane l: key l%16, elements 8*(l/16)..+7
+//                 of the slice — four lanes read 64 contiguous bytes of a key
+//                 row), B = the same elements of the 16 query rows; the
+//                 result gives lane l the scores of keys 4*(l/16)+i, i < 4,
+//                 of each block for query row l%16;
+//   softmax       per query row: the lane's eight scores, then across the
+//                 four lanes of the row (two cross-lane maxima);
+//   O^T += V^T P^T with v_mfma_f32_16x16x32_{f16,bf16} over the chunk's 32
+//                 keys: B = the probabilities exactly as the scores came out
+//                 (lane l: keys 4*(l/16)+i of both blocks for row l%16,
+//                 rounded to the 16-bit type), A = V transposed — lane l
+//                 reads 8 bytes (4 elements) of each of its 8 keys, 16 lanes
+//                 cover a 128-byte line, and byte permutes regroup the
+//                 elements by column; the column labels of the 4 products of
+//                 a 64-element slice are chosen so that lane l ends with 16
+//                 consecutive output elements of row l%16.  The row sums are
+//                 one more such product with every value 1.
 // Two chunks are in flight (loads of the next chunk are issued before the
 // current one is consumed).  Masked keys (after a row's position, or past the
 // context in the last block) get probability 0 by selection, and V rows past
