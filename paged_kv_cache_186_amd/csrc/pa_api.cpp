@@ -56,8 +56,34 @@ struct DecodePlan {
   int group_width;
   size_t rows;   // arrival counters: one per (sequence, query head)
   size_t slots;  // partial slots (each of head_dim fp32 sums and a (max, sum) pair)
+  int max_items;     // kMfma: items the workspace holds
+  int mfma_slots;    // kMfma: workgroups resident at once
+  size_t off_offset; // kMfma: byte offset of the item offsets in the workspace
   pa::WorkspaceLayout ws;
 };
+
+// Compute units of the current device (256 on an MI355X), asked once per
+// device; 256 if HIP cannot tell (the sizes then stay valid, only the
+// partition choice of the grouped-query kernel is less tuned).
+int cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 // Query heads that one K/V tile load serves in the balanced kernel: 4 or 2,
 // the largest dividing the group size, for 16-bit queries; 1 otherwise.  A
@@ -83,7 +109,7 @@ int group_width(int num_heads, int num_kv_heads, pa_dtype_t dtype, pa_dtype_t kv
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                        int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                        int32_t partition_size, pa_dtype_t dtype, pa_dtype_t kv_dtype) {
-  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, 1, 0, 0, {0, 0, 0, 0}};
+  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, 1, 0, 0, 0, 0, 0, {0, 0, 0, 0}};
   if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0 || num_kv_heads <= 0 ||
       num_heads % num_kv_heads != 0) {
     p.status = PA_ERR_INVALID_ARG;
@@ -99,6 +125,37 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     return p;
   }
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads;
+  const int group = num_heads / num_kv_heads;
+  if (partition_size == 0 && num_seqs <= pa::kBalancedMaxSeqs && group >= pa::kMfmaMinGroup &&
+      group <= pa::kMfmaMaxGroup && (dtype == PA_DTYPE_F16 || dtype == PA_DTYPE_BF16) && kv_dtype == dtype) {
+    // the group's heads as the rows of matrix-core tiles; items (sequence,
+    // K/V head, partition), the partition (>= 128 tokens) chosen on the device
+    p.mode = pa::DecodeMode::kMfma;
+    const long long ctx = static_cast<long long>(max_blocks_per_seq) * block_size;
+    const long long parts = (ctx + pa::kMfmaMinPartTokens - 1) / pa::kMfmaMinPartTokens;
+    const long long items = static_cast<long long>(num_seqs) * num_kv_heads * parts;
+    if (items > INT_MAX / pa::kMfmaMaxGroup) {
+      p.status = PA_ERR_INVALID_ARG;
+      return p;
+    }
+    p.max_items = static_cast<int>(items);
+    // grid: the items of the partition the kernel would pick if every
+    // sequence filled the table (more items: workgroups take several)
+    p.mfma_slots = cu_count() * pa::mfma_wg_per_cu(group);
+    const long long per_slot = static_cast<long long>(num_seqs) * num_kv_heads * ctx / p.mfma_slots;
+    int pt = pa::kMfmaMaxPartTokens;
+    while (pt > pa::kMfmaMinPartTokens && pt > per_slot) pt /= 2;
+    const long long grid = static_cast<long long>(num_seqs) * num_kv_heads * ((ctx + pt - 1) / pt);
+    p.workgroups = static_cast<int>(grid < 1 ? 1 : (grid > pa::kMfmaMaxWorkgroups ? pa::kMfmaMaxWorkgroups : grid));
+    p.rows = rows;
+    if (ctx > pa::kMfmaMinPartTokens) {  // a row can span several partitions
+      p.slots = static_cast<size_t>(items) * group;
+      p.ws = pa::workspace_layout(rows, p.slots, head_dim);
+      p.off_offset = p.ws.total;
+      p.ws.total = pa::align_up(p.ws.total + (static_cast<size_t>(num_seqs) + 2) * sizeof(int), 256);
+    }
+    return p;
+  }
   if (partition_size == 0 && num_seqs <= pa::kBalancedMaxSeqs &&
       pa::balanced_cost_fits(num_seqs, static_cast<long long>(rows), max_blocks_per_seq)) {
     p.mode = pa::DecodeMode::kBalanced;
@@ -265,15 +322,19 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void
   a.partition_blocks = plan.part_blocks;
   a.max_partitions = plan.max_parts;
   a.workgroups = plan.workgroups;
+  a.max_items = plan.max_items;
+  a.mfma_slots = plan.mfma_slots;
   if (layout.total > 0) {
     char* ws = static_cast<char*>(workspace);
     a.counters = reinterpret_cast<uint32_t*>(ws + layout.counter_offset);
     a.ws_ml = reinterpret_cast<float*>(ws + layout.ml_offset);
     a.ws_acc = reinterpret_cast<float*>(ws + layout.acc_offset);
+    if (plan.mode == pa::DecodeMode::kMfma) a.ws_off = reinterpret_cast<int*>(ws + plan.off_offset);
   }
-  const hipError_t e = plan.mode == pa::DecodeMode::kBalanced
-                           ? pa::launch_decode_balanced(a, static_cast<hipStream_t>(stream))
-                           : pa::launch_decode_partitioned(a, static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = plan.mode == pa::DecodeMode::kBalanced ? pa::launch_decode_balanced(a, hs)
+                       : plan.mode == pa::DecodeMode::kMfma   ? pa::launch_decode_mfma(a, hs)
+                                                              : pa::launch_decode_partitioned(a, hs);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

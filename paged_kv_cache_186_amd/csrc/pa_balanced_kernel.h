@@ -446,9 +446,9 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     const char* kb = k_pool + tile + lane * kVecBytes;
     const char* vb = v_pool + tile + lane * kVecBytes;
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) st.k[i] = load16(kb + i * C::kLoadBytes);
+    for (int i = 0; i < C::kLoads; ++i) st.k[i] = load16_stream(kb + i * C::kLoadBytes);
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) st.v[i] = load16(vb + i * C::kLoadBytes);
+    for (int i = 0; i < C::kLoads; ++i) st.v[i] = load16_stream(vb + i * C::kLoadBytes);
     if constexpr (GW == 1) load_q();
     if constexpr (KT::kScaled) {
       st.sk = load_uniform_f32(k_scales + static_cast<size_t>(phys) * HKV + kvh);

@@ -238,9 +238,9 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
     const char* kb = k_pool + tile + lane * kVecBytes;
     const char* vb = v_pool + tile + lane * kVecBytes;
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) st.k[g][i] = load16(kb + i * C::kLoadBytes);
+    for (int i = 0; i < C::kLoads; ++i) st.k[g][i] = load16_stream(kb + i * C::kLoadBytes);
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i) st.v[g][i] = load16(vb + i * C::kLoadBytes);
+    for (int i = 0; i < C::kLoads; ++i) st.v[g][i] = load16_stream(vb + i * C::kLoadBytes);
     if constexpr (KT::kScaled) {
       st.sk[g] = load_uniform_f32(k_scales + static_cast<size_t>(phys) * num_kv_heads + kvh);
       st.sv[g] = load_uniform_f32(v_scales + static_cast<size_t>(phys) * num_kv_heads + kvh);

@@ -1,0 +1,552 @@
+// Grouped-query decode on the matrix cores (gfx950 MFMA).
+//
+// What is computed: pa_decode with fewer K/V heads than query heads — every
+// query head h of sequence s attends over the K/V rows of K/V head h / G
+// found through the block table (vLLM tutorial page "3. PagedAttention原理",
+// §3.2 and the closing remarks of §3.4; page "PagedAttentionMetal：基于Metal 3
+// 的Apple Silicon原生LLM推理加速方案", section 注意力计算优化), contexts split
+// into partitions whose softmax partials are merged with the log-sum-exp
+// identity (the "Flash-Dec" milestone of "PagedAttention MLX：为Apple Silicon
+// 打造的高吞吐量LLM推理引擎").
+//
+// Why the matrix cores: the G query heads of a group read the same keys and
+// values, so per K/V byte there are G dot products and G weighted sums.  On
+// the vector unit that arithmetic, not the bytes, bounds a group of 4 or
+// more; as a 16-row MFMA tile (rows = the group's heads) it costs a few
+// products per 16 keys, and the kernel is left with the bytes.
+//
+// Work decomposition (our design).  Items are (sequence, K/V head, partition
+// of P tokens); P, a power of two from 128 to 2048 tokens, is chosen on the
+// device from the lengths — the largest not above the K/V tokens per
+// resident workgroup, so that a long context gives each workgroup one long
+// item and a ragged batch many short ones — and every workgroup rebuilds the
+// per-sequence item offsets in LDS.  The four waves of
+// a workgroup share an item: wave w takes its 32-key steps w, w + 4, ...
+// (adjacent waves read adjacent 8 KiB of K and V at once), each with its own
+// online softmax over NT tiles of 16 query rows; at the end of the item the
+// four states are merged through LDS.  An item that is its row's only
+// partition writes the output; otherwise it writes its (max, sum, weighted V
+// sum) per head to the workspace, and a second, small kernel merges each
+// split row's partials (one workgroup per (sequence, query head)) — a
+// 131072-token context on one K/V head has hundreds of partials, far more
+// than one wave could merge at the end of the first kernel.
+//
+// One 32-key step of one wave (two 16-key blocks), per tile of 16 query rows:
+//   S^T = K Q^T    v_mfma_f32_16x16x32_{f16,bf16}, D/32 products per block:
+//                  A = 16 keys x 32 elements (lane l: key l%16, elements
+//                  8*(l/16)..+7), B = the same elements of the 16 query rows;
+//                  lane l gets keys 4*(l/16)+i of the block for row l%16;
+//   softmax        the lane's 8 scores, the row's maximum across its four
+//                  lanes; rescaling deferred until a row's maximum grows by
+//                  more than 2^8;
+//   O^T += V^T P^T v_mfma_f32_16x16x32 over the step's 32 keys (the operand
+//                  layout of the query kernels), D/16 products, plus one with
+//                  every value 1 for the row sums of the rounded weights.
+
+#include "pa_attend.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_mfma.h"
+#include "pagedattn.h"
+
+namespace pa {
+namespace {
+
+constexpr int kGqWaves = 4;
+
+template <typename T, int D, int BS, int NT>
+__global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_kernel(
+    typename T::storage* __restrict__ out, const typename T::storage* __restrict__ q,
+    const char* __restrict__ k_pool, const char* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int* __restrict__ ws_off, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc, float qk_scale, uint32_t q_sign_bits, int num_seqs, int num_heads,
+    int num_kv_heads, int group, int num_blocks, int max_blocks, int max_items, int slots) {
+  static_assert(D % 64 == 0 && BS % 16 == 0, "MFMA slices");
+  using S16 = typename T::storage;
+  using M = Mfma<T>;
+  using PV = PvOps<T, 2>;
+  using pw_t = typename PV::word_t;
+  constexpr int kTblRegs = (kMfmaMaxPartTokens / BS + kWave - 1) / kWave;  // table entries per lane
+  constexpr int kQK = D / 32;  // S^T products per 16 keys
+  constexpr int kDq = D / 64;  // 64-element value slices
+  constexpr int kThreads = kGqWaves * kWave;
+  constexpr int kPer = (kBalancedMaxSeqs + kThreads - 1) / kThreads;
+  // partition candidates kMfmaMaxPartTokens, half that, ... kMfmaMinPartTokens
+  constexpr int kMinShift = __builtin_ctz(kMfmaMinPartTokens);
+  constexpr int kMaxShift = __builtin_ctz(kMfmaMaxPartTokens);
+  constexpr int kParts = kMaxShift - kMinShift + 1;
+  __shared__ int s_off[kBalancedMaxSeqs + 1];
+  __shared__ int s_len[kBalancedMaxSeqs];
+  __shared__ int s_wsum[kParts][kGqWaves];
+  __shared__ int s_wtok[kGqWaves];
+  __shared__ float s_m[kGqWaves][NT][16];
+  __shared__ float s_l[kGqWaves][NT][16];
+  __shared__ int s_bad[kGqWaves];
+  __shared__ f4_t s_o[kGqWaves][NT][16][D / 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int S = num_seqs;
+  const int HKV = num_kv_heads;
+  const int G = group;
+  const int cap = max_blocks * BS;
+
+  // 1. lengths, then the items per sequence for each candidate partition
+  //    (HKV * ceil(L / P)), their exclusive prefix sums for the chosen one
+  for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);
+  __syncthreads();
+  int mine[kParts];
+#pragma unroll
+  for (int c = 0; c < kParts; ++c) mine[c] = 0;
+  int mine_tok = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    const int L = s < S ? s_len[s] : 0;
+    mine_tok += L;
+#pragma unroll
+    for (int c = 0; c < kParts; ++c) mine[c] += HKV * ((L + (1 << (kMaxShift - c)) - 1) >> (kMaxShift - c));
+  }
+  int incl[kParts];
+#pragma unroll
+  for (int c = 0; c < kParts; ++c) {
+    incl[c] = wave_prefix_sum(mine[c]);
+    if (lane == kWave - 1) s_wsum[c][wave] = incl[c];
+  }
+  const int incl_tok = wave_prefix_sum(mine_tok);
+  if (lane == kWave - 1) s_wtok[wave] = incl_tok;
+  __syncthreads();
+  // the partition: the largest power of two (kMfmaMinPartTokens ..
+  // kMfmaMaxPartTokens) not above the K/V tokens per resident workgroup,
+  // HKV * sum(L) / slots — long contexts get one long item per workgroup,
+  // ragged batches many short ones
+  long long tokens = 0;
+#pragma unroll
+  for (int w = 0; w < kGqWaves; ++w) tokens += s_wtok[w];
+  const long long per_slot = static_cast<long long>(HKV) * tokens / max(slots, 1);
+  int ci = kParts - 1;
+  int total = 0;
+  int run = 0;
+#pragma unroll
+  for (int c = kParts - 1; c >= 0; --c) {
+    int tot = 0, bef = 0;
+#pragma unroll
+    for (int w = 0; w < kGqWaves; ++w) {
+      tot += s_wsum[c][w];
+      bef += (w < wave) ? s_wsum[c][w] : 0;
+    }
+    if (c == kParts - 1 || (1LL << (kMaxShift - c)) <= per_slot) {
+      ci = c;
+      total = tot;
+      run = bef + incl[c] - mine[c];
+    }
+  }
+  ci = __builtin_amdgcn_readfirstlane(ci);
+  const int pshift = kMaxShift - ci;  // P = 2^pshift tokens
+  const int P = 1 << pshift;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    if (s < S) s_off[s] = run;
+    run += s < S ? HKV * ((s_len[s] + P - 1) >> pshift) : 0;
+  }
+  total = min(__builtin_amdgcn_readfirstlane(total), max_items);
+  if (tid == 0) s_off[S] = total;
+  __syncthreads();
+  // the merge kernel reads the same offsets and partition size
+  if (blockIdx.x == 0 && ws_off != nullptr) {
+    for (int s = tid; s <= S; s += kThreads) ws_off[s] = s_off[s];
+    if (tid == 0) ws_off[S + 1] = P;
+  }
+
+  // 2. empty contexts give zero rows (spread over the workgroups)
+  for (int s = blockIdx.x; s < S; s += gridDim.x)
+    if (s_len[s] == 0)
+      for (int i = tid; i < num_heads * D; i += kThreads)
+        out[static_cast<size_t>(s) * num_heads * D + i] = T::pack(0.f);
+
+  const u32x4 q_sign = {q_sign_bits, q_sign_bits, q_sign_bits, q_sign_bits};
+  const int col = lane % 16;  // query row of a tile / key of a 16-key block
+  const int g4 = lane / 16;   // lane group: 8-element slice of S^T's K dim, key quad of P
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    // 3. which (sequence, K/V head, partition)
+    int lo = 0;
+    int hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= item)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(lo);
+    const int L = __builtin_amdgcn_readfirstlane(s_len[s]);
+    const int parts = (L + P - 1) >> pshift;
+    const int local = item - __builtin_amdgcn_readfirstlane(s_off[s]);
+    const int kvh = local / parts;
+    const int part = local - kvh * parts;
+    const int k_begin = part * P;
+    const int k_end = min(k_begin + P, L);
+
+    // query rows of tile t: heads kvh*G + 16t + col (B operand of S^T)
+    u32x4 qv[NT][kQK];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r = 16 * t + col;
+      const bool ok = r < G;
+      const S16* qrow = q + (static_cast<size_t>(s) * num_heads + kvh * G + (ok ? r : 0)) * D + 8 * g4;
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) {
+        const u32x4 v = load16(qrow + 32 * j) ^ q_sign;  // a negative scale flips q's signs instead
+        qv[t][j] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+
+    float m[NT];
+    f4_t lacc[NT];
+    f4_t acc[NT][kDq][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      m[t] = -INFINITY;
+      lacc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][dq][e] = f4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    int bad = 0;
+
+    struct Stage {
+      u32x4 k[2][kQK];
+      u32x2 v[2][kDq][4];
+      int c;
+      int bad;
+    };
+    // the item's block-table entries, one per lane (entry blk0 + lane + 64r),
+    // loaded once: each step then takes its block ids by v_readlane instead
+    // of a scalar memory round trip before its K/V loads can be issued
+    const int32_t* tbl = block_tables + static_cast<size_t>(s) * max_blocks;
+    const int blk0 = k_begin / BS;
+    const int nblk = (k_end - k_begin + BS - 1) / BS;
+    int tblv[kTblRegs];
+#pragma unroll
+    for (int r = 0; r < kTblRegs; ++r) tblv[r] = tbl[blk0 + min(lane + kWave * r, nblk - 1)];
+    auto load_step = [&](Stage& st, int c) __attribute__((always_inline)) {
+      st.c = c;
+      st.bad = 0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // a 16-key block wholly past the item's keys reads the step's first
+        // block again (its table entry may not exist); its keys are masked
+        const int key0 = (c + 16 * kb < k_end) ? c + 16 * kb : c;
+        const int b = key0 / BS - blk0;  // < nblk
+        int tv = tblv[0];
+#pragma unroll
+        for (int r = 1; r < kTblRegs; ++r) tv = (b >> 6) == r ? tblv[r] : tv;
+        int phys = __builtin_amdgcn_readlane(tv, b & (kWave - 1));
+        if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
+          st.bad = 1;  // never dereference an id outside the pool
+          phys = 0;
+        }
+        const size_t row0 = (static_cast<size_t>(phys) * HKV + kvh) * BS + (key0 % BS);
+        const char* kp = k_pool + row0 * (D * sizeof(S16)) + static_cast<uint32_t>((col * D + 8 * g4) * sizeof(S16));
+#pragma unroll
+        for (int j = 0; j < kQK; ++j) st.k[kb][j] = load16_stream(kp + 32 * j * sizeof(S16));
+        const char* vp = v_pool + row0 * (D * sizeof(S16)) + static_cast<uint32_t>((4 * g4 * D + 4 * col) * sizeof(S16));
+#pragma unroll
+        for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st.v[kb][dq][e] = load8_stream(vp + (e * D + 64 * dq) * sizeof(S16));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto attend_step = [&](Stage& st) __attribute__((always_inline)) {
+      bad |= st.bad;
+      if (st.c + 32 > L) {  // value rows past the context may hold anything: zero
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (st.c + 16 * kb + 4 * g4 + e >= L)
+#pragma unroll
+              for (int dq = 0; dq < kDq; ++dq) st.v[kb][dq][e] = u32x2{0u, 0u};
+      }
+      const bool masked = st.c + 32 > k_end;
+      f4_t scs[NT][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          f4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < kQK; ++j) sc = M::qk(st.k[kb][j], qv[t][j], sc);
+          scs[t][kb] = sc;
+        }
+      pw_t pw[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float z[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[kb][i] = scs[t][kb][i];
+          if (masked) {
+            const int key = st.c + 16 * kb + 4 * g4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[kb][i] = (key + i < k_end) ? z[kb][i] : -INFINITY;
+          }
+        }
+        float cm = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                         fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+        cm = fold_max<16>(cm);  // the row's four lanes: l, l ^ 16, l ^ 32, l ^ 48
+        const float cms = (cm == -INFINITY) ? -INFINITY : cm * qk_scale;  // qk_scale >= 0
+        const float mn = fmaxf(m[t], cms);
+        if (__builtin_amdgcn_ballot_w64(mn > m[t] + kRescaleLog2) != 0) {
+          const float alpha = (m[t] == -INFINITY) ? 0.f : fast_exp2(m[t] - mn);
+          lacc[t] *= alpha;
+#pragma unroll
+          for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t][dq][e] *= alpha;
+          m[t] = mn;
+        }
+        // p = 2^(scale*log2e*z - m); masked scores (-inf) are set to 0
+        // explicitly (a zero scale would make -inf * scale a NaN)
+        const float nm = -m[t];
+        float p[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
+            p[kb][i] = (masked && z[kb][i] == -INFINITY) ? 0.f : x;
+          }
+        pw[t] = pw_t{M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3]), M::pack2(p[1][0], p[1][1]),
+                     M::pack2(p[1][2], p[1][3])};
+      }
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const pw_t a = {col_pair(st.v[0][dq][0], st.v[0][dq][1], e), col_pair(st.v[0][dq][2], st.v[0][dq][3], e),
+                          col_pair(st.v[1][dq][0], st.v[1][dq][1], e), col_pair(st.v[1][dq][2], st.v[1][dq][3], e)};
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t][dq][e] = PV::mma(a, pw[t], acc[t][dq][e]);
+        }
+      const pw_t ones = {M::kOnes, M::kOnes, M::kOnes, M::kOnes};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) lacc[t] = PV::mma(ones, pw[t], lacc[t]);
+    };
+
+    // 4. this wave's steps of the item: keys k_begin + 32*(wave + 4i), two in flight
+    const int first = k_begin + 32 * wave;
+    const int n_steps = k_end > first ? (k_end - first + 32 * kGqWaves - 1) / (32 * kGqWaves) : 0;
+    if (n_steps > 0) {
+      Stage a, b;
+      load_step(a, first);
+      int c = 0;
+      for (; c + 2 < n_steps; c += 2) {
+        load_step(b, first + (c + 1) * 32 * kGqWaves);
+        attend_step(a);
+        load_step(a, first + (c + 2) * 32 * kGqWaves);
+        attend_step(b);
+      }
+      if (c + 1 < n_steps) {
+        load_step(b, first + (c + 1) * 32 * kGqWaves);
+        attend_step(a);
+        attend_step(b);
+      } else {
+        attend_step(a);
+      }
+    }
+
+    // 5. the four waves' states merged through LDS; lane l holds, for row col
+    //    of tile t, value elements 64*dq + 16*g4 + 4*i + e
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (g4 == 0) {
+        s_m[wave][t][col] = m[t];
+        s_l[wave][t][col] = lacc[t][0];
+      }
+#pragma unroll
+      for (int dq = 0; dq < kDq; ++dq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_o[wave][t][col][16 * dq + 4 * g4 + i] =
+              f4_t{acc[t][dq][0][i], acc[t][dq][1][i], acc[t][dq][2][i], acc[t][dq][3][i]};
+    }
+    if (lane == 0) s_bad[wave] = bad;
+    __syncthreads();
+    const bool any_bad = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
+    constexpr int kQuads = NT * 16 * (D / 4);  // 4-element pieces of the item's output
+    for (int x = tid; x < kQuads; x += kThreads) {
+      const int c4 = x % (D / 4);
+      const int r = (x / (D / 4)) % 16;
+      const int t = x / (16 * (D / 4));
+      const int row = 16 * t + r;  // head of the group
+      if (row >= G) continue;
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kGqWaves; ++w) Mx = fmaxf(Mx, s_m[w][t][r]);
+      float l = 0.f;
+      f4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kGqWaves; ++w) {
+        const float mw = s_m[w][t][r];
+        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - Mx);
+        l += f * s_l[w][t][r];
+        o += f * s_o[w][t][r][c4];
+      }
+      if (any_bad) l = __builtin_nanf("");
+      const size_t h = static_cast<size_t>(kvh) * G + row;
+      if (parts == 1) {
+        const float inv = 1.f / l;
+        const uint32_t w0 = M::pack2(o[0] * inv, o[1] * inv);
+        const uint32_t w1 = M::pack2(o[2] * inv, o[3] * inv);
+        *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(s) * num_heads + h) * D + 4 * c4) = u32x2{w0, w1};
+      } else {
+        const size_t slot = static_cast<size_t>(item) * G + row;
+        *reinterpret_cast<f4_t*>(ws_acc + slot * D + 4 * c4) = o;
+        if (c4 == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{Mx, l};
+      }
+    }
+    __syncthreads();  // the LDS state is rewritten by the next item
+  }
+}
+
+// One workgroup per (sequence, query head, 32-element slice of D): the
+// log-sum-exp merge of the partials of a row split into several partitions
+// (nothing to do for a row of one partition: the first kernel wrote it).
+// kC = 8 lanes cover one partial's 32 sums (4 each) and the kG = 32 lane
+// groups take every kG-th partial, kU of them per round with all their loads
+// issued at once — a row of up to 256 partials is one memory round trip; each
+// round is folded into a running (max, sum, sums) with the online rescaling,
+// and the groups are combined through LDS.  Slicing D spreads a long row's
+// partials (hundreds of KiB for 32 heads) over several CUs.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeSlice = 32;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void decode_mfma_merge_kernel(
+    typename T::storage* __restrict__ out, const int* __restrict__ ws_off, const float* __restrict__ ws_ml,
+    const float* __restrict__ ws_acc, const int32_t* __restrict__ context_lens, int num_seqs, int num_heads,
+    int group, int cap) {
+  constexpr int kSlices = D / kMergeSlice;
+  constexpr int kC = kMergeSlice / 4;
+  constexpr int kG = kMergeThreads / kC;
+  constexpr int kU = 8;
+  __shared__ float s_M[kG];
+  __shared__ float s_den[kG];
+  __shared__ f4_t s_num[kG][kC];
+  const int slice = blockIdx.x % kSlices;
+  const int row = blockIdx.x / kSlices;
+  const int s = row / num_heads;
+  const int h = row % num_heads;
+  const int L = min(max(context_lens[s], 0), cap);
+  const int P = ws_off[num_seqs + 1];
+  const int parts = (L + P - 1) / P;
+  if (parts <= 1) return;
+  const int kvh = h / group;
+  const int g = h % group;
+  const size_t item0 = static_cast<size_t>(ws_off[s]) + static_cast<size_t>(kvh) * parts;
+  const int tid = threadIdx.x;
+  const int c = tid % kC;
+  const int grp = tid / kC;
+  const int e0 = slice * kMergeSlice + 4 * c;  // first element of this lane
+  float Mx = -INFINITY, den = 0.f;
+  f4_t num = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = grp; p0 < parts; p0 += kG * kU) {
+    f32x2 ml[kU];
+    f4_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t slot = (item0 + min(p0 + u * kG, parts - 1)) * group + g;
+      ml[u] = *reinterpret_cast<const f32x2*>(ws_ml + slot * 2);
+      v[u] = *reinterpret_cast<const f4_t*>(ws_acc + slot * D + e0);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (p0 + u * kG < parts) bm = fmaxf(bm, ml[u][0]);
+    const float mn = fmaxf(Mx, bm);
+    if (mn == -INFINITY) continue;  // only empty partials so far
+    const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
+    den *= a;
+    num *= a;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float mu = ml[u][0];
+      const float wgt = (p0 + u * kG < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f;
+      den = fmaf(wgt, ml[u][1], den);
+      num += wgt * v[u];
+    }
+    Mx = mn;
+  }
+  if (c == 0) {
+    s_M[grp] = Mx;
+    s_den[grp] = den;
+  }
+  s_num[grp][c] = num;
+  __syncthreads();
+  if (tid >= kC) return;
+  float M2 = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kG; ++k) M2 = fmaxf(M2, s_M[k]);
+  float d = 0.f;
+  f4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int k = 0; k < kG; ++k) {
+    const float f = (s_M[k] == -INFINITY) ? 0.f : fast_exp2(s_M[k] - M2);
+    d = fmaf(f, s_den[k], d);
+    o += f * s_num[k][tid];
+  }
+  const float inv = 1.f / d;
+  const uint32_t w0 = Mfma<T>::pack2(o[0] * inv, o[1] * inv);
+  const uint32_t w1 = Mfma<T>::pack2(o[2] * inv, o[3] * inv);
+  *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(s) * num_heads + h) * D + e0) = u32x2{w0, w1};
+}
+
+template <typename T, int D, int BS, int NT>
+hipError_t run_mfma(const DecodeArgs& a, hipStream_t stream) {
+  using S16 = typename T::storage;
+  hipLaunchKernelGGL((decode_mfma_kernel<T, D, BS, NT>), dim3(a.workgroups), dim3(kGqWaves * kWave), 0, stream,
+                     static_cast<S16*>(a.out), static_cast<const S16*>(a.q), static_cast<const char*>(a.k_pool),
+                     static_cast<const char*>(a.v_pool), a.block_tables, a.context_lens, a.ws_off, a.ws_ml,
+                     a.ws_acc, fabsf(a.scale) * kLog2e, a.scale < 0.f ? 0x80008000u : 0u, a.num_seqs,
+                     a.num_heads, a.num_kv_heads, a.num_heads / a.num_kv_heads, a.num_blocks,
+                     a.max_blocks_per_seq, a.max_items, a.mfma_slots);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ws_ml == nullptr) return e;
+  hipLaunchKernelGGL((decode_mfma_merge_kernel<T, D>), dim3(a.num_seqs * a.num_heads * (D / kMergeSlice)),
+                     dim3(kMergeThreads), 0, stream,
+                     static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
+                     a.num_heads, a.num_heads / a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int BS>
+hipError_t run_mfma_nt(const DecodeArgs& a, hipStream_t stream) {
+  return (a.num_heads / a.num_kv_heads) > 16 ? run_mfma<T, D, BS, 2>(a, stream) : run_mfma<T, D, BS, 1>(a, stream);
+}
+
+template <typename T, int D>
+hipError_t run_mfma_bs(const DecodeArgs& a, hipStream_t stream) {
+  return a.block_size == 16 ? run_mfma_nt<T, D, 16>(a, stream) : run_mfma_nt<T, D, 32>(a, stream);
+}
+
+template <typename T>
+hipError_t run_mfma_d(const DecodeArgs& a, hipStream_t stream) {
+  return a.head_dim == 64 ? run_mfma_bs<T, 64>(a, stream) : run_mfma_bs<T, 128>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+  return a.dtype == PA_DTYPE_BF16 ? run_mfma_d<BF16>(a, stream) : run_mfma_d<F16>(a, stream);
+}
+
+}  // namespace pa

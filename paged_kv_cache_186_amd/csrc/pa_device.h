@@ -320,6 +320,20 @@ __device__ __forceinline__ float load_uniform_f32(const float* p) {
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+
+// K/V cache reads of the decode kernels: every byte is used once per call, so
+// they are non-temporal (streaming) loads, which keep the stream from
+// displacing other lines in the caches.  Measured against plain loads on the
+// same kernels: 4 x 131072 tokens 1399 -> 1240 us, 131072 tokens 355 -> 318
+// us, continuous batching 154 -> 136 us, layer shape 24.2 -> 22.2 us; the
+// grouped-query matrix-core kernel 55.7 -> 49.2 us (4 K/V heads over 128K).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2_t load8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }

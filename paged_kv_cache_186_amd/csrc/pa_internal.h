@@ -38,7 +38,11 @@ constexpr int kCopyChunkBytes = 16384;  // bytes one copy_blocks workgroup moves
 //  * kPartitioned (partition_size > 0, or more sequences): one workgroup per
 //    (head, partition, sequence); every multi-partition row produces one
 //    partial per partition.
-enum class DecodeMode { kBalanced, kPartitioned };
+//  * kMfma (grouped-query heads, a group of 3 to 32 heads, 16-bit q and
+//    cache, partition_size 0, at most kBalancedMaxSeqs sequences): items of
+//    (sequence, K/V head, partition) on the matrix cores, the group's heads
+//    as the rows of a 16-row tile; split rows merged by a second kernel.
+enum class DecodeMode { kBalanced, kPartitioned, kMfma };
 
 struct DecodeArgs {
   void* out;
@@ -67,6 +71,9 @@ struct DecodeArgs {
   uint32_t* counters;    // [S][H] arrival tickets (null when no row can be split)
   float* ws_ml;          // [slots][2]  (max, sum) of each partial
   float* ws_acc;         // [slots][D]  unnormalised weighted V sum of each partial
+  int* ws_off;           // kMfma: [S + 2] item offsets and the partition size, for the merge
+  int max_items;         // kMfma: items the workspace holds (slots = max_items * group)
+  int mfma_slots;        // kMfma: workgroups resident on the whole GPU at once
 };
 
 // Workspace of pa_decode: the ticket counters come first (they must be zero
@@ -154,6 +161,22 @@ hipError_t launch_decode_balanced(const DecodeArgs& a, hipStream_t stream);
 // group_width 2, 4
 hipError_t launch_decode_balanced_gqa2(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_balanced_gqa4(const DecodeArgs& a, hipStream_t stream);
+// grouped-query heads on the matrix cores (kMfma)
+constexpr int kMfmaMinGroup = 3;
+constexpr int kMfmaMaxGroup = 32;
+constexpr int kMfmaMinPartTokens = 128;   // the smallest partition the kernel picks
+#ifndef PA_GQ_MAX_PART
+#define PA_GQ_MAX_PART 2048
+#endif
+#ifndef PA_GQ_MAX_WG
+#define PA_GQ_MAX_WG 1024
+#endif
+constexpr int kMfmaMaxPartTokens = PA_GQ_MAX_PART;  // the largest
+constexpr int kMfmaMaxWorkgroups = PA_GQ_MAX_WG;
+// Workgroups of the kernel resident on one CU: two with one 16-row tile
+// (groups of up to 16 heads), one with two (register file).
+inline int mfma_wg_per_cu(int group) { return group > 16 ? 1 : 2; }
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 
 // Attention of several query rows per (sequence, K/V head) on the matrix
 // cores: multi-token queries (pa_prefill) and decode over an MLA latent cache

@@ -1,0 +1,144 @@
+"""GPU parity of grouped-query decode on the matrix cores (pa_decode_gqa with
+a group of 3 to 32 query heads per K/V head, fp16 / bf16 queries and cache,
+the default split) against the float64 oracle, through the C ABI.
+
+The kernel picks its partition (512, 256 or 128 tokens) from the lengths;
+the cases below reach each of the three, rows of one partition (written by
+the first kernel) and of many (merged by the second), every group size
+class (one tile of 16 rows partly filled, two tiles), both head dims and
+block sizes, empty and one-token contexts, NaN-poisoned unreferenced slots,
+an out-of-pool table id, negative and zero softmax scales, and the 128K
+context with 4 and 1 K/V heads (the benchmark's shapes) on every head.
+"""
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_186_amd as pa
+from paged_kv_cache_186_amd import workloads as W
+from oracle import decode_gqa_ref
+from gpu_support import DEV, announce, assert_close, bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _workload(lens, H, Hkv, D, bs, dtype, seed, scale=None, poison=True):
+    rng = np.random.default_rng(seed)
+    nb = sum(-(-L // bs) for L in lens) + len(lens) + 4
+    m = W.BlockManager(nb, bs, free_order=rng.permutation(nb).tolist())
+    for s, L in enumerate(lens):
+        m.allocate(s)
+        m.append_slots(s, L)
+    width = max(1, max(-(-L // bs) for L in lens))
+    w = W.PagedWorkload("gqa_mfma", dtype, H, D, bs, nb, 0.9 / np.sqrt(D) if scale is None else scale, m,
+                        list(range(len(lens))), width, seed, DEV)
+    W.fill_values(w, poison=False)
+    w.k_pool = w.k_pool[:, :Hkv].contiguous()
+    w.v_pool = w.v_pool[:, :Hkv].contiguous()
+    if poison:
+        W.poison_unreferenced(w)
+    return w
+
+
+def _run(w, tables=None):
+    out = torch.empty_like(w.q)
+    bt = w.block_tables().to(DEV) if tables is None else tables
+    pa.pa_decode_gqa(out, w.q, w.k_pool, w.v_pool, bt, w.context_lens().to(DEV), w.scale, w.block_size)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle(w, tables=None):
+    return decode_gqa_ref(w.q.cpu(), w.k_pool.cpu(), w.v_pool.cpu(),
+                          w.block_tables_np() if tables is None else tables, w.context_lens_np(), w.scale,
+                          w.block_size)
+
+
+# total K/V-head items per partition size 512 / 256 / 128 decide the choice
+# (the largest with at least 256 items): each case below lands on one
+PARTITION_CASES = {
+    512: ([131072], 2),             # 2 x 256 items at 512 tokens
+    256: ([40000, 3], 2),           # 2 x (79 + 1) = 160 at 512, 2 x (157 + 1) = 316 at 256
+    128: ([0, 1, 900, 2, 333, 17, 2500, 1], 4),   # few tokens: 128-token partitions
+}
+
+
+@pytest.mark.parametrize("part", [512, 256, 128])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_partition_choices(part, dtype):
+    lens, Hkv = PARTITION_CASES[part]
+    announce(f"gqa mfma partition {part} {dtype}")
+    w = _workload(lens, 8 * Hkv, Hkv, 128, 16, dtype, 100 + part)
+    out = _run(w)
+    assert_close(out, _oracle(w), dtype, f"partition {part}")
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert not out[s].any()
+    assert torch.equal(bits(_run(w)), bits(out)), "second call differs"
+
+
+@pytest.mark.parametrize("H,Hkv", [(12, 4), (20, 4), (24, 4), (48, 3), (32, 2), (32, 1), (64, 2)])
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 32)])
+def test_group_sizes(H, Hkv, D, bs):
+    """Groups of 3, 5, 6 (one 16-row tile, partly filled), 16 (one full tile),
+    16 again over two K/V heads, 32 (two tiles) and 32 over two K/V heads."""
+    announce(f"gqa mfma H={H} Hkv={Hkv} D={D} bs={bs}")
+    lens = [0, 1, 700, 31, 4097, 64, 2]
+    w = _workload(lens, H, Hkv, D, bs, torch.float16, 7 * H + Hkv + D + bs)
+    assert_close(_run(w), _oracle(w), torch.float16, f"H={H} Hkv={Hkv} D={D} bs={bs}")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
+def test_negative_zero_and_large_scales(scale):
+    announce(f"gqa mfma scale {scale}")
+    w = _workload([300, 5000, 1], 32, 4, 128, 32, torch.bfloat16, 11, scale=scale)
+    assert_close(_run(w), _oracle(w), torch.bfloat16, f"scale {scale}")
+
+
+def test_out_of_pool_table_id():
+    """A referenced table entry outside the pool makes NaN exactly the rows of
+    the query heads that read it (every head of its K/V head's group, in that
+    sequence); the other rows are exact."""
+    announce("gqa mfma out-of-pool id")
+    w = _workload([3000, 700, 9000], 32, 4, 128, 16, torch.float16, 12)
+    bt = w.block_tables().to(DEV)
+    bt[1, 5] = w.num_blocks + 3
+    out = _run(w, tables=bt)
+    assert torch.isnan(out[1].float()).all()
+    ref = _oracle(w)
+    assert_close(out[[0, 2]], ref[[0, 2]], torch.float16, "other sequences")
+
+
+def _oracle_rows(w, heads):
+    tables, lens = w.block_tables_np(), w.context_lens_np()
+    G = w.num_heads // w.k_pool.shape[1]
+    qh, kh, vh = w.q.cpu(), w.k_pool.cpu(), w.v_pool.cpu()
+
+    def one(h):
+        kv = h // G
+        return h, decode_gqa_ref(qh[:, h:h + 1], kh[:, kv:kv + 1], vh[:, kv:kv + 1], tables, lens, w.scale,
+                                 w.block_size)
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        return dict(ex.map(one, heads))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("Hkv", [4, 1])
+def test_long_context_every_head(Hkv):
+    """One 131072-token context (8192 scattered blocks, fp16), 32 query heads
+    over 4 K/V heads or one: every head against the oracle."""
+    announce(f"gqa mfma long context 32/{Hkv}")
+    w = W.long_context(0, batch=1, device=DEV)
+    w.k_pool = w.k_pool[:, :Hkv].contiguous()
+    w.v_pool = w.v_pool[:, :Hkv].contiguous()
+    torch.cuda.empty_cache()
+    out = _run(w)
+    ref = _oracle_rows(w, list(range(32)))
+    want = np.concatenate([ref[h] for h in range(32)], axis=1)
+    err = assert_close(out, want, torch.float16, f"long context 32/{Hkv}")
+    print(f"long context 32 query / {Hkv} K/V heads: max abs err {err:.2e}")
+    del w
+    torch.cuda.empty_cache()
