@@ -424,6 +424,104 @@ PrefillPlan plan_prefill(int32_t num_seqs, int32_t num_query_rows, int32_t num_h
   return p;
 }
 
+// pa_decode_mla with at least kMlaHeadsMin heads: items (sequence, group of
+// 64 heads, partition), the partition (1024..4096 tokens) chosen on the
+// device; the workspace holds every item's 64 partials (for the smallest
+// partition) and the item offsets the merge kernel reads.
+// the many-heads latent kernel: default split, at least kMlaHeadsMin heads,
+// at most kMlaHeadsMaxSeqs sequences (more take the split kernel)
+bool use_mla_heads(int32_t num_seqs, int32_t num_heads, int32_t partition_size) {
+  return partition_size == 0 && num_heads >= pa::kMlaHeadsMin && num_seqs <= pa::kMlaHeadsMaxSeqs;
+}
+
+struct MlaHeadsPlan {
+  pa_status_t status;
+  int max_items;
+  int workgroups;
+  size_t off_offset;
+  pa::WorkspaceLayout ws;
+};
+
+MlaHeadsPlan plan_mla_heads(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq, int32_t block_size,
+                            bool sizes_only) {
+  MlaHeadsPlan p{PA_OK, 0, 0, 0, {0, 0, 0, 0}};
+  if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0 || max_blocks_per_seq > INT_MAX / block_size / 2 ||
+      num_seqs > pa::kMlaHeadsMaxSeqs) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  const long long ctx = static_cast<long long>(max_blocks_per_seq) * block_size;
+  const long long groups = (num_heads + pa::kMlaHeadsGroup - 1) / pa::kMlaHeadsGroup;
+  const long long items =
+      static_cast<long long>(num_seqs) * groups * ((ctx + pa::kMlaHeadsMinPart - 1) / pa::kMlaHeadsMinPart);
+  if (items > INT_MAX / pa::kMlaHeadsGroup) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  p.max_items = static_cast<int>(items);
+  if (!sizes_only) {
+    const long long per_cu = static_cast<long long>(num_seqs) * groups * ctx / cu_count();
+    int pt = pa::kMlaHeadsMaxPart;
+    while (pt > pa::kMlaHeadsMinPart && pt > per_cu) pt /= 2;
+    const long long grid = static_cast<long long>(num_seqs) * groups * ((ctx + pt - 1) / pt);
+    p.workgroups = static_cast<int>(grid < 1 ? 1 : (grid > pa::kMlaHeadsMaxWorkgroups ? pa::kMlaHeadsMaxWorkgroups : grid));
+  }
+  if (ctx > pa::kMlaHeadsMinPart) {  // a row can span several partitions
+    p.ws = pa::workspace_layout(0, static_cast<size_t>(items) * pa::kMlaHeadsGroup, pa::kMlaVDim);
+    p.off_offset = p.ws.total;
+    p.ws.total = pa::align_up(p.ws.total + (static_cast<size_t>(num_seqs) + 2) * sizeof(int), 256);
+  }
+  return p;
+}
+
+pa_status_t mla_heads_impl(void* out, const void* q, const void* kv_pool, const int32_t* block_tables,
+                           const int32_t* context_lens, float scale, int32_t block_size, int32_t num_seqs,
+                           int32_t num_heads, int32_t num_blocks, int32_t max_blocks_per_seq, pa_dtype_t dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (block_size != 16 && block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > pa::kMlaHeadsMaxSeqs) return PA_ERR_INVALID_ARG;
+  const MlaHeadsPlan plan = plan_mla_heads(num_seqs, num_heads, max_blocks_per_seq, block_size, false);
+  if (plan.status != PA_OK) return plan.status;
+  if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !kv_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4))
+    return PA_ERR_INVALID_ARG;
+  if (plan.ws.total > 0) {
+    if (!workspace || workspace_bytes < plan.ws.total) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+  }
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = kv_pool;
+  a.v_pool = kv_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.block_size = block_size;
+  a.num_seqs = num_seqs;
+  a.num_query_rows = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = 1;
+  a.head_dim = pa::kMlaQkDim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.dtype = dtype;
+  a.latent = true;
+  a.max_items = plan.max_items;
+  a.workgroups = plan.workgroups;
+  a.slots = cu_count();
+  if (plan.ws.total > 0) {
+    char* ws = static_cast<char*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
+    a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
+    a.ws_off = reinterpret_cast<int*>(ws + plan.off_offset);
+  }
+  return pa::launch_mla_heads(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 // Shared by pa_prefill and pa_decode_mla; the caller has checked dtype and
 // the head dimension.  Launches once per group of kPfMaxSeqs sequences (the
 // query bounds are absolute row numbers, so q and out are passed whole).
@@ -776,6 +874,10 @@ pa_status_t pa_prefill(void* out, const void* q, const void* k_pool, const void*
 size_t pa_decode_mla_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                     int32_t block_size, int32_t partition_size) {
   if (block_size != 16 && block_size != 32) return 0;
+  if (use_mla_heads(num_seqs, num_heads, partition_size)) {
+    const MlaHeadsPlan p = plan_mla_heads(num_seqs, num_heads, max_blocks_per_seq, block_size, true);
+    return p.status == PA_OK ? p.ws.total : 0;
+  }
   const PrefillPlan p = plan_prefill(num_seqs, num_seqs, num_heads, 1, max_blocks_per_seq, block_size,
                                      partition_size, pa::kMlaVDim, 1, 1, true);
   return p.status == PA_OK ? p.ws.total : 0;
@@ -787,6 +889,9 @@ pa_status_t pa_decode_mla(void* out, const void* q, const void* kv_pool, const i
                           int32_t max_blocks_per_seq, int32_t partition_size, pa_dtype_t dtype,
                           void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (use_mla_heads(num_seqs, num_heads, partition_size))
+    return mla_heads_impl(out, q, kv_pool, block_tables, context_lens, scale, block_size, num_seqs, num_heads,
+                          num_blocks, max_blocks_per_seq, dtype, workspace, workspace_bytes, stream);
   return prefill_impl(out, q, kv_pool, kv_pool, block_tables, context_lens, nullptr, scale,
                       block_size, num_seqs, num_seqs, num_heads, 1, pa::kMlaQkDim, num_blocks,
                       max_blocks_per_seq, partition_size, dtype, true, workspace, workspace_bytes,

@@ -53,6 +53,10 @@ namespace pa {
 namespace {
 
 constexpr int kGqWaves = 4;
+// the merge of split rows: 32-element slices of D per workgroup of 256
+// threads (32 lane groups, 8 partials each per round)
+constexpr int kDecodeMergeSlice = 32;
+constexpr int kDecodeMergeThreads = 256;
 
 template <typename T, int D, int BS, int NT>
 __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_kernel(
@@ -418,98 +422,6 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
   }
 }
 
-// One workgroup per (sequence, query head, 32-element slice of D): the
-// log-sum-exp merge of the partials of a row split into several partitions
-// (nothing to do for a row of one partition: the first kernel wrote it).
-// kC = 8 lanes cover one partial's 32 sums (4 each) and the kG = 32 lane
-// groups take every kG-th partial, kU of them per round with all their loads
-// issued at once — a row of up to 256 partials is one memory round trip; each
-// round is folded into a running (max, sum, sums) with the online rescaling,
-// and the groups are combined through LDS.  Slicing D spreads a long row's
-// partials (hundreds of KiB for 32 heads) over several CUs.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeSlice = 32;
-
-template <typename T, int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_mfma_merge_kernel(
-    typename T::storage* __restrict__ out, const int* __restrict__ ws_off, const float* __restrict__ ws_ml,
-    const float* __restrict__ ws_acc, const int32_t* __restrict__ context_lens, int num_seqs, int num_heads,
-    int group, int cap) {
-  constexpr int kSlices = D / kMergeSlice;
-  constexpr int kC = kMergeSlice / 4;
-  constexpr int kG = kMergeThreads / kC;
-  constexpr int kU = 8;
-  __shared__ float s_M[kG];
-  __shared__ float s_den[kG];
-  __shared__ f4_t s_num[kG][kC];
-  const int slice = blockIdx.x % kSlices;
-  const int row = blockIdx.x / kSlices;
-  const int s = row / num_heads;
-  const int h = row % num_heads;
-  const int L = min(max(context_lens[s], 0), cap);
-  const int P = ws_off[num_seqs + 1];
-  const int parts = (L + P - 1) / P;
-  if (parts <= 1) return;
-  const int kvh = h / group;
-  const int g = h % group;
-  const size_t item0 = static_cast<size_t>(ws_off[s]) + static_cast<size_t>(kvh) * parts;
-  const int tid = threadIdx.x;
-  const int c = tid % kC;
-  const int grp = tid / kC;
-  const int e0 = slice * kMergeSlice + 4 * c;  // first element of this lane
-  float Mx = -INFINITY, den = 0.f;
-  f4_t num = {0.f, 0.f, 0.f, 0.f};
-  for (int p0 = grp; p0 < parts; p0 += kG * kU) {
-    f32x2 ml[kU];
-    f4_t v[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const size_t slot = (item0 + min(p0 + u * kG, parts - 1)) * group + g;
-      ml[u] = *reinterpret_cast<const f32x2*>(ws_ml + slot * 2);
-      v[u] = *reinterpret_cast<const f4_t*>(ws_acc + slot * D + e0);
-    }
-    float bm = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-      if (p0 + u * kG < parts) bm = fmaxf(bm, ml[u][0]);
-    const float mn = fmaxf(Mx, bm);
-    if (mn == -INFINITY) continue;  // only empty partials so far
-    const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
-    den *= a;
-    num *= a;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const float mu = ml[u][0];
-      const float wgt = (p0 + u * kG < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f;
-      den = fmaf(wgt, ml[u][1], den);
-      num += wgt * v[u];
-    }
-    Mx = mn;
-  }
-  if (c == 0) {
-    s_M[grp] = Mx;
-    s_den[grp] = den;
-  }
-  s_num[grp][c] = num;
-  __syncthreads();
-  if (tid >= kC) return;
-  float M2 = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kG; ++k) M2 = fmaxf(M2, s_M[k]);
-  float d = 0.f;
-  f4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int k = 0; k < kG; ++k) {
-    const float f = (s_M[k] == -INFINITY) ? 0.f : fast_exp2(s_M[k] - M2);
-    d = fmaf(f, s_den[k], d);
-    o += f * s_num[k][tid];
-  }
-  const float inv = 1.f / d;
-  const uint32_t w0 = Mfma<T>::pack2(o[0] * inv, o[1] * inv);
-  const uint32_t w1 = Mfma<T>::pack2(o[2] * inv, o[3] * inv);
-  *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(s) * num_heads + h) * D + e0) = u32x2{w0, w1};
-}
-
 template <typename T, int D, int BS, int NT>
 hipError_t run_mfma(const DecodeArgs& a, hipStream_t stream) {
   using S16 = typename T::storage;
@@ -521,8 +433,8 @@ hipError_t run_mfma(const DecodeArgs& a, hipStream_t stream) {
                      a.max_blocks_per_seq, a.max_items, a.mfma_slots);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ws_ml == nullptr) return e;
-  hipLaunchKernelGGL((decode_mfma_merge_kernel<T, D>), dim3(a.num_seqs * a.num_heads * (D / kMergeSlice)),
-                     dim3(kMergeThreads), 0, stream,
+  hipLaunchKernelGGL((lse_merge_kernel<T, D, kDecodeMergeSlice, kDecodeMergeThreads>),
+                     dim3(a.num_seqs * a.num_heads * (D / kDecodeMergeSlice)), dim3(kDecodeMergeThreads), 0, stream,
                      static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
                      a.num_heads, a.num_heads / a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
   return hipGetLastError();

@@ -210,11 +210,23 @@ struct PrefillArgs {
   uint32_t* counters;  // [max_items] (null when no row can be split)
   float* ws_ml;        // [max_items][16 * row_tiles][2]
   float* ws_acc;       // [max_items][16 * row_tiles][DV]
+  int* ws_off;         // mla_heads: [S + 2] item offsets and the partition size, for the merge
+  int slots;           // mla_heads: CUs of the device
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // the latent cache: one workgroup per (sequence, 16 heads, partition), the
 // 576 elements of a row split across its four waves
 hipError_t launch_mla_split(const PrefillArgs& a, hipStream_t stream);
+// the latent cache with many heads: one workgroup per (sequence, 64 heads,
+// partition of 1024..4096 tokens), each wave 16 heads over the whole row, the
+// rows staged in LDS once per workgroup; split rows merged by a second kernel
+constexpr int kMlaHeadsMin = 64;        // heads from which pa_decode_mla takes this kernel
+constexpr int kMlaHeadsGroup = 64;      // heads per workgroup
+constexpr int kMlaHeadsMinPart = 1024;  // partition candidates (tokens)
+constexpr int kMlaHeadsMaxPart = 4096;
+constexpr int kMlaHeadsMaxWorkgroups = 1024;
+constexpr int kMlaHeadsMaxSeqs = 512;   // per-sequence offsets in LDS beside the rows and queries
+hipError_t launch_mla_heads(const PrefillArgs& a, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                                     const int32_t* slot_mapping, int num_tokens, int num_heads,

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "pa_device.h"
+#include "pa_attend.h"
 
 namespace pa {
 
@@ -100,5 +101,105 @@ struct PvOps<BF16, 2> {
                                                    0, 0, 0);
   }
 };
+
+// Log-sum-exp merge of rows split into several partitions, a kernel of its
+// own (after the kernel that wrote the partials): one workgroup per
+// (sequence, query head, SLICE-element slice of the D output elements).
+// Partials are laid out by item — (sequence, head group, partition), the
+// partition fastest — with `group` heads per item: the partial of head h of
+// sequence s in partition p sits in slot (off[s] + (h / group) * parts + p)
+// * group + h % group, where off[] (S + 1 item offsets) and the partition
+// size P (off[S + 1]) are what the first kernel wrote.  A row of one
+// partition was written by the first kernel: nothing to do.  kC = SLICE / 4
+// lanes cover one partial's slice (4 sums each) and the kG lane groups take
+// every kG-th partial, kU per round with all their loads issued at once;
+// each round is folded into a running (max, sum, sums) with the online
+// rescaling, and the groups are combined through LDS.
+template <typename T, int D, int SLICE, int THREADS>
+__global__ __launch_bounds__(THREADS) void lse_merge_kernel(
+    typename T::storage* __restrict__ out, const int* __restrict__ ws_off, const float* __restrict__ ws_ml,
+    const float* __restrict__ ws_acc, const int32_t* __restrict__ context_lens, int num_seqs, int num_heads,
+    int group, int cap) {
+  static_assert(D % SLICE == 0 && SLICE % 4 == 0 && THREADS % (SLICE / 4) == 0, "whole slices");
+  constexpr int kSlices = D / SLICE;
+  constexpr int kC = SLICE / 4;
+  constexpr int kG = THREADS / kC;
+  constexpr int kU = 8;
+  __shared__ float s_M[kG];
+  __shared__ float s_den[kG];
+  __shared__ f4_t s_num[kG][kC];
+  const int slice = blockIdx.x % kSlices;
+  const int row = blockIdx.x / kSlices;
+  const int s = row / num_heads;
+  const int h = row % num_heads;
+  const int L = min(max(context_lens[s], 0), cap);
+  const int P = ws_off[num_seqs + 1];
+  const int parts = (L + P - 1) / P;
+  if (parts <= 1) return;
+  const size_t item0 = static_cast<size_t>(ws_off[s]) + static_cast<size_t>(h / group) * parts;
+  const int g = h % group;
+  const int tid = threadIdx.x;
+  const int c = tid % kC;
+  const int grp = tid / kC;
+  const int e0 = slice * SLICE + 4 * c;  // first element of this lane
+  float Mx = -INFINITY, den = 0.f;
+  f4_t num = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = grp; p0 < parts; p0 += kG * kU) {
+    f32x2 ml[kU];
+    f4_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t slot = (item0 + min(p0 + u * kG, parts - 1)) * group + g;
+      ml[u] = *reinterpret_cast<const f32x2*>(ws_ml + slot * 2);
+      v[u] = *reinterpret_cast<const f4_t*>(ws_acc + slot * D + e0);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (p0 + u * kG < parts) bm = fmaxf(bm, ml[u][0]);
+    const float mn = fmaxf(Mx, bm);
+    if (mn == -INFINITY) continue;  // only empty partials so far
+    const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
+    den *= a;
+    num *= a;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float mu = ml[u][0];
+      const float wgt = (p0 + u * kG < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f;
+      den = fmaf(wgt, ml[u][1], den);
+      num += wgt * v[u];
+    }
+    Mx = mn;
+  }
+  if (kG == 1) {  // one lane group: nothing to combine
+    const float inv = 1.f / den;
+    const uint32_t w0 = Mfma<T>::pack2(num[0] * inv, num[1] * inv);
+    const uint32_t w1 = Mfma<T>::pack2(num[2] * inv, num[3] * inv);
+    *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(s) * num_heads + h) * D + e0) = u32x2{w0, w1};
+    return;
+  }
+  if (c == 0) {
+    s_M[grp] = Mx;
+    s_den[grp] = den;
+  }
+  s_num[grp][c] = num;
+  __syncthreads();
+  if (tid >= kC) return;
+  float M2 = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kG; ++k) M2 = fmaxf(M2, s_M[k]);
+  float d = 0.f;
+  f4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int k = 0; k < kG; ++k) {
+    const float f = (s_M[k] == -INFINITY) ? 0.f : fast_exp2(s_M[k] - M2);
+    d = fmaf(f, s_den[k], d);
+    o += f * s_num[k][tid];
+  }
+  const float inv = 1.f / d;
+  const uint32_t w0 = Mfma<T>::pack2(o[0] * inv, o[1] * inv);
+  const uint32_t w1 = Mfma<T>::pack2(o[2] * inv, o[3] * inv);
+  *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(s) * num_heads + h) * D + e0) = u32x2{w0, w1};
+}
 
 }  // namespace pa

@@ -1,0 +1,437 @@
+// Decode over the MLA latent cache with many query heads (gfx950 MFMA).
+//
+// What is computed: multi-head latent attention decode in its absorbed form
+// ("PagedAttention MLX：为Apple Silicon打造的高吞吐量LLM推理引擎", roadmap
+// milestone 3, names MLA; the form is the published one: one 576-element
+// cache row per token — 512-element latent then 64-element rotary key — every
+// query head scores scale * <q_h, row_t> over all 576 elements and takes the
+// row's first 512 elements as its value), through the block table (vLLM
+// tutorial page "3. PagedAttention原理", §3.2), long contexts split into
+// partitions merged with the log-sum-exp identity ("Flash-Dec", milestone 4).
+//
+// Why a kernel of its own for many heads: every head of a sequence reads the
+// same latent rows, so the rows should come from HBM once per sequence and
+// feed as many heads as possible.  Here a workgroup serves 64 heads: each of
+// its four waves owns 16 heads (the rows of its MFMA tiles) over the whole
+// 576-element row, and each 32-key step's rows (36 KiB) are loaded from HBM
+// once per workgroup into LDS (row stride padded by 16 bytes so that the 16
+// rows an operand load touches fall on different banks), from where every
+// wave reads its operands; the workgroup's 64 query rows sit in LDS too (in
+// registers, beside the 128 accumulator registers of a wave's 16 x 512
+// outputs, they would not fit).  The next step's rows are in flight in
+// registers while a step is computed; one barrier per step.
+//
+// Per step and wave (16 heads, 32 keys):
+//   S^T = K Q^T     18 v_mfma_f32_16x16x32 per 16-key block over the 576
+//                   elements (A = 16 keys x 32 elements from LDS, B = the
+//                   wave's queries, kept in registers for the whole item);
+//   softmax         the lane's 8 scores, the row's maximum across its four
+//                   lanes, rescaling deferred until it grows by more than 2^8;
+//   O^T += V^T P^T  32 products over the 512 latent values (A = V transposed
+//                   from LDS by byte permutes, as in the query kernels), plus
+//                   one with every value 1 for the row sums.
+// Items are (sequence, group of 64 heads, partition of P tokens), P a power
+// of two from 1024 to 4096 chosen on the device (the largest not above the
+// latent tokens per CU); a row of one partition is written at once, the
+// partials of split rows are merged by lse_merge_kernel.
+
+#include "pa_attend.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_mfma.h"
+#include "pagedattn.h"
+
+namespace pa {
+namespace {
+
+constexpr int kMhWaves = 4;
+constexpr int kMhHeads = kMlaHeadsGroup;             // heads per workgroup (16 per wave)
+constexpr int kMhRowB = kMlaQkDim * 2;               // bytes of one latent row
+constexpr int kMhLdsRow = kMhRowB + 16;              // padded LDS row stride
+constexpr int kMhStepKeys = 32;
+constexpr int kMhChunks = kMhRowB / 16;              // 16-byte chunks per row (72)
+constexpr int kMhLoads = kMhStepKeys * kMhChunks / (kMhWaves * kWave);  // per thread per step (9)
+static_assert(kMhLoads * kMhWaves * kWave == kMhStepKeys * kMhChunks, "whole rows per step");
+constexpr int kMhQK = kMlaQkDim / 32;                // S^T products per 16 keys (18)
+constexpr int kMhDq = kMlaVDim / 64;                 // 64-element value slices (8)
+constexpr int kMhMaxBlocks = kMlaHeadsMaxPart / 16;  // table entries of the longest item
+
+template <typename T, int BS>
+__global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
+    typename T::storage* __restrict__ out, const typename T::storage* __restrict__ q,
+    const char* __restrict__ kv_pool, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int* __restrict__ ws_off, float* __restrict__ ws_ml,
+    float* __restrict__ ws_acc, float qk_scale, uint32_t q_sign_bits, int num_seqs, int num_heads,
+    int num_blocks, int max_blocks, int max_items, int slots) {
+  using S16 = typename T::storage;
+  using M = Mfma<T>;
+  using PV = PvOps<T, 2>;
+  using pw_t = typename PV::word_t;
+  constexpr int kThreads = kMhWaves * kWave;
+  constexpr int kPer = (kMlaHeadsMaxSeqs + kThreads - 1) / kThreads;
+  constexpr int kMinShift = __builtin_ctz(kMlaHeadsMinPart);
+  constexpr int kMaxShift = __builtin_ctz(kMlaHeadsMaxPart);
+  constexpr int kParts = kMaxShift - kMinShift + 1;
+  __shared__ int s_off[kMlaHeadsMaxSeqs + 1];
+  __shared__ int s_len[kMlaHeadsMaxSeqs];
+  __shared__ int s_wsum[kParts][kMhWaves];
+  __shared__ int s_wtok[kMhWaves];
+  __shared__ int s_tbl[kMhMaxBlocks];
+  // the workgroup's 64 query rows and two steps of latent rows (padded rows)
+  __shared__ __attribute__((aligned(16))) char s_q[kMhHeads * kMhLdsRow];
+  __shared__ __attribute__((aligned(16))) char s_rows[2][kMhStepKeys * kMhLdsRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int S = num_seqs;
+  const int NG = (num_heads + kMhHeads - 1) / kMhHeads;  // head groups per sequence
+  const int cap = max_blocks * BS;
+
+  // 1. lengths, items per sequence (NG * ceil(L / P)) for every candidate P,
+  //    and the total of latent tokens
+  for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);
+  __syncthreads();
+  int mine[kParts];
+#pragma unroll
+  for (int c = 0; c < kParts; ++c) mine[c] = 0;
+  int mine_tok = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    const int L = s < S ? s_len[s] : 0;
+    mine_tok += L;
+#pragma unroll
+    for (int c = 0; c < kParts; ++c) mine[c] += NG * ((L + (1 << (kMaxShift - c)) - 1) >> (kMaxShift - c));
+  }
+  int incl[kParts];
+#pragma unroll
+  for (int c = 0; c < kParts; ++c) {
+    incl[c] = wave_prefix_sum(mine[c]);
+    if (lane == kWave - 1) s_wsum[c][wave] = incl[c];
+  }
+  const int incl_tok = wave_prefix_sum(mine_tok);
+  if (lane == kWave - 1) s_wtok[wave] = incl_tok;
+  __syncthreads();
+  // the partition: the largest candidate not above the latent tokens (times
+  // head groups) per CU — one long item per CU for long contexts
+  long long tokens = 0;
+#pragma unroll
+  for (int w = 0; w < kMhWaves; ++w) tokens += s_wtok[w];
+  const long long per_slot = static_cast<long long>(NG) * tokens / max(slots, 1);
+  int ci = kParts - 1;
+  int total = 0;
+  int run = 0;
+#pragma unroll
+  for (int c = kParts - 1; c >= 0; --c) {
+    int tot = 0, bef = 0;
+#pragma unroll
+    for (int w = 0; w < kMhWaves; ++w) {
+      tot += s_wsum[c][w];
+      bef += (w < wave) ? s_wsum[c][w] : 0;
+    }
+    if (c == kParts - 1 || (1LL << (kMaxShift - c)) <= per_slot) {
+      ci = c;
+      total = tot;
+      run = bef + incl[c] - mine[c];
+    }
+  }
+  ci = __builtin_amdgcn_readfirstlane(ci);
+  const int pshift = kMaxShift - ci;
+  const int P = 1 << pshift;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = tid * kPer + i;
+    if (s < S) s_off[s] = run;
+    run += s < S ? NG * ((s_len[s] + P - 1) >> pshift) : 0;
+  }
+  total = min(__builtin_amdgcn_readfirstlane(total), max_items);
+  if (tid == 0) s_off[S] = total;
+  __syncthreads();
+  if (blockIdx.x == 0 && ws_off != nullptr) {
+    for (int s = tid; s <= S; s += kThreads) ws_off[s] = s_off[s];
+    if (tid == 0) ws_off[S + 1] = P;
+  }
+
+  // 2. empty contexts give zero rows
+  for (int s = blockIdx.x; s < S; s += gridDim.x)
+    if (s_len[s] == 0)
+      for (int i = tid; i < num_heads * kMlaVDim; i += kThreads)
+        out[static_cast<size_t>(s) * num_heads * kMlaVDim + i] = T::pack(0.f);
+
+  const u32x4 q_sign = {q_sign_bits, q_sign_bits, q_sign_bits, q_sign_bits};
+  const int col = lane % 16;
+  const int g4 = lane / 16;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0;
+    int hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= item)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(lo);
+    const int L = __builtin_amdgcn_readfirstlane(s_len[s]);
+    const int parts = (L + P - 1) >> pshift;
+    const int local = item - __builtin_amdgcn_readfirstlane(s_off[s]);
+    const int hg = local / parts;
+    const int part = local - hg * parts;
+    const int k_begin = part * P;
+    const int k_end = min(k_begin + P, L);
+    const int n_steps = (k_end - k_begin + kMhStepKeys - 1) / kMhStepKeys;
+    const int blk0 = k_begin / BS;
+    const int nblk = (k_end - k_begin + BS - 1) / BS;
+
+    // the item's block-table entries in LDS (the step loads gather per lane)
+    const int32_t* tbl = block_tables + static_cast<size_t>(s) * max_blocks;
+    for (int b = tid; b < nblk; b += kThreads) s_tbl[b] = tbl[blk0 + b];
+
+    // this wave's 16 heads; the workgroup's 64 query rows go to LDS (the B
+    // operands of S^T are read from there every step: in registers they and
+    // the O^T accumulators would not fit the register file)
+    const int h = hg * kMhHeads + wave * 16 + col;
+    const bool row_ok = h < num_heads;
+    {
+      const S16* qg = q + (static_cast<size_t>(s) * num_heads + hg * kMhHeads) * kMlaQkDim;
+      constexpr int kQLoads = kMhHeads * kMhChunks / kThreads;  // 18 per thread
+#pragma unroll
+      for (int i0 = 0; i0 < kQLoads; i0 += kMhLoads) {
+        u32x4 r[kMhLoads];
+#pragma unroll
+        for (int i = 0; i < kMhLoads; ++i) {
+          const int x = tid + (i0 + i) * kThreads;
+          const int row = x / kMhChunks;
+          const int chunk = x - row * kMhChunks;
+          const bool ok = hg * kMhHeads + row < num_heads;
+          // a negative scale flips q's signs instead
+          r[i] = ok ? (load16(reinterpret_cast<const char*>(qg + static_cast<size_t>(row) * kMlaQkDim) + chunk * 16) ^
+                       q_sign)
+                    : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < kMhLoads; ++i) {
+          const int x = tid + (i0 + i) * kThreads;
+          const int row = x / kMhChunks;
+          const int chunk = x - row * kMhChunks;
+          *reinterpret_cast<u32x4*>(&s_q[row * kMhLdsRow + chunk * 16]) = r[i];
+        }
+      }
+    }
+    float m = -INFINITY;
+    f4_t lacc = {0.f, 0.f, 0.f, 0.f};
+    f4_t acc[kMhDq][4];
+#pragma unroll
+    for (int dq = 0; dq < kMhDq; ++dq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[dq][e] = f4_t{0.f, 0.f, 0.f, 0.f};
+    int bad = 0;
+    __syncthreads();  // s_tbl and s_q written; the previous item's LDS rows no longer read
+
+    // cooperative load of one step's 32 rows: thread chunk x = tid + 256 i
+    // covers row x / 72, 16-byte chunk x % 72; keys past the item's end read
+    // the step's first row instead (their table entry may not exist; they
+    // are masked)
+    auto load_step = [&](u32x4 (&r)[kMhLoads], int step) __attribute__((always_inline)) {
+      const int c0 = k_begin + step * kMhStepKeys;
+#pragma unroll
+      for (int i = 0; i < kMhLoads; ++i) {
+        const int x = tid + i * kThreads;
+        const int key = x / kMhChunks;
+        const int chunk = x - key * kMhChunks;
+        const int k = (c0 + key < k_end) ? c0 + key : c0;
+        int phys = s_tbl[k / BS - blk0];
+        if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
+          bad = 1;  // never dereference an id outside the pool
+          phys = 0;
+        }
+        r[i] = load16(kv_pool + (static_cast<size_t>(phys) * BS + k % BS) * kMhRowB + chunk * 16);
+      }
+    };
+    auto store_step = [&](const u32x4 (&r)[kMhLoads], int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < kMhLoads; ++i) {
+        const int x = tid + i * kThreads;
+        const int key = x / kMhChunks;
+        const int chunk = x - key * kMhChunks;
+        *reinterpret_cast<u32x4*>(&s_rows[buf][key * kMhLdsRow + chunk * 16]) = r[i];
+      }
+    };
+
+    auto compute_step = [&](int buf, int step) __attribute__((always_inline)) {
+      const int c0 = k_begin + step * kMhStepKeys;
+      const char* rows = s_rows[buf];
+      // S^T: the 36 operand loads of the two blocks in chunks of kQc, each
+      // chunk's loads issued before the previous chunk's products (the
+      // scheduling barriers keep the compiler from hoisting every load at
+      // once, which would not fit the register file)
+      // S^T over the 576 elements, kQc 32-element slices at a time: the K
+      // operands of both blocks and the wave's query operands from LDS, the
+      // next chunk's loads issued before this chunk's products (scheduling
+      // barriers keep the compiler from hoisting every load at once)
+      f4_t sc[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
+      constexpr int kQc = 2;
+      constexpr int kChunksQ = kMhQK / kQc;
+      u32x4 kbuf[2][2][kQc], qbuf[2][kQc];
+      const char* qrow = s_q + (wave * 16 + col) * kMhLdsRow + 16 * g4;
+      auto load_qc = [&](int ch, u32x4 (&kd)[2][kQc], u32x4 (&qd)[kQc]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kQc; ++j) {
+          const int off = 64 * (ch * kQc + j);
+          qd[j] = *reinterpret_cast<const u32x4*>(qrow + off);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            kd[kb][j] = *reinterpret_cast<const u32x4*>(rows + (16 * kb + col) * kMhLdsRow + 16 * g4 + off);
+        }
+      };
+      load_qc(0, kbuf[0], qbuf[0]);
+#pragma unroll
+      for (int ch = 0; ch < kChunksQ; ++ch) {
+        if (ch + 1 < kChunksQ) load_qc(ch + 1, kbuf[(ch + 1) & 1], qbuf[(ch + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kQc; ++j)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) sc[kb] = M::qk(kbuf[ch & 1][kb][j], qbuf[ch & 1][j], sc[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bool masked = c0 + kMhStepKeys > k_end;
+      float z[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          z[kb][i] = (!masked || c0 + 16 * kb + 4 * g4 + i < k_end) ? sc[kb][i] : -INFINITY;
+      float cm = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+      cm = fold_max<16>(cm);
+      const float cms = (cm == -INFINITY) ? -INFINITY : cm * qk_scale;
+      const float mn = fmaxf(m, cms);
+      if (__builtin_amdgcn_ballot_w64(mn > m + kRescaleLog2) != 0) {
+        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+        lacc *= alpha;
+#pragma unroll
+        for (int dq = 0; dq < kMhDq; ++dq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[dq][e] *= alpha;
+        m = mn;
+      }
+      const float nm = -m;
+      float p[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
+          p[kb][i] = (masked && z[kb][i] == -INFINITY) ? 0.f : x;
+        }
+      const pw_t pw = {M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3]), M::pack2(p[1][0], p[1][1]),
+                       M::pack2(p[1][2], p[1][3])};
+      // V^T operand: lane l reads 4 latent values (64dq + 4col ..) of its 8
+      // keys (4*g4 + e of both blocks) and permutes them by column
+      u32x2 vbuf[2][2][4];
+      auto load_vc = [&](int dq, u32x2 (&dst)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dst[kb][e] = *reinterpret_cast<const u32x2*>(rows + (16 * kb + 4 * g4 + e) * kMhLdsRow + (64 * dq + 4 * col) * 2);
+      };
+      load_vc(0, vbuf[0]);
+#pragma unroll
+      for (int dq = 0; dq < kMhDq; ++dq) {
+        if (dq + 1 < kMhDq) load_vc(dq + 1, vbuf[(dq + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x2 (&v)[2][4] = vbuf[dq & 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const pw_t a = {col_pair(v[0][0], v[0][1], e), col_pair(v[0][2], v[0][3], e), col_pair(v[1][0], v[1][1], e),
+                          col_pair(v[1][2], v[1][3], e)};
+          acc[dq][e] = PV::mma(a, pw, acc[dq][e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const pw_t ones = {M::kOnes, M::kOnes, M::kOnes, M::kOnes};
+      lacc = PV::mma(ones, pw, lacc);
+    };
+
+    // steps: LDS double-buffered, the next step's rows in flight in registers
+    // while a step is computed, one barrier per step
+    u32x4 ra[kMhLoads];
+    load_step(ra, 0);
+    store_step(ra, 0);
+    __syncthreads();
+    if (n_steps > 1) load_step(ra, 1);
+    for (int st = 0; st < n_steps; ++st) {
+      compute_step(st & 1, st);
+      if (st + 1 < n_steps) store_step(ra, (st + 1) & 1);
+      __syncthreads();
+      if (st + 2 < n_steps) load_step(ra, st + 2);
+    }
+
+    // 3. this wave's 16 rows: the output (one partition) or a partial;
+    //    lane l holds row col's value elements 64*dq + 16*g4 + 4*i + e
+    const int any_bad = __syncthreads_or(bad);
+    float lrow = lacc[0];  // the row sum (every element of the ones product holds it)
+    if (any_bad) lrow = __builtin_nanf("");
+    if (parts == 1) {
+      if (row_ok) {
+        const float inv = 1.f / lrow;
+        S16* orow = out + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 16 * g4;
+#pragma unroll
+        for (int dq = 0; dq < kMhDq; ++dq) {
+          uint32_t w[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            w[2 * i] = M::pack2(acc[dq][0][i] * inv, acc[dq][1][i] * inv);
+            w[2 * i + 1] = M::pack2(acc[dq][2][i] * inv, acc[dq][3][i] * inv);
+          }
+          store16(orow + 64 * dq, u32x4{w[0], w[1], w[2], w[3]});
+          store16(orow + 64 * dq + 8, u32x4{w[4], w[5], w[6], w[7]});
+        }
+      }
+    } else {
+      const size_t slot = static_cast<size_t>(item) * kMhHeads + wave * 16 + col;
+      if (g4 == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{m, lrow};
+      float* av = ws_acc + slot * kMlaVDim + 16 * g4;
+#pragma unroll
+      for (int dq = 0; dq < kMhDq; ++dq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f4_t*>(av + 64 * dq + 4 * i) = f4_t{acc[dq][0][i], acc[dq][1][i], acc[dq][2][i], acc[dq][3][i]};
+    }
+  }
+}
+
+constexpr int kMlaMergeThreads = 128;  // one lane group of 128 lanes x 4 sums per 512-element partial
+
+template <typename T, int BS>
+hipError_t run_mla_heads(const PrefillArgs& a, hipStream_t stream) {
+  using S16 = typename T::storage;
+  hipLaunchKernelGGL((mla_heads_kernel<T, BS>), dim3(a.workgroups), dim3(kMhWaves * kWave), 0, stream,
+                     static_cast<S16*>(a.out), static_cast<const S16*>(a.q), static_cast<const char*>(a.k_pool),
+                     a.block_tables, a.context_lens, a.ws_off, a.ws_ml, a.ws_acc, fabsf(a.scale) * kLog2e,
+                     a.scale < 0.f ? 0x80008000u : 0u, a.num_seqs, a.num_heads, a.num_blocks, a.max_blocks_per_seq,
+                     a.max_items, a.slots);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ws_ml == nullptr) return e;
+  hipLaunchKernelGGL((lse_merge_kernel<T, kMlaVDim, kMlaVDim, kMlaMergeThreads>), dim3(a.num_seqs * a.num_heads),
+                     dim3(kMlaMergeThreads), 0, stream, static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc,
+                     a.context_lens, a.num_seqs, a.num_heads, kMhHeads, a.max_blocks_per_seq * a.block_size);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_mla_heads_t(const PrefillArgs& a, hipStream_t stream) {
+  return a.block_size == 16 ? run_mla_heads<T, 16>(a, stream) : run_mla_heads<T, 32>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_mla_heads(const PrefillArgs& a, hipStream_t stream) {
+  return a.dtype == PA_DTYPE_BF16 ? run_mla_heads_t<BF16>(a, stream) : run_mla_heads_t<F16>(a, stream);
+}
+
+}  // namespace pa

@@ -101,3 +101,54 @@ def test_more_sequences_than_one_launch_holds():
     lens = rng.integers(0, 40, size=2100).tolist()
     c = LatentCase(lens, 16, 16, torch.bfloat16, 98)
     assert_close(c.run(), c.oracle(), torch.bfloat16, "2100 sequences")
+
+
+# ---- many heads: the workgroup-per-64-heads kernel (default split, >= 64 heads)
+
+@pytest.mark.parametrize("H", [64, 96, 128, 192])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_many_heads(H, dtype):
+    """64 heads (one full group), 96 (a full and a half group), 128, 192;
+    contexts of one partition and of several (merged by the second kernel),
+    empty ones, NaN-poisoned unreferenced slots."""
+    announce(f"mla many heads H={H} {dtype}")
+    c = LatentCase([0, 1, 700, 33, 9000, 16, 4100], H, 16, dtype, 190 + H)
+    out = c.run()
+    assert_close(out, c.oracle(), dtype, f"many heads H={H}")
+    assert not out[0].any()
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_many_heads_long_context_and_block_sizes(bs):
+    announce(f"mla many heads long bs={bs}")
+    c = LatentCase([20000, 3000], 128, bs, torch.bfloat16, 200 + bs)
+    assert_close(c.run(), c.oracle(), torch.bfloat16, f"many heads bs={bs}")
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_many_heads_negative_and_zero_scale(scale):
+    announce(f"mla many heads scale {scale}")
+    c = LatentCase([900, 5000], 64, 16, torch.float16, 210)
+    c.scale = scale
+    assert_close(c.run(), c.oracle(), torch.float16, f"scale {scale}")
+
+
+def test_many_heads_out_of_pool_id():
+    announce("mla many heads bad id")
+    c = LatentCase([1000, 6000, 50], 128, 16, torch.bfloat16, 211)
+    bt = torch.from_numpy(c.tables).to(DEV)
+    bt[1, 100] = -3
+    out = c.run(tables=bt)
+    assert torch.isnan(out[1].float()).all()
+    ref = c.oracle()
+    assert_close(out[[0, 2]], ref[[0, 2]], torch.bfloat16, "other sequences")
+
+
+def test_many_heads_more_sequences_than_the_kernel_takes():
+    """600 sequences with 64 heads: past the many-heads kernel's 512, the call
+    takes the split kernel; the result is the same attention."""
+    announce("mla many heads 600 sequences")
+    rng = np.random.default_rng(212)
+    lens = rng.integers(0, 60, size=600).tolist()
+    c = LatentCase(lens, 64, 16, torch.bfloat16, 212)
+    assert_close(c.run(), c.oracle(), torch.bfloat16, "600 sequences")
