@@ -45,13 +45,14 @@ COLD_BYTES = 2 << 30           # replica footprint that defeats the 256 MB last-
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_decode_balanced.hip", "pa_decode_balanced_gqa2.hip",
-                            "pa_decode_balanced_gqa4.hip",
-                            "pa_balanced_kernel.h", "pa_attend.h", "pa_device.h", "pa_internal.h",
+                            "pa_decode_balanced_gqa4.hip", "pa_decode_mfma.hip",
+                            "pa_balanced_kernel.h", "pa_attend.h", "pa_device.h", "pa_mfma.h", "pa_internal.h",
                             "pa_api.cpp")]
 
 
 PF_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
-              for f in ("pa_prefill.hip", "pa_attend.h", "pa_device.h", "pa_internal.h", "pa_api.cpp")]
+              for f in ("pa_prefill.hip", "pa_mla_heads.hip", "pa_attend.h", "pa_device.h", "pa_mfma.h",
+                        "pa_internal.h", "pa_api.cpp")]
 
 
 def log(msg: str) -> None:
@@ -442,7 +443,10 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
     mfma_bound = op == "prefill"
     digest = kernel_source_digest(PF_SOURCES)
     tag = op + (f"_h{H}" if heads else "") + (f"_p{partition}" if partition else "")
-    kernel = "mla_split_kernel" if mla else "prefill_kernel"
+    # pa_decode_mla takes its many-heads kernel from 64 heads (default split,
+    # up to 512 sequences)
+    kernel = (("mla_heads_kernel" if H >= 64 and not partition and S <= 512 else "mla_split_kernel") if mla
+              else "prefill_kernel")
     traffic = traffic_from_profile(digest, os.path.join(PROFILES, f"{kernel}_{tag}_traffic.txt"))
     metric = {"prefill": "chunked prefill over the paged cache (pa_prefill): achieved TFLOP/s, 1 MI355X",
               "verify": "speculative verification over the paged cache (pa_prefill): achieved HBM GB/s, 1 MI355X",

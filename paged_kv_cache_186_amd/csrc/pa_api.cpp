@@ -4,6 +4,7 @@
 // check returns a status and launches nothing.  No allocation; the only state
 // is the per-device address of pa_decode_noalloc's static scratch array.
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -452,24 +453,33 @@ MlaHeadsPlan plan_mla_heads(int32_t num_seqs, int32_t num_heads, int32_t max_blo
   }
   const long long ctx = static_cast<long long>(max_blocks_per_seq) * block_size;
   const long long groups = (num_heads + pa::kMlaHeadsGroup - 1) / pa::kMlaHeadsGroup;
-  const long long items =
-      static_cast<long long>(num_seqs) * groups * ((ctx + pa::kMlaHeadsMinPart - 1) / pa::kMlaHeadsMinPart);
+  // the kernel picks its partition P on the device: below the largest size
+  // only when that leaves at most one item per resident workgroup (one per
+  // CU), so the items number at most max(slots, rows * ceil(ctx / largest))
+  // and never more than at the smallest size
+  const long long rows = static_cast<long long>(num_seqs) * groups;
+  const long long slots = cu_count();
+  const long long at_min = rows * ((ctx + pa::kMlaHeadsMinPart - 1) / pa::kMlaHeadsMinPart);
+  const long long at_max = rows * ((ctx + pa::kMlaHeadsMaxPart - 1) / pa::kMlaHeadsMaxPart);
+  const long long items = std::min(at_min, std::max(slots, at_max));
   if (items > INT_MAX / pa::kMlaHeadsGroup) {
     p.status = PA_ERR_INVALID_ARG;
     return p;
   }
   p.max_items = static_cast<int>(items);
   if (!sizes_only) {
-    const long long per_cu = static_cast<long long>(num_seqs) * groups * ctx / cu_count();
-    int pt = pa::kMlaHeadsMaxPart;
-    while (pt > pa::kMlaHeadsMinPart && pt > per_cu) pt /= 2;
-    const long long grid = static_cast<long long>(num_seqs) * groups * ((ctx + pt - 1) / pt);
-    p.workgroups = static_cast<int>(grid < 1 ? 1 : (grid > pa::kMlaHeadsMaxWorkgroups ? pa::kMlaHeadsMaxWorkgroups : grid));
+    const long long grid = std::min(items, slots);
+    p.workgroups = static_cast<int>(grid < 1 ? 1 : grid);
   }
   if (ctx > pa::kMlaHeadsMinPart) {  // a row can span several partitions
-    p.ws = pa::workspace_layout(0, static_cast<size_t>(items) * pa::kMlaHeadsGroup, pa::kMlaVDim);
-    p.off_offset = p.ws.total;
-    p.ws.total = pa::align_up(p.ws.total + (static_cast<size_t>(num_seqs) + 2) * sizeof(int), 256);
+    // per item and head the partial's (max, sum) in fp32 and its 512
+    // normalised values in the output type (2 bytes); then the S + 2 item
+    // offsets and partition size the merge reads
+    const size_t slots_n = static_cast<size_t>(items) * pa::kMlaHeadsGroup;
+    p.ws.ml_offset = 0;
+    p.ws.acc_offset = pa::align_up(slots_n * 2 * sizeof(float), 256);
+    p.off_offset = pa::align_up(p.ws.acc_offset + slots_n * pa::kMlaVDim * 2, 256);
+    p.ws.total = pa::align_up(p.off_offset + (static_cast<size_t>(num_seqs) + 2) * sizeof(int), 256);
   }
   return p;
 }
@@ -516,7 +526,7 @@ pa_status_t mla_heads_impl(void* out, const void* q, const void* kv_pool, const 
   if (plan.ws.total > 0) {
     char* ws = static_cast<char*>(workspace);
     a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
-    a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
+    a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);  // the 2-byte partials
     a.ws_off = reinterpret_cast<int*>(ws + plan.off_offset);
   }
   return pa::launch_mla_heads(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;

@@ -240,6 +240,29 @@ __device__ __forceinline__ void swap_pair(float x, float& lo, float& hi) {
   hi = __builtin_bit_cast(float, b);
 }
 
+// ceil(x / d) for 0 <= x < 2^31 and 0 < d < 2^20, given rd = 1.0 / d in
+// double precision: the product's relative error (below 2^-52) can only
+// take an exact quotient k to just under k, so the truncated estimate is
+// floor(x / d) or one less, and one remainder test corrects it.
+__device__ __forceinline__ int ceil_div_nonneg(int x, int d, double rd) {
+  int q = static_cast<int>(static_cast<double>(x) * rd);
+  int r = x - q * d;
+  if (r >= d) {
+    ++q;
+    r -= d;
+  }
+  return q + (r > 0 ? 1 : 0);
+}
+
+// Logical index of workgroup b of a G-workgroup grid such that consecutive
+// logical indices run on one XCD: the dispatcher deals workgroups to the 8
+// XCDs in turn (b goes to XCD b % 8), so XCD x holds the x-th contiguous
+// range of logical indices (G / 8 of them, one more for the first G % 8).
+__device__ __forceinline__ int xcd_local_index(int b, int G) {
+  const int x = b & 7;
+  return x * (G >> 3) + min(x, G & 7) + (b >> 3);
+}
+
 // Inclusive prefix sum of x over the 64 lanes of a wave, in DPP steps (no
 // LDS round trips): sums within each 16-lane row by shifts of 1, 2, 4 and 8
 // lanes (a lane shifted in from outside the row reads 0), then the total of

@@ -217,14 +217,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // the latent cache: one workgroup per (sequence, 16 heads, partition), the
 // 576 elements of a row split across its four waves
 hipError_t launch_mla_split(const PrefillArgs& a, hipStream_t stream);
-// the latent cache with many heads: one workgroup per (sequence, 64 heads,
-// partition of 1024..4096 tokens), each wave 16 heads over the whole row, the
-// rows staged in LDS once per workgroup; split rows merged by a second kernel
+// the latent cache with many heads: items (sequence, partition of 256..4096
+// tokens, 64 heads), one workgroup per CU, each wave 16 heads over the whole
+// row, the rows staged in LDS once per workgroup; split rows merged by a
+// second kernel
 constexpr int kMlaHeadsMin = 64;        // heads from which pa_decode_mla takes this kernel
 constexpr int kMlaHeadsGroup = 64;      // heads per workgroup
-constexpr int kMlaHeadsMinPart = 1024;  // partition candidates (tokens)
+constexpr int kMlaHeadsMinPart = 256;   // partition sizes (tokens, multiples of 32)
 constexpr int kMlaHeadsMaxPart = 4096;
-constexpr int kMlaHeadsMaxWorkgroups = 1024;
 constexpr int kMlaHeadsMaxSeqs = 512;   // per-sequence offsets in LDS beside the rows and queries
 hipError_t launch_mla_heads(const PrefillArgs& a, hipStream_t stream);
 

@@ -30,10 +30,15 @@
 //   O^T += V^T P^T  32 products over the 512 latent values (A = V transposed
 //                   from LDS by byte permutes, as in the query kernels), plus
 //                   one with every value 1 for the row sums.
-// Items are (sequence, group of 64 heads, partition of P tokens), P a power
-// of two from 1024 to 4096 chosen on the device (the largest not above the
-// latent tokens per CU); a row of one partition is written at once, the
-// partials of split rows are merged by lse_merge_kernel.
+// Items are (sequence, partition of P tokens, group of 64 heads), in that
+// order, one workgroup per CU.  P, a multiple of 32 from 256 to 4096, is
+// chosen on the device from the lengths: the smallest of eight sizes between
+// the two bounds below that gives every workgroup at most one item, so that
+// the longest item, which sets the kernel's time, is as short as the lengths
+// allow.  Consecutive items run on one XCD, so the head groups of a
+// partition, which read the same rows, share that XCD's L2.  A row of one
+// partition is written at once, the partials of split rows are merged by
+// lse_merge_kernel.
 
 #include "pa_attend.h"
 #include "pa_device.h"
@@ -56,26 +61,49 @@ constexpr int kMhQK = kMlaQkDim / 32;                // S^T products per 16 keys
 constexpr int kMhDq = kMlaVDim / 64;                 // 64-element value slices (8)
 constexpr int kMhMaxBlocks = kMlaHeadsMaxPart / 16;  // table entries of the longest item
 
+// A lane's share of one head's 512 outputs: eight 16-element chunks (per
+// 64-element slice dq, the chunk 64 dq + 16 g4 .. + 15, element 4 i + e of
+// it in acc[dq][e][i]), scaled by inv and packed two to a word: element
+// 4 i + e goes to word 2 i + e / 2, low half for even e.
+template <typename T>
+__device__ __forceinline__ void pack_chunk(const f4_t (&a)[4], float inv, uint32_t (&w)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[2 * i] = Mfma<T>::pack2(a[0][i] * inv, a[1][i] * inv);
+    w[2 * i + 1] = Mfma<T>::pack2(a[2][i] * inv, a[3][i] * inv);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_row(typename T::storage* row, const f4_t (&acc)[kMlaVDim / 64][4], float inv) {
+#pragma unroll
+  for (int dq = 0; dq < kMlaVDim / 64; ++dq) {
+    uint32_t w[8];
+    pack_chunk<T>(acc[dq], inv, w);
+    store16(row + 64 * dq, u32x4{w[0], w[1], w[2], w[3]});
+    store16(row + 64 * dq + 8, u32x4{w[4], w[5], w[6], w[7]});
+  }
+}
+
 template <typename T, int BS>
 __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     typename T::storage* __restrict__ out, const typename T::storage* __restrict__ q,
     const char* __restrict__ kv_pool, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int* __restrict__ ws_off, float* __restrict__ ws_ml,
-    float* __restrict__ ws_acc, float qk_scale, uint32_t q_sign_bits, int num_seqs, int num_heads,
-    int num_blocks, int max_blocks, int max_items, int slots) {
+    typename T::storage* __restrict__ ws_part, float qk_scale, uint32_t q_sign_bits, int num_seqs,
+    int num_heads, int num_blocks, int max_blocks, int max_items, int slots) {
   using S16 = typename T::storage;
   using M = Mfma<T>;
   using PV = PvOps<T, 2>;
   using pw_t = typename PV::word_t;
   constexpr int kThreads = kMhWaves * kWave;
   constexpr int kPer = (kMlaHeadsMaxSeqs + kThreads - 1) / kThreads;
-  constexpr int kMinShift = __builtin_ctz(kMlaHeadsMinPart);
-  constexpr int kMaxShift = __builtin_ctz(kMlaHeadsMaxPart);
-  constexpr int kParts = kMaxShift - kMinShift + 1;
+  constexpr int kCand = 8;  // partition sizes tried
   __shared__ int s_off[kMlaHeadsMaxSeqs + 1];
   __shared__ int s_len[kMlaHeadsMaxSeqs];
-  __shared__ int s_wsum[kParts][kMhWaves];
+  __shared__ int s_wsum[kCand][kMhWaves];
   __shared__ int s_wtok[kMhWaves];
+  __shared__ int s_wpre[kMhWaves];
   __shared__ int s_tbl[kMhMaxBlocks];
   // the workgroup's 64 query rows and two steps of latent rows (padded rows)
   __shared__ __attribute__((aligned(16))) char s_q[kMhHeads * kMhLdsRow];
@@ -88,72 +116,105 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
   const int NG = (num_heads + kMhHeads - 1) / kMhHeads;  // head groups per sequence
   const int cap = max_blocks * BS;
 
-  // 1. lengths, items per sequence (NG * ceil(L / P)) for every candidate P,
-  //    and the total of latent tokens
+  // 1. lengths (thread t holds sequences kPer t ..) and their total
   for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);
   __syncthreads();
-  int mine[kParts];
-#pragma unroll
-  for (int c = 0; c < kParts; ++c) mine[c] = 0;
+  int lens[kPer];
   int mine_tok = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int s = tid * kPer + i;
-    const int L = s < S ? s_len[s] : 0;
-    mine_tok += L;
-#pragma unroll
-    for (int c = 0; c < kParts; ++c) mine[c] += NG * ((L + (1 << (kMaxShift - c)) - 1) >> (kMaxShift - c));
-  }
-  int incl[kParts];
-#pragma unroll
-  for (int c = 0; c < kParts; ++c) {
-    incl[c] = wave_prefix_sum(mine[c]);
-    if (lane == kWave - 1) s_wsum[c][wave] = incl[c];
+    lens[i] = s < S ? s_len[s] : 0;
+    mine_tok += lens[i];
   }
   const int incl_tok = wave_prefix_sum(mine_tok);
   if (lane == kWave - 1) s_wtok[wave] = incl_tok;
   __syncthreads();
-  // the partition: the largest candidate not above the latent tokens (times
-  // head groups) per CU — one long item per CU for long contexts
   long long tokens = 0;
 #pragma unroll
   for (int w = 0; w < kMhWaves; ++w) tokens += s_wtok[w];
-  const long long per_slot = static_cast<long long>(NG) * tokens / max(slots, 1);
-  int ci = kParts - 1;
-  int total = 0;
-  int run = 0;
+
+  // 2. the partition P, a multiple of the 32-key step: items (sequence,
+  //    partition, head group) number NG * sum ceil(L / P); the smallest P
+  //    with at most one item per resident workgroup is wanted.  NG * tokens
+  //    / slots bounds it from below, NG * tokens / (slots - NG * S) from
+  //    above (each sequence adds less than one partition); kCand sizes
+  //    spaced geometrically between the two are counted, the smallest that
+  //    fits is taken (else the largest), clamped to [min, max] partition.
+  const long long work = static_cast<long long>(NG) * tokens;
+  const int free_slots = slots - NG * S;
+  auto round_part = [](long long x) {
+    x = (x + kMhStepKeys - 1) / kMhStepKeys * kMhStepKeys;
+    return static_cast<int>(min(max(x, static_cast<long long>(kMlaHeadsMinPart)),
+                                static_cast<long long>(kMlaHeadsMaxPart)));
+  };
+  const int p_lo = round_part((work + slots - 1) / max(slots, 1));
+  const int p_hi = free_slots > 0 ? max(p_lo, round_part((work + free_slots - 1) / free_slots)) : kMlaHeadsMaxPart;
+  const float lg = log2f(static_cast<float>(p_hi) / static_cast<float>(p_lo));
+  int cand[kCand];
+  double rcand[kCand];
+  int cnt[kCand];
 #pragma unroll
-  for (int c = kParts - 1; c >= 0; --c) {
-    int tot = 0, bef = 0;
-#pragma unroll
-    for (int w = 0; w < kMhWaves; ++w) {
-      tot += s_wsum[c][w];
-      bef += (w < wave) ? s_wsum[c][w] : 0;
-    }
-    if (c == kParts - 1 || (1LL << (kMaxShift - c)) <= per_slot) {
-      ci = c;
-      total = tot;
-      run = bef + incl[c] - mine[c];
-    }
+  for (int c = 0; c < kCand; ++c) {
+    const float x = static_cast<float>(p_lo) * exp2f(lg * c / (kCand - 1));
+    cand[c] = (c == kCand - 1) ? p_hi : min(round_part(static_cast<long long>(x)), p_hi);
+    rcand[c] = 1.0 / cand[c];
+    cnt[c] = 0;
   }
-  ci = __builtin_amdgcn_readfirstlane(ci);
-  const int pshift = kMaxShift - ci;
-  const int P = 1 << pshift;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+#pragma unroll
+    for (int c = 0; c < kCand; ++c) cnt[c] += ceil_div_nonneg(lens[i], cand[c], rcand[c]);
+#pragma unroll
+  for (int c = 0; c < kCand; ++c) {
+    const int incl = wave_prefix_sum(cnt[c]);
+    if (lane == kWave - 1) s_wsum[c][wave] = incl;
+  }
+  __syncthreads();
+  int P = cand[kCand - 1];
+#pragma unroll
+  for (int c = kCand - 1; c >= 0; --c) {
+    long long tot = 0;
+#pragma unroll
+    for (int w = 0; w < kMhWaves; ++w) tot += s_wsum[c][w];
+    if (static_cast<long long>(NG) * tot <= slots) P = cand[c];
+  }
+  P = __builtin_amdgcn_readfirstlane(P);
+
+  // 3. item offsets of the sequences for that P
+  const double rP = 1.0 / P;
+  int parts_of[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    parts_of[i] = ceil_div_nonneg(lens[i], P, rP);
+    mine += NG * parts_of[i];
+  }
+  const int incl = wave_prefix_sum(mine);
+  if (lane == kWave - 1) s_wpre[wave] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kMhWaves; ++w) {
+    run += (w < wave) ? s_wpre[w] : 0;
+    total += s_wpre[w];
+  }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int s = tid * kPer + i;
     if (s < S) s_off[s] = run;
-    run += s < S ? NG * ((s_len[s] + P - 1) >> pshift) : 0;
+    run += NG * parts_of[i];
   }
   total = min(__builtin_amdgcn_readfirstlane(total), max_items);
   if (tid == 0) s_off[S] = total;
   __syncthreads();
-  if (blockIdx.x == 0 && ws_off != nullptr) {
+  if (blockIdx.x == 0 && ws_off != nullptr) {  // for the merge
     for (int s = tid; s <= S; s += kThreads) ws_off[s] = s_off[s];
     if (tid == 0) ws_off[S + 1] = P;
   }
 
-  // 2. empty contexts give zero rows
+  // 4. empty contexts give zero rows
   for (int s = blockIdx.x; s < S; s += gridDim.x)
     if (s_len[s] == 0)
       for (int i = tid; i < num_heads * kMlaVDim; i += kThreads)
@@ -163,7 +224,10 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
   const int col = lane % 16;
   const int g4 = lane / 16;
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  // items in order (sequence, partition, head group); workgroup b runs on
+  // XCD b % 8, and its logical index makes consecutive items share an XCD:
+  // the head groups of one partition read the same rows through one L2
+  for (int item = xcd_local_index(blockIdx.x, gridDim.x); item < total; item += gridDim.x) {
     int lo = 0;
     int hi = S - 1;
     while (lo < hi) {
@@ -175,10 +239,10 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     }
     const int s = __builtin_amdgcn_readfirstlane(lo);
     const int L = __builtin_amdgcn_readfirstlane(s_len[s]);
-    const int parts = (L + P - 1) >> pshift;
+    const int parts = (L + P - 1) / P;
     const int local = item - __builtin_amdgcn_readfirstlane(s_off[s]);
-    const int hg = local / parts;
-    const int part = local - hg * parts;
+    const int part = local / NG;
+    const int hg = local - part * NG;
     const int k_begin = part * P;
     const int k_end = min(k_begin + P, L);
     const int n_steps = (k_end - k_begin + kMhStepKeys - 1) / kMhStepKeys;
@@ -371,55 +435,108 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
       if (st + 2 < n_steps) load_step(ra, st + 2);
     }
 
-    // 3. this wave's 16 rows: the output (one partition) or a partial;
-    //    lane l holds row col's value elements 64*dq + 16*g4 + 4*i + e
+    // 5. this wave's 16 rows; lane l holds row col's value elements
+    //    64 dq + 16 g4 + 4 i + e in acc[dq][e][i]
+    // (the output and workspace addresses are formed only here: opaque
+    // copies of the base pointers keep the compiler from computing them
+    // before the steps and holding them in registers across the loop)
+    S16* out_b = out;
+    S16* part_b = ws_part;
+    float* ml_b = ws_ml;
+    asm volatile("" : "+s"(out_b), "+s"(part_b), "+s"(ml_b));
     const int any_bad = __syncthreads_or(bad);
     float lrow = lacc[0];  // the row sum (every element of the ones product holds it)
     if (any_bad) lrow = __builtin_nanf("");
+    S16* orow = out_b + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 16 * g4;
     if (parts == 1) {
-      if (row_ok) {
-        const float inv = 1.f / lrow;
-        S16* orow = out + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 16 * g4;
-#pragma unroll
-        for (int dq = 0; dq < kMhDq; ++dq) {
-          uint32_t w[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            w[2 * i] = M::pack2(acc[dq][0][i] * inv, acc[dq][1][i] * inv);
-            w[2 * i + 1] = M::pack2(acc[dq][2][i] * inv, acc[dq][3][i] * inv);
-          }
-          store16(orow + 64 * dq, u32x4{w[0], w[1], w[2], w[3]});
-          store16(orow + 64 * dq + 8, u32x4{w[4], w[5], w[6], w[7]});
-        }
-      }
-    } else {
-      const size_t slot = static_cast<size_t>(item) * kMhHeads + wave * 16 + col;
-      if (g4 == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{m, lrow};
-      float* av = ws_acc + slot * kMlaVDim + 16 * g4;
-#pragma unroll
-      for (int dq = 0; dq < kMhDq; ++dq)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<f4_t*>(av + 64 * dq + 4 * i) = f4_t{acc[dq][0][i], acc[dq][1][i], acc[dq][2][i], acc[dq][3][i]};
+      if (row_ok) store_row<T>(orow, acc, 1.f / lrow);
+      continue;
     }
+    // a split row: the item's partial, normalised and rounded to the output
+    // type, and its (max, sum) in fp32, for mla_merge_kernel
+    const size_t slot = static_cast<size_t>(item) * kMhHeads + wave * 16 + col;
+    store_row<T>(part_b + slot * kMlaVDim + 16 * g4, acc, 1.f / lrow);
+    if (g4 == 0) *reinterpret_cast<f32x2*>(ml_b + slot * 2) = f32x2{m, lrow};
   }
 }
 
-constexpr int kMlaMergeThreads = 128;  // one lane group of 128 lanes x 4 sums per 512-element partial
+// The rows split over several partitions: one wave per (sequence, head),
+// lane l owning elements 8 l .. 8 l + 7.  A partial holds o_p = acc_p / l_p
+// (output type) and (m_p, l_p); the row is sum_p w_p o_p / sum_p w_p with
+// w_p = l_p 2^(m_p - M), M the running maximum, folded in partition order
+// with kU partials' loads in flight.  Item (sequence s, partition p, head
+// group g) is off[s] + p * NG + g, off[] and P as the first kernel wrote them.
+template <typename T>
+__global__ __launch_bounds__(kWave) void mla_merge_kernel(typename T::storage* __restrict__ out,
+                                                          const int* __restrict__ ws_off,
+                                                          const float* __restrict__ ws_ml,
+                                                          const typename T::storage* __restrict__ ws_part,
+                                                          const int32_t* __restrict__ context_lens, int num_seqs,
+                                                          int num_heads, int cap) {
+  constexpr int kU = 8;
+  const int s = blockIdx.x / num_heads;
+  const int h = blockIdx.x % num_heads;
+  const int NG = (num_heads + kMhHeads - 1) / kMhHeads;
+  const int L = min(max(context_lens[s], 0), cap);
+  const int P = ws_off[num_seqs + 1];
+  const int parts = (L + P - 1) / P;
+  if (parts <= 1) return;
+  const size_t item0 = static_cast<size_t>(ws_off[s]) + h / kMhHeads;
+  const int g = h % kMhHeads;
+  const int lane = threadIdx.x;
+  float mx = -INFINITY, den = 0.f;
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < parts; p0 += kU) {
+    f32x2 ml[kU];
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t slot = (item0 + static_cast<size_t>(min(p0 + u, parts - 1)) * NG) * kMhHeads + g;
+      ml[u] = *reinterpret_cast<const f32x2*>(ws_ml + slot * 2);
+      v[u] = load16(ws_part + slot * kMlaVDim + 8 * lane);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (p0 + u < parts) bm = fmaxf(bm, ml[u][0]);
+    const float mn = fmaxf(mx, bm);
+    if (mn == -INFINITY) continue;
+    const float a = (mx == -INFINITY) ? 0.f : fast_exp2(mx - mn);
+    den *= a;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) num[k] *= a;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float mu = ml[u][0];
+      const float w = (p0 + u < parts && mu != -INFINITY) ? fast_exp2(mu - mn) * ml[u][1] : 0.f;
+      float o[8];
+      T::unpack(v[u], o);
+      den += w;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) num[k] = fmaf(w, o[k], num[k]);
+    }
+    mx = mn;
+  }
+  const float inv = 1.f / den;
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = Mfma<T>::pack2(num[2 * k] * inv, num[2 * k + 1] * inv);
+  store16(out + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 8 * lane, u32x4{w[0], w[1], w[2], w[3]});
+}
 
 template <typename T, int BS>
 hipError_t run_mla_heads(const PrefillArgs& a, hipStream_t stream) {
   using S16 = typename T::storage;
   hipLaunchKernelGGL((mla_heads_kernel<T, BS>), dim3(a.workgroups), dim3(kMhWaves * kWave), 0, stream,
                      static_cast<S16*>(a.out), static_cast<const S16*>(a.q), static_cast<const char*>(a.k_pool),
-                     a.block_tables, a.context_lens, a.ws_off, a.ws_ml, a.ws_acc, fabsf(a.scale) * kLog2e,
-                     a.scale < 0.f ? 0x80008000u : 0u, a.num_seqs, a.num_heads, a.num_blocks, a.max_blocks_per_seq,
-                     a.max_items, a.slots);
+                     a.block_tables, a.context_lens, a.ws_off, a.ws_ml, reinterpret_cast<S16*>(a.ws_acc),
+                     fabsf(a.scale) * kLog2e, a.scale < 0.f ? 0x80008000u : 0u, a.num_seqs, a.num_heads,
+                     a.num_blocks, a.max_blocks_per_seq, a.max_items, a.slots);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ws_ml == nullptr) return e;
-  hipLaunchKernelGGL((lse_merge_kernel<T, kMlaVDim, kMlaVDim, kMlaMergeThreads>), dim3(a.num_seqs * a.num_heads),
-                     dim3(kMlaMergeThreads), 0, stream, static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc,
-                     a.context_lens, a.num_seqs, a.num_heads, kMhHeads, a.max_blocks_per_seq * a.block_size);
+  hipLaunchKernelGGL((mla_merge_kernel<T>), dim3(a.num_seqs * a.num_heads), dim3(kWave), 0, stream,
+                     static_cast<S16*>(a.out), a.ws_off, a.ws_ml, reinterpret_cast<const S16*>(a.ws_acc),
+                     a.context_lens, a.num_seqs, a.num_heads, a.max_blocks_per_seq * a.block_size);
   return hipGetLastError();
 }
 

@@ -152,3 +152,16 @@ def test_many_heads_more_sequences_than_the_kernel_takes():
     lens = rng.integers(0, 60, size=600).tolist()
     c = LatentCase(lens, 64, 16, torch.bfloat16, 212)
     assert_close(c.run(), c.oracle(), torch.bfloat16, "600 sequences")
+
+
+def test_many_heads_more_items_than_workgroups():
+    """400 sequences with 64 heads: more rows than the GPU has workgroups, so
+    the kernel takes its largest partition and its workgroups run several
+    items each; the short contexts are whole items, the longer ones split."""
+    announce("mla many heads 400 sequences")
+    rng = np.random.default_rng(213)
+    lens = rng.integers(0, 600, size=400)
+    lens[[7, 100, 399]] = [5000, 9000, 4097]
+    lens = lens.tolist()
+    c = LatentCase(lens, 64, 16, torch.bfloat16, 213)
+    assert_close(c.run(), c.oracle(), torch.bfloat16, "400 sequences")
