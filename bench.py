@@ -51,7 +51,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
 
 
 PF_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
-              for f in ("pa_prefill.hip", "pa_mla_heads.hip", "pa_attend.h", "pa_device.h", "pa_mfma.h",
+              for f in ("pa_prefill.hip", "pa_prefill_tiles.hip", "pa_mla_heads.hip", "pa_attend.h", "pa_device.h", "pa_mfma.h",
                         "pa_internal.h", "pa_api.cpp")]
 
 

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
 SOURCES = ["pa_decode.hip", "pa_decode_balanced.hip", "pa_decode_balanced_gqa2.hip",
-           "pa_decode_balanced_gqa4.hip", "pa_decode_mfma.hip", "pa_mla_heads.hip", "pa_prefill.hip", "pa_cache_ops.hip",
+           "pa_decode_balanced_gqa4.hip", "pa_decode_mfma.hip", "pa_mla_heads.hip", "pa_prefill.hip", "pa_prefill_tiles.hip", "pa_cache_ops.hip",
            "pa_api.cpp"]
 
 # Packed-FP32 VALU forms are disabled: plain fp32 code only.

@@ -586,6 +586,14 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const voi
     a.ws_ml = reinterpret_cast<float*>(ws + plan.ws.ml_offset);
     a.ws_acc = reinterpret_cast<float*>(ws + plan.ws.acc_offset);
   }
+  // the row-block kernel when every row stays in one partition, the caller
+  // left the split to the library and the 128-row blocks fill the GPU
+  const long long group = num_heads / num_kv_heads;
+  const long long full_blocks = num_kv_heads * (static_cast<long long>(num_query_rows) * group / pa::kPfTileRows);
+  const bool tiles = !latent && partition_size == 0 &&
+                     plan.part_tokens >= static_cast<long long>(max_blocks_per_seq) * block_size &&
+                     full_blocks >= cu_count() &&
+                     static_cast<long long>(num_query_rows) * group >= 64LL * num_seqs;
   for (int32_t s0 = 0; s0 < num_seqs; s0 += pa::kPfMaxSeqs) {
     a.num_seqs = num_seqs - s0 < pa::kPfMaxSeqs ? num_seqs - s0 : pa::kPfMaxSeqs;
     a.block_tables = block_tables + static_cast<size_t>(s0) * max_blocks_per_seq;
@@ -597,8 +605,16 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const voi
               static_cast<size_t>(s0) * num_heads * (latent ? pa::kMlaVDim : head_dim) * 2;
       a.num_query_rows = a.num_seqs;
     }
-    const hipError_t e = latent ? pa::launch_mla_split(a, static_cast<hipStream_t>(stream))
-                                : pa::launch_prefill(a, static_cast<hipStream_t>(stream));
+    if (tiles) {  // one workgroup per item: at most this many 128-row blocks
+      const long long items =
+          num_kv_heads * ((static_cast<long long>(num_query_rows) * group + pa::kPfTileRows - 1) / pa::kPfTileRows +
+                          a.num_seqs);
+      a.max_items = static_cast<int>(std::min(items, static_cast<long long>(INT_MAX)));
+      a.workgroups = a.max_items;
+    }
+    const hipError_t e = latent  ? pa::launch_mla_split(a, static_cast<hipStream_t>(stream))
+                         : tiles ? pa::launch_prefill_tiles(a, static_cast<hipStream_t>(stream))
+                                 : pa::launch_prefill(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;

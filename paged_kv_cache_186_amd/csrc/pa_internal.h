@@ -214,6 +214,11 @@ struct PrefillArgs {
   int slots;           // mla_heads: CUs of the device
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// many query rows per sequence and the default split (one partition): one
+// workgroup per block of 128 rows of a (sequence, K/V head), the keys and
+// values of each step staged in LDS by direct loads (pa_prefill_tiles.hip)
+constexpr int kPfTileRows = 128;
+hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream);
 // the latent cache: one workgroup per (sequence, 16 heads, partition), the
 // 576 elements of a row split across its four waves
 hipError_t launch_mla_split(const PrefillArgs& a, hipStream_t stream);
