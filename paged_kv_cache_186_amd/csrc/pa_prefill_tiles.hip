@@ -64,6 +64,8 @@ constexpr int kTlKeys = PA_PREFILL_TILE_KEYS;    // keys per step (32 or 64)
 constexpr int kTlKB = kTlKeys / 16;              // 16-key blocks per step
 constexpr int kTlWaveKeys = kTlKeys / 4;         // keys of a step one wave loads
 
+typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+
 // one 16-byte direct global-to-LDS load per lane: the wave's 64 lanes fill
 // the 1 KiB at lds (a wave-uniform address) in lane order
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
@@ -106,7 +108,12 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
   static_assert(kUnits * 1024 * kTlWaves == kStepB, "whole 1 KiB loads");
   static_assert(kUnits * 1024 / kRowB == kTlWaveKeys, "each wave loads a quarter of a step");
   constexpr int kSl = D / 32;                        // 32-element slices of the S^T contraction
-  constexpr int kDq = D / 64;                        // 64-element value slices
+  // chunk swizzles (16-byte chunk c of key k sits at position c ^ swz(k)):
+  // K operands read the same chunk of 16 keys, which must fall on distinct
+  // banks; V reads read 2 chunks of 4 consecutive keys, 8 distinct chunks
+  auto swz_k = [](int k) { return (k / kRowsPer256) % kCpr; };
+  auto swz_v = [](int k) { return 2 * (k & 3); };
+  constexpr int kDt = D / 16;                        // 16-element value tiles (rows of the P.V A operand)
   constexpr int kPer = (kPfMaxSeqs + kThreads - 1) / kThreads;
   // two steps in flight, each stage a separate array (K and V)
   __shared__ __attribute__((aligned(1024))) char s_k0[kStepB];
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
     const int n_keys = min(L, first + (min(Mrows, (rb + 1) * kTlRows) - 1) / G + 1);
     const int n_steps = n_keys > 0 ? (n_keys + kTlKeys - 1) / kTlKeys : 0;
 
-    f4_t acc[kTlTiles][kDq][4];
+    f4_t acc[kTlTiles][kDt];
     f4_t lacc[kTlTiles];
     float m[kTlTiles];
 #pragma unroll
@@ -218,9 +225,7 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
       m[t] = -INFINITY;
       lacc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dq = 0; dq < kDq; ++dq)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[t][dq][e] = f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < kDt; ++dt) acc[t][dt] = f4_t{0.f, 0.f, 0.f, 0.f};
     }
     bool bad[kTlTiles] = {false, false};
 
@@ -256,8 +261,9 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
       // whether its id was outside the pool; the V loads of the step reuse
       // the block.
       size_t row0 = 0;  // first pool row of the wave's block for the step being loaded
-      auto issue_rows = [&](int c, const char* pool, char* stage_base, bool lookup, int stage)
+      auto issue_rows = [&](int c, const char* pool, char* stage_base, bool is_v, int stage)
           __attribute__((always_inline)) {
+        const bool lookup = !is_v;
         const int c0 = c * kTlKeys;
         if (lookup) {
           const int kw = min(c0 + kTlWaveKeys * wave, n_keys - 1);
@@ -276,30 +282,27 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
         for (int u = 0; u < kUnits; ++u) {
           const int slot = (wave * kUnits + u) * kWave + lane;  // 16-byte slot of the step's rows
           const int kk = slot / kCpr;
-          const int cg = (slot % kCpr) ^ ((kk / kRowsPer256) % kCpr);  // the chunk stored in that slot
+          const int cg = (slot % kCpr) ^ (is_v ? swz_v(kk) : swz_k(kk));  // the chunk stored in that slot
           const int key = min(c0 + kk, n_keys - 1);
           load_lds16(pool + (row0 + key % BS) * kRowB + cg * 16, stage_base + (wave * kUnits + u) * 1024);
         }
       };
 
-      // LDS byte offsets of the lane's operands within a stage.  K: key
-      // 16 kb + col, elements 32 sl + 8 g4 ..; V: key 16 j + 4 g4 + e, values
-      // 64 dq + 4 col ..  The chunk swizzle of these keys does not depend on
-      // kb or j (16 keys span whole 256-byte bank rows), so one offset per
-      // slice (K) or per (dq, e) (V) serves every block, the block adding a
-      // constant.
+      // LDS byte offsets of the lane's operands within a stage.  K (read
+      // by ds_read_b128): key 16 kb + col, elements 32 sl + 8 g4 ..; its
+      // swizzle does not depend on kb (16 keys span whole 256-byte bank
+      // rows), so one offset per slice serves every block.  V (read by
+      // ds_read_b64_tr_b16, see below): key 4 g4 + (col / 4) of each 16-key
+      // block, values 16 dt + 4 (col % 4) ..; one offset per value tile.
       int koff[kSl];
-      int voff[kDq][4];
+      int voff[kDt];
 #pragma unroll
-      for (int sl = 0; sl < kSl; ++sl)
-        koff[sl] = col * kRowB + (((4 * sl + g4) ^ ((col / kRowsPer256) % kCpr)) * 16);
+      for (int sl = 0; sl < kSl; ++sl) koff[sl] = col * kRowB + (((4 * sl + g4) ^ swz_k(col)) * 16);
 #pragma unroll
-      for (int dq = 0; dq < kDq; ++dq)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = 4 * g4 + e;
-          voff[dq][e] = kk * kRowB + (((8 * dq + col / 2) ^ ((kk / kRowsPer256) % kCpr)) * 16) + 8 * (col & 1);
-        }
+      for (int dt = 0; dt < kDt; ++dt) {
+        const int kk = 4 * g4 + col / 4;
+        voff[dt] = kk * kRowB + (((2 * dt + (col % 4) / 2) ^ swz_v(kk)) * 16) + 8 * (col % 2);
+      }
 
       // 3. the steps.  A read of LDS after a direct load was issued waits
       //    for every direct load in flight (the compiler cannot tell the
@@ -309,8 +312,8 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
       //    by slice between the P.V products, come after.  The barrier at the
       //    top of a step follows every wave's wait for its own loads of that
       //    step.
-      issue_rows(0, k_pool, s_k0, true, 0);
-      issue_rows(0, v_pool, s_v0, false, 0);
+      issue_rows(0, k_pool, s_k0, false, 0);
+      issue_rows(0, v_pool, s_v0, true, 0);
       for (int c = 0; c < n_steps; ++c) {
         const int stage = c & 1;
         const char* sk = stage ? s_k1 : s_k0;
@@ -339,8 +342,8 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
           for (int kb = 0; kb < kTlKB; ++kb)
             ka[sl][kb] = *reinterpret_cast<const u32x4*>(sk + koff[sl] + kb * 16 * kRowB);
         if (next) {
-          issue_rows(c + 1, k_pool, nk, true, stage ^ 1);
-          issue_rows(c + 1, v_pool, nv, false, stage ^ 1);
+          issue_rows(c + 1, k_pool, nk, false, stage ^ 1);
+          issue_rows(c + 1, v_pool, nv, true, stage ^ 1);
         }
         f4_t sc[kTlTiles][kTlKB];
 #pragma unroll
@@ -387,9 +390,7 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
             const float alpha = (m[t] == -INFINITY) ? 0.f : fast_exp2(m[t] - mn);
             lacc[t] *= alpha;
 #pragma unroll
-            for (int dq = 0; dq < kDq; ++dq)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[t][dq][e] *= alpha;
+            for (int dt = 0; dt < kDt; ++dt) acc[t][dt] *= alpha;
             m[t] = mn;
           }
         }
@@ -414,70 +415,60 @@ __global__ __launch_bounds__(kTlWaves* kWave, 2) void prefill_tile_kernel(
             pw[t][h] = pw_t{M::pack2(p[2 * h][0], p[2 * h][1]), M::pack2(p[2 * h][2], p[2 * h][3]),
                             M::pack2(p[2 * h + 1][0], p[2 * h + 1][1]), M::pack2(p[2 * h + 1][2], p[2 * h + 1][3])};
         }
-        // O^T += V^T P^T per 32 keys (blocks 2 h, 2 h + 1) and value slice:
-        // lane l reads 4 values (64 dq + 4 col ..) of each of its 8 keys, one
-        // slice ahead, and permutes them by column into the A operand
-        u32x2 va[2][2][4];
-        auto load_v = [&](int j, u32x2 (&dst)[2][4]) __attribute__((always_inline)) {
-          const int h = j / kDq;
-          const int dq = j % kDq;
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              dst[kb2][e] = *reinterpret_cast<const u32x2*>(sv + voff[dq][e] + 16 * (2 * h + kb2) * kRowB);
+        // O^T += V^T P^T per 32 keys (blocks 2 h, 2 h + 1) and 16-value tile
+        // dt.  The A operand (V transposed: 16 values x 32 keys) comes from two
+        // transposing reads: in each group of 16 lanes, lane 4 j + a reads 4
+        // values (16 dt + 4 a ..) of key j of the group's four, and the read
+        // hands lane 4 a + b value 16 dt + 4 a + b of all four keys — lane l
+        // gets value 16 dt + l % 16 of keys 4 (l / 16) + j of the block, the
+        // keys its P operand holds.  Reads run one tile ahead.
+        auto load_v = [&](int j, u32x4& dst) __attribute__((always_inline)) {
+          const int h = j / kDt;
+          const int dt = j % kDt;
+          const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s4_t*)(sv + voff[dt] + 32 * h * kRowB));
+          const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s4_t*)(sv + voff[dt] + (32 * h + 16) * kRowB));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+          const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+          dst = u32x4{l2.x, l2.y, h2.x, h2.y};
         };
+        u32x4 va[2];
         load_v(0, va[0]);
 #pragma unroll
-        for (int j = 0; j < kTlKB / 2 * kDq; ++j) {
-          const int h = j / kDq;
-          const int dq = j % kDq;
-          if (j + 1 < kTlKB / 2 * kDq) load_v(j + 1, va[(j + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          const u32x2 (&v)[2][4] = va[j & 1];
+        for (int j = 0; j < kTlKB / 2 * kDt; ++j) {
+          const int h = j / kDt;
+          const int dt = j % kDt;
+          if (j + 1 < kTlKB / 2 * kDt) load_v(j + 1, va[(j + 1) & 1]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const pw_t a = {col_pair(v[0][0], v[0][1], e), col_pair(v[0][2], v[0][3], e),
-                            col_pair(v[1][0], v[1][1], e), col_pair(v[1][2], v[1][3], e)};
-#pragma unroll
-            for (int t = 0; t < kTlTiles; ++t) acc[t][dq][e] = PV::mma(a, pw[t][h], acc[t][dq][e]);
-          }
-          if (dq == kDq - 1) {
+          for (int t = 0; t < kTlTiles; ++t) acc[t][dt] = PV::mma(va[j & 1], pw[t][h], acc[t][dt]);
+          if (dt == kDt - 1) {
             const pw_t ones = {M::kOnes, M::kOnes, M::kOnes, M::kOnes};
 #pragma unroll
             for (int t = 0; t < kTlTiles; ++t) lacc[t] = PV::mma(ones, pw[t][h], lacc[t]);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
-    // 4. the rows: lane l holds row col's value elements 64 dq + 16 g4 +
-    //    4 i + e in acc[t][dq][e][i]; a row that sees no key is zero
+    // 4. the rows: lane l holds row col's values 16 dt + 4 g4 + i in
+    //    acc[t][dt][i]; a row that sees no key is zero
 #pragma unroll
     for (int t = 0; t < kTlTiles; ++t) {
       if (!ok[t]) continue;
       float lrow = lacc[t][0];
       if (bad[t]) lrow = __builtin_nanf("");
       const float inv = (lrow == 0.f) ? 0.f : 1.f / lrow;
-      S16* orow = out + (static_cast<size_t>(q0 + tok[t]) * num_heads + head[t]) * D + 16 * g4;
+      S16* orow = out + (static_cast<size_t>(q0 + tok[t]) * num_heads + head[t]) * D + 4 * g4;
 #pragma unroll
-      for (int dq = 0; dq < kDq; ++dq) {
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w[2 * i] = M::pack2(acc[t][dq][0][i] * inv, acc[t][dq][1][i] * inv);
-          w[2 * i + 1] = M::pack2(acc[t][dq][2][i] * inv, acc[t][dq][3][i] * inv);
-        }
-        store16(orow + 64 * dq, u32x4{w[0], w[1], w[2], w[3]});
-        store16(orow + 64 * dq + 8, u32x4{w[4], w[5], w[6], w[7]});
-      }
+      for (int dt = 0; dt < kDt; ++dt)
+        *reinterpret_cast<u32x2*>(orow + 16 * dt) =
+            u32x2{M::pack2(acc[t][dt][0] * inv, acc[t][dt][1] * inv), M::pack2(acc[t][dt][2] * inv, acc[t][dt][3] * inv)};
     }
     __syncthreads();  // the stages and s_bad are free for the next item
   }
 }
-
 template <typename T, int D, int BS>
 hipError_t run_tiles(const PrefillArgs& a, hipStream_t stream) {
   using S16 = typename T::storage;
