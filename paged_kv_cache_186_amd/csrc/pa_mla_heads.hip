@@ -49,6 +49,8 @@
 namespace pa {
 namespace {
 
+typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+
 constexpr int kMhWaves = 4;
 constexpr int kMhHeads = kMlaHeadsGroup;             // heads per workgroup (16 per wave)
 constexpr int kMhRowB = kMlaQkDim * 2;               // bytes of one latent row
@@ -58,31 +60,18 @@ constexpr int kMhChunks = kMhRowB / 16;              // 16-byte chunks per row (
 constexpr int kMhLoads = kMhStepKeys * kMhChunks / (kMhWaves * kWave);  // per thread per step (9)
 static_assert(kMhLoads * kMhWaves * kWave == kMhStepKeys * kMhChunks, "whole rows per step");
 constexpr int kMhQK = kMlaQkDim / 32;                // S^T products per 16 keys (18)
-constexpr int kMhDq = kMlaVDim / 64;                 // 64-element value slices (8)
+constexpr int kMhDt = kMlaVDim / 16;                 // 16-value tiles (32): rows of the P.V A operand
 constexpr int kMhMaxBlocks = kMlaHeadsMaxPart / 16;  // table entries of the longest item
 
-// A lane's share of one head's 512 outputs: eight 16-element chunks (per
-// 64-element slice dq, the chunk 64 dq + 16 g4 .. + 15, element 4 i + e of
-// it in acc[dq][e][i]), scaled by inv and packed two to a word: element
-// 4 i + e goes to word 2 i + e / 2, low half for even e.
+// A lane's share of one head's 512 outputs: 4 consecutive values of each
+// 16-value tile (values 16 dt + 4 g4 + i in acc[dt][i]), scaled by inv,
+// rounded and stored 8 bytes a tile; row points at the lane's first value.
 template <typename T>
-__device__ __forceinline__ void pack_chunk(const f4_t (&a)[4], float inv, uint32_t (&w)[8]) {
+__device__ __forceinline__ void store_row(typename T::storage* row, const f4_t (&acc)[kMlaVDim / 16], float inv) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w[2 * i] = Mfma<T>::pack2(a[0][i] * inv, a[1][i] * inv);
-    w[2 * i + 1] = Mfma<T>::pack2(a[2][i] * inv, a[3][i] * inv);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void store_row(typename T::storage* row, const f4_t (&acc)[kMlaVDim / 64][4], float inv) {
-#pragma unroll
-  for (int dq = 0; dq < kMlaVDim / 64; ++dq) {
-    uint32_t w[8];
-    pack_chunk<T>(acc[dq], inv, w);
-    store16(row + 64 * dq, u32x4{w[0], w[1], w[2], w[3]});
-    store16(row + 64 * dq + 8, u32x4{w[4], w[5], w[6], w[7]});
-  }
+  for (int dt = 0; dt < kMlaVDim / 16; ++dt)
+    *reinterpret_cast<u32x2*>(row + 16 * dt) = u32x2{Mfma<T>::pack2(acc[dt][0] * inv, acc[dt][1] * inv),
+                                                     Mfma<T>::pack2(acc[dt][2] * inv, acc[dt][3] * inv)};
 }
 
 template <typename T, int BS>
@@ -286,11 +275,9 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     }
     float m = -INFINITY;
     f4_t lacc = {0.f, 0.f, 0.f, 0.f};
-    f4_t acc[kMhDq][4];
+    f4_t acc[kMhDt];
 #pragma unroll
-    for (int dq = 0; dq < kMhDq; ++dq)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[dq][e] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < kMhDt; ++dt) acc[dt] = f4_t{0.f, 0.f, 0.f, 0.f};
     int bad = 0;
     __syncthreads();  // s_tbl and s_q written; the previous item's LDS rows no longer read
 
@@ -377,9 +364,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
         const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
         lacc *= alpha;
 #pragma unroll
-        for (int dq = 0; dq < kMhDq; ++dq)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[dq][e] *= alpha;
+        for (int dt = 0; dt < kMhDt; ++dt) acc[dt] *= alpha;
         m = mn;
       }
       const float nm = -m;
@@ -393,28 +378,26 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
         }
       const pw_t pw = {M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3]), M::pack2(p[1][0], p[1][1]),
                        M::pack2(p[1][2], p[1][3])};
-      // V^T operand: lane l reads 4 latent values (64dq + 4col ..) of its 8
-      // keys (4*g4 + e of both blocks) and permutes them by column
-      u32x2 vbuf[2][2][4];
-      auto load_vc = [&](int dq, u32x2 (&dst)[2][4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dst[kb][e] = *reinterpret_cast<const u32x2*>(rows + (16 * kb + 4 * g4 + e) * kMhLdsRow + (64 * dq + 4 * col) * 2);
+      // V^T operand per 16-value tile dt by two transposing reads
+      // (ds_read_b64_tr_b16): in each group of 16 lanes, lane 4 j + a reads
+      // values 16 dt + 4 a .. of key j of the group's four (4 g4 + j of each
+      // block), and the read hands lane l value 16 dt + l % 16 of all four —
+      // the keys its P operand holds.  One tile ahead.
+      const char* vrow = rows + (4 * g4 + col / 4) * kMhLdsRow + 8 * (col % 4);
+      auto load_vt = [&](int dt, u32x4& dst) __attribute__((always_inline)) {
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vrow + 32 * dt)));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t*)(vrow + 16 * kMhLdsRow + 32 * dt)));
+        dst = u32x4{lo.x, lo.y, hi.x, hi.y};
       };
-      load_vc(0, vbuf[0]);
+      u32x4 vbuf[2];
+      load_vt(0, vbuf[0]);
 #pragma unroll
-      for (int dq = 0; dq < kMhDq; ++dq) {
-        if (dq + 1 < kMhDq) load_vc(dq + 1, vbuf[(dq + 1) & 1]);
+      for (int dt = 0; dt < kMhDt; ++dt) {
+        if (dt + 1 < kMhDt) load_vt(dt + 1, vbuf[(dt + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        const u32x2 (&v)[2][4] = vbuf[dq & 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const pw_t a = {col_pair(v[0][0], v[0][1], e), col_pair(v[0][2], v[0][3], e), col_pair(v[1][0], v[1][1], e),
-                          col_pair(v[1][2], v[1][3], e)};
-          acc[dq][e] = PV::mma(a, pw, acc[dq][e]);
-        }
+        acc[dt] = PV::mma(vbuf[dt & 1], pw, acc[dt]);
         __builtin_amdgcn_sched_barrier(0);
       }
       const pw_t ones = {M::kOnes, M::kOnes, M::kOnes, M::kOnes};
@@ -435,8 +418,8 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
       if (st + 2 < n_steps) load_step(ra, st + 2);
     }
 
-    // 5. this wave's 16 rows; lane l holds row col's value elements
-    //    64 dq + 16 g4 + 4 i + e in acc[dq][e][i]
+    // 5. this wave's 16 rows; lane l holds row col's values 16 dt + 4 g4 + i
+    //    in acc[dt][i]
     // (the output and workspace addresses are formed only here: opaque
     // copies of the base pointers keep the compiler from computing them
     // before the steps and holding them in registers across the loop)
@@ -447,7 +430,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     const int any_bad = __syncthreads_or(bad);
     float lrow = lacc[0];  // the row sum (every element of the ones product holds it)
     if (any_bad) lrow = __builtin_nanf("");
-    S16* orow = out_b + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 16 * g4;
+    S16* orow = out_b + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 4 * g4;
     if (parts == 1) {
       if (row_ok) store_row<T>(orow, acc, 1.f / lrow);
       continue;
@@ -455,7 +438,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     // a split row: the item's partial, normalised and rounded to the output
     // type, and its (max, sum) in fp32, for mla_merge_kernel
     const size_t slot = static_cast<size_t>(item) * kMhHeads + wave * 16 + col;
-    store_row<T>(part_b + slot * kMlaVDim + 16 * g4, acc, 1.f / lrow);
+    store_row<T>(part_b + slot * kMlaVDim + 4 * g4, acc, 1.f / lrow);
     if (g4 == 0) *reinterpret_cast<f32x2*>(ml_b + slot * 2) = f32x2{m, lrow};
   }
 }
