@@ -165,3 +165,15 @@ def test_many_heads_more_items_than_workgroups():
     lens = lens.tolist()
     c = LatentCase(lens, 64, 16, torch.bfloat16, 213)
     assert_close(c.run(), c.oracle(), torch.bfloat16, "400 sequences")
+
+
+def test_many_heads_512_sequences():
+    """512 sequences (the many-heads kernel's limit) with 64 heads: one item
+    per row at the largest partition for the short ones, split rows for the
+    few long ones."""
+    announce("mla many heads 512 sequences")
+    rng = np.random.default_rng(214)
+    lens = rng.integers(1, 300, size=512)
+    lens[[3, 511]] = [6000, 4500]
+    c = LatentCase(lens.tolist(), 64, 32, torch.float16, 214)
+    assert_close(c.run(), c.oracle(), torch.float16, "512 sequences")

@@ -185,3 +185,20 @@ def test_negative_and_zero_scale(scale):
     out = c.run()
     rows, ref = c.oracle_rows(c.sample(np.random.default_rng(11)))
     assert_close(out[rows], ref, torch.bfloat16, f"scale {scale}")
+
+
+def test_many_sequences_and_more_than_one_launch():
+    """2100 sequences of 40 query tokens over 40..300-token contexts: the
+    workgroups' item offsets over all of a launch's sequences (8 per thread)
+    and a second launch for the sequences past 2048."""
+    announce("prefill tiles 2100 sequences")
+    rng = np.random.default_rng(370)
+    S = 2100
+    tq = [40] * S
+    lens = rng.integers(40, 301, size=S).tolist()
+    c = TileCase(lens, tq, 32, 8, 128, 16, torch.float16, 370)
+    out = c.run()
+    picks = [(s, i) for s in (0, 1, 1000, 2047, 2048, 2049, S - 1) for i in (0, 17, 39)]
+    picks += [(int(s), int(i)) for s, i in zip(rng.integers(0, S, size=24), rng.integers(0, 40, size=24))]
+    rows, ref = c.oracle_rows(picks)
+    assert_close(out[rows], ref, torch.float16, "2100 sequences")
