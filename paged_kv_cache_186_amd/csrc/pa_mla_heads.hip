@@ -23,13 +23,13 @@
 //
 // Per step and wave (16 heads, 32 keys):
 //   S^T = K Q^T     18 v_mfma_f32_16x16x32 per 16-key block over the 576
-//                   elements (A = 16 keys x 32 elements from LDS, B = the
-//                   wave's queries, kept in registers for the whole item);
+//                   elements (A = 16 keys x 32 elements, B = the wave's 16
+//                   query rows, both from LDS);
 //   softmax         the lane's 8 scores, the row's maximum across its four
 //                   lanes, rescaling deferred until it grows by more than 2^8;
-//   O^T += V^T P^T  32 products over the 512 latent values (A = V transposed
-//                   from LDS by byte permutes, as in the query kernels), plus
-//                   one with every value 1 for the row sums.
+//   O^T += V^T P^T  one product per 16-value tile of the 512 latent values
+//                   (A = V transposed, from LDS by two transposing reads),
+//                   plus one with every value 1 for the row sums.
 // Items are (sequence, partition of P tokens, group of 64 heads), in that
 // order, one workgroup per CU.  P, a multiple of 32 from 256 to 4096, is
 // chosen on the device from the lengths: the smallest of eight sizes between

@@ -19,11 +19,11 @@
 // 64: each step's K and V rows (2 x 16 KiB at D = 128) are copied from HBM
 // straight into LDS by the direct global-to-LDS loads of gfx950 (no
 // registers: global_load_lds_dwordx4, 1 KiB per wave instruction, 16 bytes
-// per lane), two steps in flight; all four waves read their MFMA operands
-// from there, so every K/V byte reaches the CU once per 128 query rows
-// instead of once per 16 or 32.  In LDS, the 16-byte chunk c of key k sits
-// at position c ^ swz(k) of its row, so that the 16 keys an operand load
-// touches fall on different banks.
+// per lane) into one of two stages while the other step is computed; all
+// four waves read their MFMA operands from there, so every K/V byte reaches
+// the CU once per 128 query rows instead of once per 16 or 32.  In LDS, the
+// 16-byte chunk c of key k sits at position c ^ swz(k) of its row, so that
+// the keys an operand read touches fall on different banks.
 //
 // Per step and wave (32 rows, 64 keys):
 //   S^T = K Q^T     per 16-key block and 32-element slice one
@@ -34,8 +34,8 @@
 //                   four lanes, rescaling deferred until it grows by 2^8;
 //                   causal and context masks only on the steps that cross a
 //                   row's position;
-//   O^T += V^T P^T  per 32 keys and 64-element value slice, four products per
-//                   tile (A = V transposed, from LDS by byte permutes, shared
+//   O^T += V^T P^T  per 32 keys and 16-value tile one product per tile (A =
+//                   V transposed, from LDS by two transposing reads, shared
 //                   by the tiles), plus one with every value 1 for the row
 //                   sums.
 // Items (sequence, K/V head, row block) run in that order, the blocks of one
