@@ -55,8 +55,15 @@ namespace {
 constexpr int kGqWaves = 4;
 // the merge of split rows: 32-element slices of D per workgroup of 256
 // threads (32 lane groups, 8 partials each per round)
-constexpr int kDecodeMergeSlice = 32;
-constexpr int kDecodeMergeThreads = 256;
+// The merge's shape: workgroups of THREADS lanes, each over a SLICE-element
+// slice of one (sequence, head) row.  Few rows (long contexts: many
+// partials per row) take 32-element slices and 128 lanes, many rows
+// (batches) 64-element slices and 128 lanes.  Measured (main kernel +
+// merge, µs; 32 / 256 before): 128K with 4 K/V heads 48.3 / 49.0 / 49.1,
+// with 1 K/V head 23.0 / 24.2 / 22.9; layer shape with 8 K/V heads 15.1 /
+// 14.1 / 16.3; continuous batching with 8 K/V heads 53.6 / 51.5 / 56.7 (32 /
+// 128, 64 / 128, 32 / 256).
+constexpr int kMergeRowsFew = 256;  // fewer (sequence, head) rows than this: few rows
 
 template <typename T, int D, int BS, int NT>
 __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_kernel(
@@ -433,10 +440,15 @@ hipError_t run_mfma(const DecodeArgs& a, hipStream_t stream) {
                      a.max_blocks_per_seq, a.max_items, a.mfma_slots);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ws_ml == nullptr) return e;
-  hipLaunchKernelGGL((lse_merge_kernel<T, D, kDecodeMergeSlice, kDecodeMergeThreads>),
-                     dim3(a.num_seqs * a.num_heads * (D / kDecodeMergeSlice)), dim3(kDecodeMergeThreads), 0, stream,
-                     static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
-                     a.num_heads, a.num_heads / a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
+  const int rows = a.num_seqs * a.num_heads;
+  if (rows < kMergeRowsFew)
+    hipLaunchKernelGGL((lse_merge_kernel<T, D, 32, 128>), dim3(rows * (D / 32)), dim3(128), 0, stream,
+                       static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
+                       a.num_heads, a.num_heads / a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
+  else
+    hipLaunchKernelGGL((lse_merge_kernel<T, D, 64, 128>), dim3(rows * (D / 64)), dim3(128), 0, stream,
+                       static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
+                       a.num_heads, a.num_heads / a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
   return hipGetLastError();
 }
 
