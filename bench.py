@@ -443,15 +443,15 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
     mfma_bound = op == "prefill"
     digest = kernel_source_digest(PF_SOURCES)
     tag = op + (f"_h{H}" if heads else "") + (f"_p{partition}" if partition else "")
-    # pa_decode_mla takes its many-heads kernel from 64 heads (default split,
-    # up to 512 sequences)
+    # pa_decode_mla takes mla_heads_kernel under the default split for up to
+    # 512 sequences
     # pa_prefill takes its row-block kernel with the default split when the
     # 128-row blocks of (sequence, K/V head) rows fill the GPU (the same test
     # the library makes)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     group = H // Hkv
     tiles = not partition and Hkv * (T * group // 128) >= cus and T * group >= 64 * S
-    kernel = (("mla_heads_kernel" if H >= 64 and not partition and S <= 512 else "mla_split_kernel") if mla
+    kernel = (("mla_heads_kernel" if not partition and S <= 512 else "mla_split_kernel") if mla
               else ("prefill_tile_kernel" if tiles else "prefill_kernel"))
     traffic = traffic_from_profile(digest, os.path.join(PROFILES, f"{kernel}_{tag}_traffic.txt"))
     metric = {"prefill": "chunked prefill over the paged cache (pa_prefill): achieved TFLOP/s, 1 MI355X",

@@ -222,11 +222,10 @@ hipError_t launch_prefill_tiles(const PrefillArgs& a, hipStream_t stream);
 // the latent cache: one workgroup per (sequence, 16 heads, partition), the
 // 576 elements of a row split across its four waves
 hipError_t launch_mla_split(const PrefillArgs& a, hipStream_t stream);
-// the latent cache with many heads: items (sequence, partition of 256..4096
-// tokens, 64 heads), one workgroup per CU, each wave 16 heads over the whole
-// row, the rows staged in LDS once per workgroup; split rows merged by a
-// second kernel
-constexpr int kMlaHeadsMin = 64;        // heads from which pa_decode_mla takes this kernel
+// the latent cache under the default split (up to kMlaHeadsMaxSeqs
+// sequences): items (sequence, partition of 256..4096 tokens, up to 64
+// heads), one workgroup per CU, each wave 16 heads over the whole row, the
+// rows staged in LDS once per workgroup; split rows merged by a second kernel
 constexpr int kMlaHeadsGroup = 64;      // heads per workgroup
 constexpr int kMlaHeadsMinPart = 256;   // partition sizes (tokens, multiples of 32)
 constexpr int kMlaHeadsMaxPart = 4096;

@@ -9,9 +9,10 @@
 // tutorial page "3. PagedAttention原理", §3.2), long contexts split into
 // partitions merged with the log-sum-exp identity ("Flash-Dec", milestone 4).
 //
-// Why a kernel of its own for many heads: every head of a sequence reads the
-// same latent rows, so the rows should come from HBM once per sequence and
-// feed as many heads as possible.  Here a workgroup serves 64 heads: each of
+// Why this shape: every head of a sequence reads the same latent rows, so the
+// rows should come from HBM once per sequence and feed as many heads as
+// possible.  Here a workgroup serves up to 64 heads (a wave whose 16 heads
+// all lie past the last one only loads rows): each of
 // its four waves owns 16 heads (the rows of its MFMA tiles) over the whole
 // 576-element row, and each 32-key step's rows (36 KiB) are loaded from HBM
 // once per workgroup into LDS (row stride padded by 16 bytes so that the 16
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     // the O^T accumulators would not fit the register file)
     const int h = hg * kMhHeads + wave * 16 + col;
     const bool row_ok = h < num_heads;
+    const bool wave_rows = hg * kMhHeads + wave * 16 < num_heads;  // the wave has a head (uniform)
     {
       const S16* qg = q + (static_cast<size_t>(s) * num_heads + hg * kMhHeads) * kMlaQkDim;
       constexpr int kQLoads = kMhHeads * kMhChunks / kThreads;  // 18 per thread
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     __syncthreads();
     if (n_steps > 1) load_step(ra, 1);
     for (int st = 0; st < n_steps; ++st) {
-      compute_step(st & 1, st);
+      if (wave_rows) compute_step(st & 1, st);  // a wave past the last head only loads
       if (st + 1 < n_steps) store_step(ra, (st + 1) & 1);
       __syncthreads();
       if (st + 2 < n_steps) load_step(ra, st + 2);

@@ -103,7 +103,8 @@ def test_more_sequences_than_one_launch_holds():
     assert_close(c.run(), c.oracle(), torch.bfloat16, "2100 sequences")
 
 
-# ---- many heads: the workgroup-per-64-heads kernel (default split, >= 64 heads)
+# ---- the workgroup-per-64-heads kernel (every head count under the default
+#      split, up to 512 sequences; the cases above with partition 0 take it too)
 
 @pytest.mark.parametrize("H", [64, 96, 128, 192])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
