@@ -47,6 +47,13 @@ namespace pa {
 namespace {
 
 constexpr int kWaveMergeBatch = 8;  // partials in flight per lane group while merging
+// Batches of up to this many sequences build their prefix sums per wave (one
+// lane per sequence) instead of per workgroup.
+#ifndef PA_WAVE_LOCAL_SEQS
+#define PA_WAVE_LOCAL_SEQS 64
+#endif
+constexpr int kWaveLocalSeqs = PA_WAVE_LOCAL_SEQS;
+static_assert(kWaveLocalSeqs <= kWave, "one lane per sequence");
 
 // Cost of one row of `units` units in the balanced split, with a row charge
 // RC (kBalancedCostUnit, kBalancedCostRow / kBalancedCostRowWide:
@@ -240,6 +247,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   constexpr int kCostRow = (GW > 1 || KT::kScaled) ? kBalancedCostRowWide : kBalancedCostRow;
   static_assert(Unit<KT, D, BS, GW>::kPerBlock <= (kCostRow == kBalancedCostRow ? 8 : 2),
                 "units per block within the host's cost bound");
+  static_assert(NW * (kWave + 1) <= kBalancedMaxSeqs, "every wave's copy of the prefix sums fits");
   __shared__ int s_off[kBalancedMaxSeqs + 1];   // units of all sequences before s (per head)
   __shared__ int s_coff[kBalancedMaxSeqs + 1];  // cost of all sequences before s (per head)
   __shared__ int s_len[kBalancedMaxSeqs];
@@ -257,62 +265,92 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
 
   // 1. clamped lengths and the exclusive prefix sums of units and of cost per
   //    sequence (one row's cost: kCostRow + kCostUnit per unit, nothing for an
-  //    empty row); thread t owns sequences [t*kPer, (t+1)*kPer)
-  for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);  // coalesced
-  __syncthreads();
-  int nbl[kPer];
-  int mine = 0;
-  int mine_c = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int s = tid * kPer + i;
-    nbl[i] = s < S ? (s_len[s] + R - 1) / R : 0;  // units of sequence s (per head)
-    mine += nbl[i];
-    mine_c += row_cost<kCostRow>(nbl[i]);
-  }
-  const int incl = wave_prefix_sum(mine);
-  const int incl_c = wave_prefix_sum(mine_c);
-  if (lane == kWave - 1) {
-    s_wsum[wave] = incl;
-    s_wcost[wave] = incl_c;
-  }
-  __syncthreads();
-  int before = 0;
+  //    empty row).  Up to kWaveLocalSeqs sequences every wave builds its own
+  //    copy (lane s owns sequence s; wave w's copy at offset w * (kWave + 1) of
+  //    each array): no workgroup barrier between the lengths load and the
+  //    first K/V loads.  Past that thread t owns sequences [t*kPer,
+  //    (t+1)*kPer) and the workgroup shares one copy.
+  const bool wave_local = S <= kWaveLocalSeqs;
+  const int sb = wave_local ? wave * (kWave + 1) : 0;
+  int* const off_l = s_off + sb;
+  int* const coff_l = s_coff + sb;
+  int* const len_l = s_len + sb;
   int total = 0;
-  int before_c = 0;
   int total_c = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int v = s_wsum[w];
-    const int vc = s_wcost[w];
-    before += (w < wave) ? v : 0;
-    before_c += (w < wave) ? vc : 0;
-    total += v;
-    total_c += vc;
-  }
-  int run = before + incl - mine;
-  int run_c = before_c + incl_c - mine_c;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int s = tid * kPer + i;
-    if (s < S) {
-      s_off[s] = run;
-      s_coff[s] = run_c;
+  if (wave_local) {
+    const int L = lane < S ? min(max(context_lens[lane], 0), cap) : 0;
+    const int nb = (L + R - 1) / R;  // units of sequence `lane` (per head)
+    const int c = row_cost<kCostRow>(nb);
+    const int incl = wave_prefix_sum(nb);
+    const int incl_c = wave_prefix_sum(c);
+    if (lane < S) {
+      len_l[lane] = L;
+      off_l[lane] = incl - nb;
+      coff_l[lane] = incl_c - c;
     }
-    run += nbl[i];
-    run_c += row_cost<kCostRow>(nbl[i]);
+    total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    total_c = __builtin_amdgcn_readlane(incl_c, kWave - 1);
+    if (lane == 0) {
+      off_l[S] = total;
+      coff_l[S] = total_c;
+    }
+    // the wave's own LDS writes before its reads below (no other wave reads them)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  } else {
+    for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);  // coalesced
+    __syncthreads();
+    int nbl[kPer];
+    int mine = 0;
+    int mine_c = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int s = tid * kPer + i;
+      nbl[i] = s < S ? (s_len[s] + R - 1) / R : 0;  // units of sequence s (per head)
+      mine += nbl[i];
+      mine_c += row_cost<kCostRow>(nbl[i]);
+    }
+    const int incl = wave_prefix_sum(mine);
+    const int incl_c = wave_prefix_sum(mine_c);
+    if (lane == kWave - 1) {
+      s_wsum[wave] = incl;
+      s_wcost[wave] = incl_c;
+    }
+    __syncthreads();
+    int before = 0;
+    int before_c = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int v = s_wsum[w];
+      const int vc = s_wcost[w];
+      before += (w < wave) ? v : 0;
+      before_c += (w < wave) ? vc : 0;
+      total += v;
+      total_c += vc;
+    }
+    int run = before + incl - mine;
+    int run_c = before_c + incl_c - mine_c;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int s = tid * kPer + i;
+      if (s < S) {
+        s_off[s] = run;
+        s_coff[s] = run_c;
+      }
+      run += nbl[i];
+      run_c += row_cost<kCostRow>(nbl[i]);
+    }
+    if (tid == 0) {
+      s_off[S] = total;
+      s_coff[S] = total_c;
+    }
+    __syncthreads();
   }
-  if (tid == 0) {
-    s_off[S] = total;
-    s_coff[S] = total_c;
-  }
-  __syncthreads();
   total = __builtin_amdgcn_readfirstlane(total);
   total_c = __builtin_amdgcn_readfirstlane(total_c);
 
   // 2. empty contexts give zero rows (spread over the workgroups)
   for (int s = blockIdx.x; s < S; s += gridDim.x)
-    if (s_len[s] == 0)
+    if (len_l[s] == 0)
       for (int i = tid; i < NH * D; i += kThreads) out[static_cast<size_t>(s) * NH * D + i] = QT::pack(0.f);
 
   // 3. this wave's share (no workgroup barrier after this point).  Work is
@@ -336,8 +374,8 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   const double rW = 1.0 / static_cast<double>(Wn);
   // cost start of the first unit of row (s, h)
   auto row_start = [&](int s, int h) __attribute__((always_inline)) {
-    const int nb = __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]);
-    return static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_coff[s]) +
+    const int nb = __builtin_amdgcn_readfirstlane(off_l[s + 1] - off_l[s]);
+    return static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(coff_l[s]) +
            static_cast<long long>(h) * row_cost<kCostRow>(nb) + kCostRow;
   };
   // the first unit whose cost start is >= c: its sequence, head and index in
@@ -356,16 +394,16 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     if (S > kWave) {
       const int stride = (S + kWave - 1) / kWave;
       const int cand = lane * stride;
-      const uint64_t pass = __builtin_amdgcn_ballot_w64(cand < S && static_cast<long long>(H) * s_coff[cand] <= c);
+      const uint64_t pass = __builtin_amdgcn_ballot_w64(cand < S && static_cast<long long>(H) * coff_l[cand] <= c);
       base = (63 - __builtin_clzll(pass)) * stride;  // lane 0 always passes (coff[0] = 0)
       span = min(stride, S - base);
     }
     const uint64_t pass =
-        __builtin_amdgcn_ballot_w64(lane < span && static_cast<long long>(H) * s_coff[base + min(lane, span - 1)] <= c);
+        __builtin_amdgcn_ballot_w64(lane < span && static_cast<long long>(H) * coff_l[base + min(lane, span - 1)] <= c);
     s = base + (63 - __builtin_clzll(pass));
-    const int nb = __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]);
+    const int nb = __builtin_amdgcn_readfirstlane(off_l[s + 1] - off_l[s]);
     const int rc = row_cost<kCostRow>(nb);
-    const long long local = c - static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_coff[s]);
+    const long long local = c - static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(coff_l[s]);
     h = static_cast<int>(floor_div(local, rc, 1.0 / static_cast<double>(rc)));
     const int o = static_cast<int>(local - static_cast<long long>(h) * rc);  // in [0, rc)
     j = o <= kCostRow ? 0 : (o - kCostRow + kCostUnit - 1) / kCostUnit;   // in [0, nb]
@@ -375,12 +413,12 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
         h = 0;
         do {
           ++s;
-        } while (s < S && __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]) == 0);
+        } while (s < S && __builtin_amdgcn_readfirstlane(off_l[s + 1] - off_l[s]) == 0);
         if (s == S) return T_all;
       }
     }
-    const int nbs = __builtin_amdgcn_readfirstlane(s_off[s + 1] - s_off[s]);
-    return static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(s_off[s]) +
+    const int nbs = __builtin_amdgcn_readfirstlane(off_l[s + 1] - off_l[s]);
+    return static_cast<long long>(H) * __builtin_amdgcn_readfirstlane(off_l[s]) +
            static_cast<long long>(h) * nbs + j;
   };
   int w_s, w_h, w_j;
@@ -390,7 +428,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   if (w_s == S || row_start(w_s, w_h) + static_cast<long long>(kCostUnit) * w_j >= c1) return;
   // the share's end is found after its first loads are issued (below)
   long long t1 = 0;
-  int w_nb = __builtin_amdgcn_readfirstlane(s_off[w_s + 1] - s_off[w_s]);
+  int w_nb = __builtin_amdgcn_readfirstlane(off_l[w_s + 1] - off_l[w_s]);
   // the K/V head of the row's query heads, updated only when the row changes
   // (no division when each work row is one whole group, as in plain MHA)
   auto kv_head = [&](int h) __attribute__((always_inline)) { return group == GW ? h : (h * GW) / group; };
@@ -406,8 +444,8 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     w_kvh = 0;
     do {
       ++w_s;
-    } while (w_s < S && __builtin_amdgcn_readfirstlane(s_off[w_s + 1] - s_off[w_s]) == 0);
-    if (w_s < S) w_nb = __builtin_amdgcn_readfirstlane(s_off[w_s + 1] - s_off[w_s]);
+    } while (w_s < S && __builtin_amdgcn_readfirstlane(off_l[w_s + 1] - off_l[w_s]) == 0);
+    if (w_s < S) w_nb = __builtin_amdgcn_readfirstlane(off_l[w_s + 1] - off_l[w_s]);
   };
 
   const int grp = lane / C::kLanesPerRow;
@@ -459,7 +497,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     st.s = w_s;
     st.h = w_h;
     st.u = w_j;
-    st.L = __builtin_amdgcn_readfirstlane(s_len[w_s]);
+    st.L = __builtin_amdgcn_readfirstlane(len_l[w_s]);
     advance();
     // keep the scheduler from sinking these loads below the compute that
     // follows: they must be in flight while the previous stage is consumed
@@ -493,8 +531,8 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   size_t pend_slot0[2] = {0, 0};
 
   auto flush = [&]() __attribute__((always_inline)) {
-    const int nb = __builtin_amdgcn_readfirstlane(s_off[cur_s + 1] - s_off[cur_s]);
-    const int off_s = __builtin_amdgcn_readfirstlane(s_off[cur_s]);
+    const int nb = __builtin_amdgcn_readfirstlane(off_l[cur_s + 1] - off_l[cur_s]);
+    const int off_s = __builtin_amdgcn_readfirstlane(off_l[cur_s]);
     const long long first = static_cast<long long>(H) * off_s + static_cast<long long>(cur_h) * nb;
     // the whole row lies in this share: final, no partial to merge
     const bool whole = first >= t0 && first + nb <= t1;

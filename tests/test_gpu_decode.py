@@ -383,6 +383,23 @@ def test_balanced_split_at_its_sequence_limit():
         assert torch.equal(out[s].cpu(), torch.zeros_like(out[s].cpu()))
 
 
+@pytest.mark.parametrize("S", [1, 63, 64, 65])
+def test_balanced_split_around_the_wave_local_limit(S):
+    """Up to 64 sequences every wave builds its own prefix sums (one lane per
+    sequence, no workgroup barrier), from 65 on the workgroup builds one copy:
+    both sides of the limit, ragged contexts with an empty one."""
+    announce(f"decode balanced {S} sequences (wave-local limit)")
+    rng = np.random.default_rng(900 + S)
+    lens = rng.integers(0, 300, size=S).tolist()
+    if S > 1:
+        lens[S // 2] = 0
+    w = _ragged_workload(lens, 4, 128, 16, torch.float16, 900 + S)
+    out = gpu_decode(w)
+    assert_close(out, oracle_decode(w), torch.float16, f"{S} sequences")
+    for s in [i for i, L in enumerate(lens) if L == 0]:
+        assert torch.equal(out[s].cpu(), torch.zeros_like(out[s].cpu()))
+
+
 def test_more_sequences_than_the_balanced_limit_use_partitions():
     announce("decode 2100 sequences (partitioned default)")
     rng = np.random.default_rng(5)
