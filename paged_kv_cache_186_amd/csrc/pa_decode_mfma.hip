@@ -104,76 +104,109 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
   const int cap = max_blocks * BS;
 
   // 1. lengths, then the items per sequence for each candidate partition
-  //    (HKV * ceil(L / P)), their exclusive prefix sums for the chosen one
-  for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);
-  __syncthreads();
-  int mine[kParts];
-#pragma unroll
-  for (int c = 0; c < kParts; ++c) mine[c] = 0;
-  int mine_tok = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int s = tid * kPer + i;
-    const int L = s < S ? s_len[s] : 0;
-    mine_tok += L;
-#pragma unroll
-    for (int c = 0; c < kParts; ++c) mine[c] += HKV * ((L + (1 << (kMaxShift - c)) - 1) >> (kMaxShift - c));
-  }
-  int incl[kParts];
-#pragma unroll
-  for (int c = 0; c < kParts; ++c) {
-    incl[c] = wave_prefix_sum(mine[c]);
-    if (lane == kWave - 1) s_wsum[c][wave] = incl[c];
-  }
-  const int incl_tok = wave_prefix_sum(mine_tok);
-  if (lane == kWave - 1) s_wtok[wave] = incl_tok;
-  __syncthreads();
-  // the partition: the largest power of two (kMfmaMinPartTokens ..
-  // kMfmaMaxPartTokens) not above the K/V tokens per resident workgroup,
-  // HKV * sum(L) / slots — long contexts get one long item per workgroup,
-  // ragged batches many short ones
-  long long tokens = 0;
-#pragma unroll
-  for (int w = 0; w < kGqWaves; ++w) tokens += s_wtok[w];
-  const long long per_slot = static_cast<long long>(HKV) * tokens / max(slots, 1);
-  int ci = kParts - 1;
+  //    (HKV * ceil(L / P)), their exclusive prefix sums for the chosen one.
+  //    The partition: the largest power of two (kMfmaMinPartTokens ..
+  //    kMfmaMaxPartTokens) not above the K/V tokens per resident workgroup,
+  //    HKV * sum(L) / slots — long contexts get one long item per workgroup,
+  //    ragged batches many short ones.  Up to kWave sequences every wave
+  //    builds its own copy (lane s owns sequence s; wave w's copy at offset
+  //    w * (kWave + 1) of each array, no workgroup barrier); past that the
+  //    workgroup shares one.
+  static_assert(kGqWaves * (kWave + 1) <= kBalancedMaxSeqs, "every wave's copy of the offsets fits");
+  const bool wave_local = S <= kWave;
+  const int sb = wave_local ? wave * (kWave + 1) : 0;
+  int* const off_l = s_off + sb;
+  int* const len_l = s_len + sb;
+  int pshift = kMinShift;
   int total = 0;
-  int run = 0;
+  if (wave_local) {
+    const int L = lane < S ? min(max(context_lens[lane], 0), cap) : 0;
+    // sum(L) exactly from two 32-bit sums (L < 2^31, at most 64 terms)
+    const long long tokens =
+        static_cast<long long>(__builtin_amdgcn_readlane(wave_prefix_sum(L & 0xFFFF), kWave - 1)) +
+        (static_cast<long long>(__builtin_amdgcn_readlane(wave_prefix_sum(L >> 16), kWave - 1)) << 16);
+    const long long per_slot = static_cast<long long>(HKV) * tokens / max(slots, 1);
 #pragma unroll
-  for (int c = kParts - 1; c >= 0; --c) {
-    int tot = 0, bef = 0;
+    for (int c = kParts - 1; c >= 0; --c)
+      if ((1LL << (kMaxShift - c)) <= per_slot) pshift = kMaxShift - c;
+    const int n = HKV * ((L + (1 << pshift) - 1) >> pshift);
+    const int incl = wave_prefix_sum(n);
+    if (lane < S) {
+      len_l[lane] = L;
+      off_l[lane] = incl - n;
+    }
+    total = min(__builtin_amdgcn_readlane(incl, kWave - 1), max_items);
+    if (lane == 0) off_l[S] = total;
+    // the wave's own LDS writes before its reads below (no other wave reads them)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  } else {
+    for (int s = tid; s < S; s += kThreads) s_len[s] = min(max(context_lens[s], 0), cap);
+    __syncthreads();
+    int mine[kParts];
 #pragma unroll
-    for (int w = 0; w < kGqWaves; ++w) {
-      tot += s_wsum[c][w];
-      bef += (w < wave) ? s_wsum[c][w] : 0;
+    for (int c = 0; c < kParts; ++c) mine[c] = 0;
+    int mine_tok = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int s = tid * kPer + i;
+      const int L = s < S ? s_len[s] : 0;
+      mine_tok += L;
+#pragma unroll
+      for (int c = 0; c < kParts; ++c) mine[c] += HKV * ((L + (1 << (kMaxShift - c)) - 1) >> (kMaxShift - c));
     }
-    if (c == kParts - 1 || (1LL << (kMaxShift - c)) <= per_slot) {
-      ci = c;
-      total = tot;
-      run = bef + incl[c] - mine[c];
+    int incl[kParts];
+#pragma unroll
+    for (int c = 0; c < kParts; ++c) {
+      incl[c] = wave_prefix_sum(mine[c]);
+      if (lane == kWave - 1) s_wsum[c][wave] = incl[c];
     }
+    const int incl_tok = wave_prefix_sum(mine_tok);
+    if (lane == kWave - 1) s_wtok[wave] = incl_tok;
+    __syncthreads();
+    long long tokens = 0;
+#pragma unroll
+    for (int w = 0; w < kGqWaves; ++w) tokens += s_wtok[w];
+    const long long per_slot = static_cast<long long>(HKV) * tokens / max(slots, 1);
+    int ci = kParts - 1;
+    int run = 0;
+#pragma unroll
+    for (int c = kParts - 1; c >= 0; --c) {
+      int tot = 0, bef = 0;
+#pragma unroll
+      for (int w = 0; w < kGqWaves; ++w) {
+        tot += s_wsum[c][w];
+        bef += (w < wave) ? s_wsum[c][w] : 0;
+      }
+      if (c == kParts - 1 || (1LL << (kMaxShift - c)) <= per_slot) {
+        ci = c;
+        total = tot;
+        run = bef + incl[c] - mine[c];
+      }
+    }
+    ci = __builtin_amdgcn_readfirstlane(ci);
+    pshift = kMaxShift - ci;  // P = 2^pshift tokens
+    const int P = 1 << pshift;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int s = tid * kPer + i;
+      if (s < S) s_off[s] = run;
+      run += s < S ? HKV * ((s_len[s] + P - 1) >> pshift) : 0;
+    }
+    total = min(__builtin_amdgcn_readfirstlane(total), max_items);
+    if (tid == 0) s_off[S] = total;
+    __syncthreads();
   }
-  ci = __builtin_amdgcn_readfirstlane(ci);
-  const int pshift = kMaxShift - ci;  // P = 2^pshift tokens
+  pshift = __builtin_amdgcn_readfirstlane(pshift);
   const int P = 1 << pshift;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int s = tid * kPer + i;
-    if (s < S) s_off[s] = run;
-    run += s < S ? HKV * ((s_len[s] + P - 1) >> pshift) : 0;
-  }
-  total = min(__builtin_amdgcn_readfirstlane(total), max_items);
-  if (tid == 0) s_off[S] = total;
-  __syncthreads();
   // the merge kernel reads the same offsets and partition size
-  if (blockIdx.x == 0 && ws_off != nullptr) {
-    for (int s = tid; s <= S; s += kThreads) ws_off[s] = s_off[s];
-    if (tid == 0) ws_off[S + 1] = P;
+  if (blockIdx.x == 0 && wave == 0 && ws_off != nullptr) {
+    for (int s = lane; s <= S; s += kWave) ws_off[s] = off_l[s];
+    if (lane == 0) ws_off[S + 1] = P;
   }
 
   // 2. empty contexts give zero rows (spread over the workgroups)
   for (int s = blockIdx.x; s < S; s += gridDim.x)
-    if (s_len[s] == 0)
+    if (len_l[s] == 0)
       for (int i = tid; i < num_heads * D; i += kThreads)
         out[static_cast<size_t>(s) * num_heads * D + i] = T::pack(0.f);
 
@@ -187,15 +220,15 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
     int hi = S - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= item)
+      if (off_l[mid] <= item)
         lo = mid;
       else
         hi = mid - 1;
     }
     const int s = __builtin_amdgcn_readfirstlane(lo);
-    const int L = __builtin_amdgcn_readfirstlane(s_len[s]);
+    const int L = __builtin_amdgcn_readfirstlane(len_l[s]);
     const int parts = (L + P - 1) >> pshift;
-    const int local = item - __builtin_amdgcn_readfirstlane(s_off[s]);
+    const int local = item - __builtin_amdgcn_readfirstlane(off_l[s]);
     const int kvh = local / parts;
     const int part = local - kvh * parts;
     const int k_begin = part * P;

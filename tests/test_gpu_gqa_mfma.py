@@ -91,6 +91,23 @@ def test_group_sizes(H, Hkv, D, bs):
     assert_close(_run(w), _oracle(w), torch.float16, f"H={H} Hkv={Hkv} D={D} bs={bs}")
 
 
+@pytest.mark.parametrize("S", [64, 65, 300])
+def test_batch_sizes_around_the_wave_local_limit(S):
+    """Up to 64 sequences every wave builds its own item offsets (one lane per
+    sequence, no workgroup barrier); from 65 on the workgroup builds one copy:
+    both sides of the limit, ragged contexts with an empty one, split and
+    unsplit rows."""
+    announce(f"gqa mfma {S} sequences")
+    rng = np.random.default_rng(40 + S)
+    lens = rng.integers(0, 1500, size=S).tolist()
+    lens[S // 2] = 0
+    w = _workload(lens, 32, 4, 128, 16, torch.float16, 40 + S)
+    out = _run(w)
+    assert_close(out, _oracle(w), torch.float16, f"{S} sequences")
+    assert not out[S // 2].any()
+    assert torch.equal(bits(_run(w)), bits(out)), "second call differs"
+
+
 @pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
 def test_negative_zero_and_large_scales(scale):
     announce(f"gqa mfma scale {scale}")
