@@ -51,8 +51,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
 
 
 PF_SOURCES = [os.path.join(ROOT, "paged_kv_cache_186_amd", "csrc", f)
-              for f in ("pa_prefill.hip", "pa_prefill_tiles.hip", "pa_mla_heads.hip", "pa_attend.h", "pa_device.h", "pa_mfma.h",
-                        "pa_internal.h", "pa_api.cpp")]
+              for f in ("pa_prefill.hip", "pa_prefill_tiles.hip", "pa_mla_heads.hip", "pa_decode_mfma.hip", "pa_attend.h",
+                        "pa_device.h", "pa_mfma.h", "pa_internal.h", "pa_api.cpp")]
 
 
 def log(msg: str) -> None:
@@ -448,10 +448,14 @@ def queries_bench(pa, dev, op: str, steps: int, warmup: int, seed: int, heads: i
     # pa_prefill takes its row-block kernel with the default split when the
     # 128-row blocks of (sequence, K/V head) rows fill the GPU (the same test
     # the library makes)
+    # and the grouped-query decode kernel for at most 64 sequences with at most
+    # 16 (32 for groups above 16) query rows per sequence and K/V head on average
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     group = H // Hkv
     tiles = not partition and Hkv * (T * group // 128) >= cus and T * group >= 64 * S
+    few = not partition and S <= 64 and T * group <= (32 if group > 16 else 16) * S
     kernel = (("mla_heads_kernel" if not partition and S <= 512 else "mla_split_kernel") if mla
+              else "decode_mfma_kernel" if few
               else ("prefill_tile_kernel" if tiles else "prefill_kernel"))
     traffic = traffic_from_profile(digest, os.path.join(PROFILES, f"{kernel}_{tag}_traffic.txt"))
     metric = {"prefill": "chunked prefill over the paged cache (pa_prefill): achieved TFLOP/s, 1 MI355X",

@@ -263,7 +263,14 @@ pa_status_t pa_decode_gqa(void* out, const void* q, const void* k_pool, const vo
  *                 block_size 16 or 32.
  *   partition_size: 0 lets the library split long contexts only when the
  *                 query rows alone would not fill the GPU; otherwise keys per
- *                 partition, a positive multiple of 16.
+ *                 partition, a positive multiple of 16.  With 0, at most 64
+ *                 sequences and few rows — num_query_tokens * (num_heads /
+ *                 num_kv_heads) <= 16 * num_seqs (32 * num_seqs for groups
+ *                 of more than 16 heads), as when verifying a few drafted
+ *                 tokens — the call runs on the grouped-query decode kernel
+ *                 (a workgroup's four waves share each item's keys) and a
+ *                 second kernel merges the split rows; its workspace holds
+ *                 the partials and 32 bytes per query token, no counters.
  *   workspace:    pa_prefill_workspace_size() bytes for the same sizes, 0
  *                 when nothing is split (then workspace may be NULL).  It
  *                 begins with arrival counters that must be zero when a call

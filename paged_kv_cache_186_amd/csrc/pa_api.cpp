@@ -536,6 +536,64 @@ pa_status_t mla_heads_impl(void* out, const void* q, const void* kv_pool, const 
 // Shared by pa_prefill and pa_decode_mla; the caller has checked dtype and
 // the head dimension.  Launches once per group of kPfMaxSeqs sequences (the
 // query bounds are absolute row numbers, so q and out are passed whole).
+// pa_prefill through the grouped-query decode kernel (launch_decode_mfma_queries):
+// at most kMfmaQueriesMaxSeqs sequences (its wave-local prologue), the default split, and
+// few rows per sequence — T * G <= 16 * NT * S, i.e. on average at most one
+// chunk of 16 * NT (query token, head) rows per (sequence, K/V head), as in
+// speculative verification of a few drafted tokens.  Its four waves share
+// each item's keys, where prefill_kernel gives an item to one wave.
+// Measured on 64 sequences of continuous-batching lengths, 32 query / 8 K/V
+// heads (prefill_kernel -> this path): 4 drafted tokens 68.8 -> 58.8 us, one
+// token 68.0 -> 51.7 us; with a partition chosen for half or a quarter of the
+// resident workgroups 62.6 / 116.7 and 59.4 / 113.7 us.
+struct QueriesPlan {
+  bool applies;
+  pa_status_t status;
+  int max_items;
+  int workgroups;
+  int slots;
+  size_t tok_offset;  // the per-token merge descriptors ([T][8] int32)
+  pa::WorkspaceLayout ws;
+};
+
+QueriesPlan plan_queries(int32_t num_seqs, int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size,
+                         int32_t head_dim) {
+  QueriesPlan p{false, PA_OK, 0, 0, 0, 0, {0, 0, 0, 0}};
+  if (partition_size != 0 || num_seqs < 1 || num_seqs > pa::kMfmaQueriesMaxSeqs || num_tokens < 1 || num_heads <= 0 ||
+      num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || max_blocks_per_seq <= 0 ||
+      max_blocks_per_seq > INT_MAX / block_size / 2)
+    return p;
+  const long long group = num_heads / num_kv_heads;
+  if (group > pa::kMfmaMaxGroup) return p;
+  const long long rows_per_item = group > 16 ? 32 : 16;
+  if (static_cast<long long>(num_tokens) * group > rows_per_item * num_seqs) return p;
+  p.applies = true;
+  // items: sum over sequences of Hkv * chunks * ceil(L / P), the partition P
+  // (128..2048) chosen on the device as the largest not above
+  // Hkv * sum(chunks * L) / slots.  Bound: that sum is at most
+  // Hkv * sum(chunks) * (L / P + 1), and Hkv * sum(chunks * L) / P is below
+  // 2 * slots unless P is the largest size, where it is at most
+  // Hkv * sum(chunks) * cap / 2048; sum(chunks) <= ceil(T * G / rows) + S.
+  p.slots = cu_count() * pa::mfma_wg_per_cu(static_cast<int>(group));
+  const long long cap = static_cast<long long>(max_blocks_per_seq) * block_size;
+  const long long chunks = (static_cast<long long>(num_tokens) * group + rows_per_item - 1) / rows_per_item + num_seqs;
+  const long long at_max = num_kv_heads * chunks * ((cap + pa::kMfmaMaxPartTokens - 1) / pa::kMfmaMaxPartTokens);
+  const long long items = std::max(2LL * p.slots, at_max) + num_kv_heads * chunks;
+  if (items * rows_per_item > INT_MAX / 2) {
+    p.status = PA_ERR_INVALID_ARG;
+    return p;
+  }
+  p.max_items = static_cast<int>(items);
+  p.workgroups = p.slots;
+  if (cap > pa::kMfmaMinPartTokens) {  // a row can span several partitions
+    p.ws = pa::workspace_layout(0, static_cast<size_t>(items) * rows_per_item, head_dim);
+    p.tok_offset = p.ws.total;
+    p.ws.total = pa::align_up(p.ws.total + static_cast<size_t>(num_tokens) * 8 * sizeof(int32_t), 256);
+  }
+  return p;
+}
+
 pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* block_tables, const int32_t* context_lens,
                          const int32_t* query_start, float scale, int32_t block_size,
@@ -551,6 +609,10 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const voi
                                         max_blocks_per_seq, block_size, partition_size,
                                         v_per_item, 1, row_tiles, latent);
   if (plan.status != PA_OK) return plan.status;
+  const QueriesPlan qp = latent ? QueriesPlan{false, PA_OK, 0, 0, 0, 0, {0, 0, 0, 0}}
+                                : plan_queries(num_seqs, num_query_rows, num_heads, num_kv_heads,
+                                               max_blocks_per_seq, block_size, partition_size, head_dim);
+  if (qp.status != PA_OK) return qp.status;
   if (num_blocks <= 0 || !std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (num_seqs == 0 || num_query_rows == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
@@ -558,9 +620,43 @@ pa_status_t prefill_impl(void* out, const void* q, const void* k_pool, const voi
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
     return PA_ERR_INVALID_ARG;
-  if (plan.ws.total > 0) {
-    if (!workspace || workspace_bytes < plan.ws.total) return PA_ERR_WORKSPACE;
+  const size_t need = qp.applies ? qp.ws.total : plan.ws.total;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return PA_ERR_INVALID_ARG;
+  }
+  if (qp.applies) {  // few rows per sequence: the grouped-query decode kernel
+    pa::DecodeArgs d{};
+    d.out = out;
+    d.q = q;
+    d.k_pool = k_pool;
+    d.v_pool = v_pool;
+    d.block_tables = block_tables;
+    d.context_lens = context_lens;
+    d.scale = scale;
+    d.block_size = block_size;
+    d.num_seqs = num_seqs;
+    d.num_heads = num_heads;
+    d.num_kv_heads = num_kv_heads;
+    d.group_width = 1;
+    d.head_dim = head_dim;
+    d.num_blocks = num_blocks;
+    d.max_blocks_per_seq = max_blocks_per_seq;
+    d.dtype = dtype;
+    d.kv_dtype = dtype;
+    d.mode = pa::DecodeMode::kMfma;
+    d.workgroups = qp.workgroups;
+    d.max_items = qp.max_items;
+    d.mfma_slots = qp.slots;
+    d.query_start = query_start;
+    d.num_tokens = num_query_rows;
+    if (qp.ws.total > 0) {
+      char* ws = static_cast<char*>(workspace);
+      d.ws_ml = reinterpret_cast<float*>(ws + qp.ws.ml_offset);
+      d.ws_acc = reinterpret_cast<float*>(ws + qp.ws.acc_offset);
+      d.ws_tok = reinterpret_cast<int*>(ws + qp.tok_offset);
+    }
+    return pa::launch_decode_mfma_queries(d, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   pa::PrefillArgs a{};
   a.out = out;
@@ -876,6 +972,9 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_query_tokens, int
                                  int32_t block_size, int32_t partition_size) {
   if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32)) return 0;
   if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return 0;
+  const QueriesPlan qp = plan_queries(num_seqs, num_query_tokens, num_heads, num_kv_heads, max_blocks_per_seq,
+                                      block_size, partition_size, head_dim);
+  if (qp.applies) return qp.status == PA_OK ? qp.ws.total : 0;
   const PrefillPlan p = plan_prefill(num_seqs, num_query_tokens, num_heads, num_kv_heads,
                                      max_blocks_per_seq, block_size, partition_size, head_dim, 1,
                                      prefill_row_tiles(num_seqs, num_query_tokens, num_heads, num_kv_heads,

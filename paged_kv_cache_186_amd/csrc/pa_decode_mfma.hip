@@ -64,14 +64,23 @@ constexpr int kGqWaves = 4;
 // 14.1 / 16.3; continuous batching with 8 K/V heads 53.6 / 51.5 / 56.7 (32 /
 // 128, 64 / 128, 32 / 256).
 constexpr int kMergeRowsFew = 256;  // fewer (sequence, head) rows than this: few rows
+static_assert(kMfmaQueriesMaxSeqs == kWave, "the query kernel keeps one sequence per lane");
 
-template <typename T, int D, int BS, int NT>
+// MQ: several query tokens per sequence (query_start, num_tokens): a
+// sequence's rows are its (query token, head of the group) pairs,
+// token-major, in chunks of 16 * NT rows; items (sequence, K/V head, chunk,
+// partition); row r of a chunk sees the keys up to its token's position
+// (causal); split rows are merged by lse_merge_tokens_kernel through the
+// per-token descriptors in ws_tok.  Only with at most kMfmaQueriesMaxSeqs
+// (= kWave) sequences (the wave-local prologue).
+template <typename T, int D, int BS, int NT, bool MQ>
 __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_kernel(
     typename T::storage* __restrict__ out, const typename T::storage* __restrict__ q,
     const char* __restrict__ k_pool, const char* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int* __restrict__ ws_off, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, float qk_scale, uint32_t q_sign_bits, int num_seqs, int num_heads,
-    int num_kv_heads, int group, int num_blocks, int max_blocks, int max_items, int slots) {
+    int num_kv_heads, int group, int num_blocks, int max_blocks, int max_items, int slots,
+    const int32_t* __restrict__ query_start, int num_tokens, int* __restrict__ ws_tok) {
   static_assert(D % 64 == 0 && BS % 16 == 0, "MFMA slices");
   using S16 = typename T::storage;
   using M = Mfma<T>;
@@ -86,8 +95,13 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
   constexpr int kMinShift = __builtin_ctz(kMfmaMinPartTokens);
   constexpr int kMaxShift = __builtin_ctz(kMfmaMaxPartTokens);
   constexpr int kParts = kMaxShift - kMinShift + 1;
+  constexpr int kRows = 16 * NT;  // rows of an item (MQ: a chunk of the sequence's rows)
   __shared__ int s_off[kBalancedMaxSeqs + 1];
   __shared__ int s_len[kBalancedMaxSeqs];
+  // MQ: first query token, query tokens and chunks of each sequence (each wave its own copy)
+  __shared__ int s_qst[MQ ? kGqWaves * (kWave + 1) : 1];
+  __shared__ int s_tq[MQ ? kGqWaves * (kWave + 1) : 1];
+  __shared__ int s_nch[MQ ? kGqWaves * (kWave + 1) : 1];
   __shared__ int s_wsum[kParts][kGqWaves];
   __shared__ int s_wtok[kGqWaves];
   __shared__ float s_m[kGqWaves][NT][16];
@@ -113,27 +127,52 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
   //    w * (kWave + 1) of each array, no workgroup barrier); past that the
   //    workgroup shares one.
   static_assert(kGqWaves * (kWave + 1) <= kBalancedMaxSeqs, "every wave's copy of the offsets fits");
+  if (MQ && S > kWave) return;  // the host never launches this
   const bool wave_local = S <= kWave;
   const int sb = wave_local ? wave * (kWave + 1) : 0;
   int* const off_l = s_off + sb;
   int* const len_l = s_len + sb;
+  int* const qst_l = s_qst + (MQ ? sb : 0);
+  int* const tq_l = s_tq + (MQ ? sb : 0);
+  int* const nch_l = s_nch + (MQ ? sb : 0);
   int pshift = kMinShift;
   int total = 0;
+  int my_qst = 0, my_tq = 0;  // MQ: lane s's first query token and query tokens
   if (wave_local) {
     const int L = lane < S ? min(max(context_lens[lane], 0), cap) : 0;
-    // sum(L) exactly from two 32-bit sums (L < 2^31, at most 64 terms)
-    const long long tokens =
-        static_cast<long long>(__builtin_amdgcn_readlane(wave_prefix_sum(L & 0xFFFF), kWave - 1)) +
-        (static_cast<long long>(__builtin_amdgcn_readlane(wave_prefix_sum(L >> 16), kWave - 1)) << 16);
+    int nch = 1;  // chunks of the sequence's rows (one row group without MQ)
+    if constexpr (MQ) {
+      if (lane < S) {
+        const int a0 = min(max(query_start[lane], 0), num_tokens);
+        const int a1 = min(max(query_start[lane + 1], 0), num_tokens);
+        my_qst = a0;
+        my_tq = max(a1 - a0, 0);
+      }
+      nch = (my_tq * G + kRows - 1) / kRows;
+    }
+    // the work: sum over sequences of chunks * L, exactly, from 21-bit pieces
+    // (chunks * L < 2^52, at most 64 terms per piece sum)
+    const unsigned long long x = static_cast<unsigned long long>(nch) * static_cast<unsigned long long>(L);
+    long long tokens = 0;
+#pragma unroll
+    for (int piece = 0; piece < (MQ ? 3 : 2); ++piece) {
+      const int v = static_cast<int>((x >> (21 * piece)) & 0x1FFFFF);
+      tokens += static_cast<long long>(__builtin_amdgcn_readlane(wave_prefix_sum(v), kWave - 1)) << (21 * piece);
+    }
     const long long per_slot = static_cast<long long>(HKV) * tokens / max(slots, 1);
 #pragma unroll
     for (int c = kParts - 1; c >= 0; --c)
       if ((1LL << (kMaxShift - c)) <= per_slot) pshift = kMaxShift - c;
-    const int n = HKV * ((L + (1 << pshift) - 1) >> pshift);
+    const int n = HKV * nch * ((L + (1 << pshift) - 1) >> pshift);
     const int incl = wave_prefix_sum(n);
     if (lane < S) {
       len_l[lane] = L;
       off_l[lane] = incl - n;
+      if constexpr (MQ) {
+        qst_l[lane] = my_qst;
+        tq_l[lane] = my_tq;
+        nch_l[lane] = nch;
+      }
     }
     total = min(__builtin_amdgcn_readlane(incl, kWave - 1), max_items);
     if (lane == 0) off_l[S] = total;
@@ -198,17 +237,54 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
   }
   pshift = __builtin_amdgcn_readfirstlane(pshift);
   const int P = 1 << pshift;
-  // the merge kernel reads the same offsets and partition size
-  if (blockIdx.x == 0 && wave == 0 && ws_off != nullptr) {
-    for (int s = lane; s <= S; s += kWave) ws_off[s] = off_l[s];
-    if (lane == 0) ws_off[S + 1] = P;
+  if constexpr (!MQ) {
+    // the merge kernel reads the same offsets and partition size
+    if (blockIdx.x == 0 && wave == 0 && ws_off != nullptr) {
+      for (int s = lane; s <= S; s += kWave) ws_off[s] = off_l[s];
+      if (lane == 0) ws_off[S + 1] = P;
+    }
+  } else if (wave == 0 && ws_tok != nullptr) {
+    // the merge kernel's descriptor of every query token (its sequence, its
+    // index there, the sequence's query tokens, item offset, partitions and
+    // chunks, the partition size; or not covered), the tokens spread over
+    // the workgroups: lane l finds its token's sequence — the last whose
+    // first token is at most its own (the lanes' first tokens are
+    // non-decreasing) — by binary lifting over the lanes, six steps in every
+    // lane: a lane that reads another's value by a cross-lane read must not
+    // have left the loop before it (an inactive source lane reads as zero)
+    for (int t0 = blockIdx.x * kWave; t0 < num_tokens; t0 += gridDim.x * kWave) {
+      const int t = t0 + lane;
+      int lo = 0;
+#pragma unroll
+      for (int step = kWave / 2; step > 0; step >>= 1) {
+        const int cand = lo + step;
+        const int v = __shfl(my_qst, min(cand, S - 1));  // every lane, every step
+        lo = (cand < S && v <= t) ? cand : lo;
+      }
+      const int a0 = __shfl(my_qst, lo);
+      const int n0 = __shfl(my_tq, lo);
+      if (t < num_tokens) {
+        const bool in = t >= a0 && t - a0 < n0;
+        const int Ls = len_l[lo];
+        const int4 d0 = {lo, t - a0, n0, off_l[lo]};
+        const int4 d1 = {(Ls + P - 1) >> pshift, nch_l[lo], P, in ? 1 : 0};
+        *reinterpret_cast<int4*>(ws_tok + 8 * static_cast<size_t>(t)) = d0;
+        *reinterpret_cast<int4*>(ws_tok + 8 * static_cast<size_t>(t) + 4) = d1;
+      }
+    }
   }
 
   // 2. empty contexts give zero rows (spread over the workgroups)
   for (int s = blockIdx.x; s < S; s += gridDim.x)
-    if (len_l[s] == 0)
-      for (int i = tid; i < num_heads * D; i += kThreads)
-        out[static_cast<size_t>(s) * num_heads * D + i] = T::pack(0.f);
+    if (len_l[s] == 0) {
+      if constexpr (MQ) {
+        const size_t r0 = static_cast<size_t>(qst_l[s]) * num_heads * D;
+        for (int i = tid; i < tq_l[s] * num_heads * D; i += kThreads) out[r0 + i] = T::pack(0.f);
+      } else {
+        for (int i = tid; i < num_heads * D; i += kThreads)
+          out[static_cast<size_t>(s) * num_heads * D + i] = T::pack(0.f);
+      }
+    }
 
   const u32x4 q_sign = {q_sign_bits, q_sign_bits, q_sign_bits, q_sign_bits};
   const int col = lane % 16;  // query row of a tile / key of a 16-key block
@@ -229,18 +305,39 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
     const int L = __builtin_amdgcn_readfirstlane(len_l[s]);
     const int parts = (L + P - 1) >> pshift;
     const int local = item - __builtin_amdgcn_readfirstlane(off_l[s]);
-    const int kvh = local / parts;
-    const int part = local - kvh * parts;
+    const int pc = local / parts;  // (K/V head, chunk) pair
+    const int part = local - pc * parts;
+    // MQ: the sequence's query tokens, its first, this item's chunk
+    const int tq = MQ ? __builtin_amdgcn_readfirstlane(tq_l[s]) : 1;
+    const int qs0 = MQ ? __builtin_amdgcn_readfirstlane(qst_l[s]) : s;
+    const int nch = MQ ? __builtin_amdgcn_readfirstlane(nch_l[s]) : 1;
+    const int kvh = MQ ? pc / nch : pc;
+    const int chunk = MQ ? pc - kvh * nch : 0;
+    const int nrows = MQ ? tq * G : G;  // rows of this (sequence, K/V head)
+    const int row0 = chunk * kRows;     // first row of the item
+    // keys the chunk's rows see: up to the position of its last row's token
+    // (query token i sits at L - tq + i); its first row's bound below which
+    // no key needs a mask
+    const int last_row = min(nrows, row0 + kRows) - 1;
+    const int L_c = MQ ? min(L, L - tq + last_row / G + 1) : L;
+    const int lim_min = MQ ? L - tq + row0 / G + 1 : L;
     const int k_begin = part * P;
-    const int k_end = min(k_begin + P, L);
+    const int k_end = max(min(k_begin + P, L_c), k_begin);  // MQ: an item past L_c has no keys
+    const int k_unmasked = min(k_end, lim_min);
 
-    // query rows of tile t: heads kvh*G + 16t + col (B operand of S^T)
+    // query rows of tile t: rows row0 + 16t + col (B operand of S^T), row r
+    // being token r / G and head kvh*G + r % G (without MQ: token 0, head
+    // kvh*G + r); klim[t]: the keys this lane's row of tile t sees
     u32x4 qv[NT][kQK];
+    int klim[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int r = 16 * t + col;
-      const bool ok = r < G;
-      const S16* qrow = q + (static_cast<size_t>(s) * num_heads + kvh * G + (ok ? r : 0)) * D + 8 * g4;
+      const int r = row0 + 16 * t + col;
+      const bool ok = r < nrows;
+      const int tok = MQ ? (ok ? r / G : 0) : 0;
+      const int hg = MQ ? (ok ? r - tok * G : 0) : (ok ? r : 0);
+      klim[t] = MQ ? min(k_end, L - tq + tok + 1) : k_end;
+      const S16* qrow = q + (static_cast<size_t>(qs0 + tok) * num_heads + kvh * G + hg) * D + 8 * g4;
 #pragma unroll
       for (int j = 0; j < kQK; ++j) {
         const u32x4 v = load16(qrow + 32 * j) ^ q_sign;  // a negative scale flips q's signs instead
@@ -273,7 +370,7 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
     // of a scalar memory round trip before its K/V loads can be issued
     const int32_t* tbl = block_tables + static_cast<size_t>(s) * max_blocks;
     const int blk0 = k_begin / BS;
-    const int nblk = (k_end - k_begin + BS - 1) / BS;
+    const int nblk = max((k_end - k_begin + BS - 1) / BS, 1);  // an empty item reads its first entry
     int tblv[kTblRegs];
 #pragma unroll
     for (int r = 0; r < kTblRegs; ++r) tblv[r] = tbl[blk0 + min(lane + kWave * r, nblk - 1)];
@@ -319,7 +416,7 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
 #pragma unroll
               for (int dq = 0; dq < kDq; ++dq) st.v[kb][dq][e] = u32x2{0u, 0u};
       }
-      const bool masked = st.c + 32 > k_end;
+      const bool masked = st.c + 32 > k_unmasked;
       f4_t scs[NT][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -341,7 +438,7 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
           if (masked) {
             const int key = st.c + 16 * kb + 4 * g4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) z[kb][i] = (key + i < k_end) ? z[kb][i] : -INFINITY;
+            for (int i = 0; i < 4; ++i) z[kb][i] = (key + i < klim[t]) ? z[kb][i] : -INFINITY;
           }
         }
         float cm = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
@@ -431,8 +528,8 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
       const int c4 = x % (D / 4);
       const int r = (x / (D / 4)) % 16;
       const int t = x / (16 * (D / 4));
-      const int row = 16 * t + r;  // head of the group
-      if (row >= G) continue;
+      const int row = 16 * t + r;  // row of the item (without MQ: head of the group)
+      if (row0 + row >= nrows) continue;
       float Mx = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kGqWaves; ++w) Mx = fmaxf(Mx, s_m[w][t][r]);
@@ -446,14 +543,18 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
         o += f * s_o[w][t][r][c4];
       }
       if (any_bad) l = __builtin_nanf("");
-      const size_t h = static_cast<size_t>(kvh) * G + row;
+      // the row's query token (a sequence's rows are token-major) and head
+      const int tok = MQ ? (row0 + row) / G : 0;
+      const size_t h = static_cast<size_t>(kvh) * G + (MQ ? row0 + row - tok * G : row);
       if (parts == 1) {
-        const float inv = 1.f / l;
+        // MQ: a row whose token sits before position 0 sees no key: zero
+        const float inv = (MQ && l == 0.f) ? 0.f : 1.f / l;
         const uint32_t w0 = M::pack2(o[0] * inv, o[1] * inv);
         const uint32_t w1 = M::pack2(o[2] * inv, o[3] * inv);
-        *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(s) * num_heads + h) * D + 4 * c4) = u32x2{w0, w1};
+        *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(qs0 + tok) * num_heads + h) * D + 4 * c4) =
+            u32x2{w0, w1};
       } else {
-        const size_t slot = static_cast<size_t>(item) * G + row;
+        const size_t slot = static_cast<size_t>(item) * (MQ ? kRows : G) + row;
         *reinterpret_cast<f4_t*>(ws_acc + slot * D + 4 * c4) = o;
         if (c4 == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{Mx, l};
       }
@@ -462,48 +563,138 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
   }
 }
 
-template <typename T, int D, int BS, int NT>
+// Log-sum-exp merge of the split rows of several query tokens per sequence
+// (launch_decode_mfma_queries): one wave per (query token, head) row, four
+// rows per workgroup.  The token's descriptor in ws_tok (what the first
+// kernel wrote: its sequence, its index i there, the sequence's query
+// tokens, item offset, partitions, chunks, partition size, whether a
+// sequence covers it) places row r = i * group + h % group of K/V head
+// h / group in chunk r / RPI of the sequence's items, at slot
+// item * RPI + r % RPI of each.  Lane l holds elements 4 * (l % kC) .. + 3 of
+// the partials l / kC, l / kC + kG, ..., kU of them in flight per round,
+// folded into a running (max, sum, sums) with the online rescaling; the kG
+// lane groups are then folded by cross-lane reads.  Slots past max_items are
+// never read; a row that saw no key (every partial empty) comes out zero.
+template <typename T, int D, int RPI>
+__global__ __launch_bounds__(256) void lse_merge_tokens_kernel(
+    typename T::storage* __restrict__ out, const int* __restrict__ ws_tok, const float* __restrict__ ws_ml,
+    const float* __restrict__ ws_acc, int num_rows, int num_heads, int group, int max_items) {
+  constexpr int kC = D / 4;        // lanes over one partial's D elements
+  constexpr int kG = kWave / kC;   // partials side by side
+  constexpr int kU = 8;
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * 4 + static_cast<int>(threadIdx.x / kWave);
+  if (row >= num_rows) return;
+  const int t = row / num_heads;
+  const int h = row - t * num_heads;
+  const int4 d0 = *reinterpret_cast<const int4*>(ws_tok + 8 * static_cast<size_t>(t));
+  const int4 d1 = *reinterpret_cast<const int4*>(ws_tok + 8 * static_cast<size_t>(t) + 4);
+  const int parts = d1.x;
+  if (d1.w == 0 || parts <= 1) return;  // not covered, or written by the first kernel
+  const int r = d0.y * group + h % group;
+  const size_t item0 = static_cast<size_t>(d0.w) + (static_cast<size_t>(h / group) * d1.y + r / RPI) * parts;
+  if (item0 + parts > static_cast<size_t>(max_items)) return;
+  const int g = r % RPI;
+  const int c = lane % kC;
+  const int gl = lane / kC;
+  float Mx = -INFINITY, den = 0.f;
+  f4_t num = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < parts; p0 += kG * kU) {
+    f32x2 ml[kU];
+    f4_t v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const size_t slot = (item0 + min(p0 + u * kG + gl, parts - 1)) * RPI + g;
+      ml[u] = *reinterpret_cast<const f32x2*>(ws_ml + slot * 2);
+      v[u] = *reinterpret_cast<const f4_t*>(ws_acc + slot * D + 4 * c);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (p0 + u * kG + gl < parts) bm = fmaxf(bm, ml[u][0]);
+    const float mn = fmaxf(Mx, bm);
+    if (mn == -INFINITY) continue;  // only empty partials so far
+    const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
+    den *= a;
+    num *= a;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float mu = ml[u][0];
+      const float wgt = (p0 + u * kG + gl < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f;
+      den = fmaf(wgt, ml[u][1], den);
+      num += wgt * v[u];
+    }
+    Mx = mn;
+  }
+  const float M = fold_max<kC>(Mx);
+  const float f = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - M);
+  den = fold_sum<kC>(den * f);
+  float o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = fold_sum<kC>(num[e] * f);
+  if (gl == 0) {
+    const float inv = den == 0.f ? 0.f : 1.f / den;
+    const uint32_t w0 = Mfma<T>::pack2(o[0] * inv, o[1] * inv);
+    const uint32_t w1 = Mfma<T>::pack2(o[2] * inv, o[3] * inv);
+    *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(t) * num_heads + h) * D + 4 * c) = u32x2{w0, w1};
+  }
+}
+
+template <typename T, int D, int BS, int NT, bool MQ>
 hipError_t run_mfma(const DecodeArgs& a, hipStream_t stream) {
   using S16 = typename T::storage;
-  hipLaunchKernelGGL((decode_mfma_kernel<T, D, BS, NT>), dim3(a.workgroups), dim3(kGqWaves * kWave), 0, stream,
+  hipLaunchKernelGGL((decode_mfma_kernel<T, D, BS, NT, MQ>), dim3(a.workgroups), dim3(kGqWaves * kWave), 0, stream,
                      static_cast<S16*>(a.out), static_cast<const S16*>(a.q), static_cast<const char*>(a.k_pool),
                      static_cast<const char*>(a.v_pool), a.block_tables, a.context_lens, a.ws_off, a.ws_ml,
                      a.ws_acc, fabsf(a.scale) * kLog2e, a.scale < 0.f ? 0x80008000u : 0u, a.num_seqs,
                      a.num_heads, a.num_kv_heads, a.num_heads / a.num_kv_heads, a.num_blocks,
-                     a.max_blocks_per_seq, a.max_items, a.mfma_slots);
+                     a.max_blocks_per_seq, a.max_items, a.mfma_slots, a.query_start, a.num_tokens, a.ws_tok);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ws_ml == nullptr) return e;
+  const int group = a.num_heads / a.num_kv_heads;
+  if constexpr (MQ) {  // (query token, head) rows, four per workgroup
+    const int rows = a.num_tokens * a.num_heads;
+    hipLaunchKernelGGL((lse_merge_tokens_kernel<T, D, 16 * NT>), dim3((rows + 3) / 4), dim3(4 * kWave), 0, stream,
+                       static_cast<S16*>(a.out), a.ws_tok, a.ws_ml, a.ws_acc, rows, a.num_heads, group, a.max_items);
+    return hipGetLastError();
+  }
   const int rows = a.num_seqs * a.num_heads;
+  const int cap = a.max_blocks_per_seq * a.block_size;
   if (rows < kMergeRowsFew)
     hipLaunchKernelGGL((lse_merge_kernel<T, D, 32, 128>), dim3(rows * (D / 32)), dim3(128), 0, stream,
                        static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
-                       a.num_heads, a.num_heads / a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
+                       a.num_heads, group, cap);
   else
     hipLaunchKernelGGL((lse_merge_kernel<T, D, 64, 128>), dim3(rows * (D / 64)), dim3(128), 0, stream,
                        static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
-                       a.num_heads, a.num_heads / a.num_kv_heads, a.max_blocks_per_seq * a.block_size);
+                       a.num_heads, group, cap);
   return hipGetLastError();
 }
 
-template <typename T, int D, int BS>
+template <typename T, int D, int BS, bool MQ>
 hipError_t run_mfma_nt(const DecodeArgs& a, hipStream_t stream) {
-  return (a.num_heads / a.num_kv_heads) > 16 ? run_mfma<T, D, BS, 2>(a, stream) : run_mfma<T, D, BS, 1>(a, stream);
+  return (a.num_heads / a.num_kv_heads) > 16 ? run_mfma<T, D, BS, 2, MQ>(a, stream)
+                                             : run_mfma<T, D, BS, 1, MQ>(a, stream);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool MQ>
 hipError_t run_mfma_bs(const DecodeArgs& a, hipStream_t stream) {
-  return a.block_size == 16 ? run_mfma_nt<T, D, 16>(a, stream) : run_mfma_nt<T, D, 32>(a, stream);
+  return a.block_size == 16 ? run_mfma_nt<T, D, 16, MQ>(a, stream) : run_mfma_nt<T, D, 32, MQ>(a, stream);
 }
 
-template <typename T>
+template <typename T, bool MQ>
 hipError_t run_mfma_d(const DecodeArgs& a, hipStream_t stream) {
-  return a.head_dim == 64 ? run_mfma_bs<T, 64>(a, stream) : run_mfma_bs<T, 128>(a, stream);
+  return a.head_dim == 64 ? run_mfma_bs<T, 64, MQ>(a, stream) : run_mfma_bs<T, 128, MQ>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
-  return a.dtype == PA_DTYPE_BF16 ? run_mfma_d<BF16>(a, stream) : run_mfma_d<F16>(a, stream);
+  return a.dtype == PA_DTYPE_BF16 ? run_mfma_d<BF16, false>(a, stream) : run_mfma_d<F16, false>(a, stream);
+}
+
+hipError_t launch_decode_mfma_queries(const DecodeArgs& a, hipStream_t stream) {
+  return a.dtype == PA_DTYPE_BF16 ? run_mfma_d<BF16, true>(a, stream) : run_mfma_d<F16, true>(a, stream);
 }
 
 }  // namespace pa

@@ -74,6 +74,12 @@ struct DecodeArgs {
   int* ws_off;           // kMfma: [S + 2] item offsets and the partition size, for the merge
   int max_items;         // kMfma: items the workspace holds (slots = max_items * group)
   int mfma_slots;        // kMfma: workgroups resident on the whole GPU at once
+  // several query tokens per sequence (pa_prefill through the grouped-query
+  // kernel): query_start [S + 1], num_tokens, and the per-token merge
+  // descriptors [num_tokens][8]; null / 0 for decode
+  const int32_t* query_start;
+  int num_tokens;
+  int* ws_tok;
 };
 
 // Workspace of pa_decode: the ticket counters come first (they must be zero
@@ -177,6 +183,11 @@ constexpr int kMfmaMaxWorkgroups = PA_GQ_MAX_WG;
 // (groups of up to 16 heads), one with two (register file).
 inline int mfma_wg_per_cu(int group) { return group > 16 ? 1 : 2; }
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+// the same kernel over several query tokens per sequence (pa_prefill with at
+// most kMfmaQueriesMaxSeqs sequences and few rows each): rows (query token, head of the
+// group), token-major, in chunks of 16 or 32; causal per row
+hipError_t launch_decode_mfma_queries(const DecodeArgs& a, hipStream_t stream);
+constexpr int kMfmaQueriesMaxSeqs = 64;  // one lane of a wave per sequence
 
 // Attention of several query rows per (sequence, K/V head) on the matrix
 // cores: multi-token queries (pa_prefill) and decode over an MLA latent cache

@@ -342,6 +342,24 @@ def test_prefill_workspace_rules(lib):
     assert lib.pa_prefill_workspace_size(2, 8, 32, 8, 96, 64, 16, 0) == 0     # unsupported head_dim
 
 
+def test_prefill_few_rows_workspace_layout(lib):
+    """At most 64 sequences with at most 16 (query token, head) rows per
+    sequence and K/V head on average take the grouped-query decode kernel:
+    its partials for a bound on the items (slots = 256 CUs x 2 workgroups;
+    items <= max(2 * slots, Hkv * chunks * ceil(cap / 2048)) + Hkv * chunks,
+    chunks = ceil(T * G / 16) + S; 16 rows each), then 8 int32 per query token."""
+    def up(x):
+        return -(-x // 256) * 256
+    S, T, H, Hkv, D, W, bs = 2, 8, 32, 8, 128, 8192, 16
+    chunks = -(-T * (H // Hkv) // 16) + S
+    items = max(2 * 512, Hkv * chunks * -(-W * bs // 2048)) + Hkv * chunks
+    slots = items * 16
+    expect = up(up(up(slots * 8) + slots * D * 4) + T * 32)
+    assert lib.pa_prefill_workspace_size(S, T, H, Hkv, D, W, bs, 0) == expect
+    # a table of at most 128 tokens: every row in one partition, no workspace
+    assert lib.pa_prefill_workspace_size(S, T, H, Hkv, D, 8, bs, 0) == 0
+
+
 def _mla(lib, **kw):
     a = dict(out=FAKE, q=FAKE, kv=FAKE, bt=FAKE, cl=FAKE, scale=0.1, bs=16, S=4, H=16, N=16, W=3, P=0,
              dt=BF16, ws=None, wsb=0)
