@@ -53,24 +53,23 @@ namespace pa {
 namespace {
 
 constexpr int kGqWaves = 4;
-// the merge of split rows: 32-element slices of D per workgroup of 256
-// threads (32 lane groups, 8 partials each per round)
-// The merge's shape: workgroups of THREADS lanes, each over a SLICE-element
-// slice of one (sequence, head) row.  Few rows (long contexts: many
-// partials per row) take 32-element slices and 128 lanes, many rows
-// (batches) 64-element slices and 128 lanes.  Measured (main kernel +
-// merge, µs; 32 / 256 before): 128K with 4 K/V heads 48.3 / 49.0 / 49.1,
-// with 1 K/V head 23.0 / 24.2 / 22.9; layer shape with 8 K/V heads 15.1 /
-// 14.1 / 16.3; continuous batching with 8 K/V heads 53.6 / 51.5 / 56.7 (32 /
-// 128, 64 / 128, 32 / 256).
-constexpr int kMergeRowsFew = 256;  // fewer (sequence, head) rows than this: few rows
+// The merge's shape.  Few (sequence, head) rows (long contexts: many
+// partials per row): lse_merge_kernel, a workgroup of 128 lanes per
+// 32-element slice of a row.  Many rows (batches: few partials each):
+// lse_merge_wave_kernel, one wave per row, four rows per workgroup.
+// Measured (main kernel + merge, µs): 128K with 4 K/V heads 48.3 / 49.0 /
+// 49.1 with slices of 32 / 64 / 32 elements over 128 / 128 / 256 lanes, with
+// 1 K/V head 23.0 / 24.2 / 22.9; layer shape with 8 K/V heads 15.1 / 14.1 /
+// 16.3 and 12.75 one wave per row; continuous batching with 8 K/V heads
+// 53.6 / 51.5 / 56.7 and 47.6, with 4 K/V heads 34.3 (64 / 128) and 32.5.
+constexpr int kMergeRowsFew = 256;  // fewer rows than this: a workgroup per slice
 static_assert(kMfmaQueriesMaxSeqs == kWave, "the query kernel keeps one sequence per lane");
 
 // MQ: several query tokens per sequence (query_start, num_tokens): a
 // sequence's rows are its (query token, head of the group) pairs,
 // token-major, in chunks of 16 * NT rows; items (sequence, K/V head, chunk,
 // partition); row r of a chunk sees the keys up to its token's position
-// (causal); split rows are merged by lse_merge_tokens_kernel through the
+// (causal); split rows are merged by lse_merge_wave_kernel through the
 // per-token descriptors in ws_tok.  Only with at most kMfmaQueriesMaxSeqs
 // (= kWave) sequences (the wave-local prologue).
 template <typename T, int D, int BS, int NT, bool MQ>
@@ -575,26 +574,45 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
 // folded into a running (max, sum, sums) with the online rescaling; the kG
 // lane groups are then folded by cross-lane reads.  Slots past max_items are
 // never read; a row that saw no key (every partial empty) comes out zero.
-template <typename T, int D, int RPI>
-__global__ __launch_bounds__(256) void lse_merge_tokens_kernel(
-    typename T::storage* __restrict__ out, const int* __restrict__ ws_tok, const float* __restrict__ ws_ml,
-    const float* __restrict__ ws_acc, int num_rows, int num_heads, int group, int max_items) {
+//
+// TOKENS false: the rows of pa_decode_gqa, (sequence, head), addressed as in
+// lse_merge_kernel through ws_off and context_lens (slot (off[s] + (h /
+// group) * parts + p) * group + h % group): for many rows with few
+// partials each, where one wave per row beats a workgroup per slice.
+template <typename T, int D, int RPI, bool TOKENS>
+__global__ __launch_bounds__(256) void lse_merge_wave_kernel(
+    typename T::storage* __restrict__ out, const int* __restrict__ ws_tok, const int* __restrict__ ws_off,
+    const int32_t* __restrict__ context_lens, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+    int num_rows, int num_seqs, int num_heads, int group, int cap, int max_items) {
   constexpr int kC = D / 4;        // lanes over one partial's D elements
   constexpr int kG = kWave / kC;   // partials side by side
   constexpr int kU = 8;
   const int lane = threadIdx.x % kWave;
   const int row = blockIdx.x * 4 + static_cast<int>(threadIdx.x / kWave);
   if (row >= num_rows) return;
-  const int t = row / num_heads;
+  const int t = row / num_heads;  // query token (TOKENS) or sequence
   const int h = row - t * num_heads;
-  const int4 d0 = *reinterpret_cast<const int4*>(ws_tok + 8 * static_cast<size_t>(t));
-  const int4 d1 = *reinterpret_cast<const int4*>(ws_tok + 8 * static_cast<size_t>(t) + 4);
-  const int parts = d1.x;
-  if (d1.w == 0 || parts <= 1) return;  // not covered, or written by the first kernel
-  const int r = d0.y * group + h % group;
-  const size_t item0 = static_cast<size_t>(d0.w) + (static_cast<size_t>(h / group) * d1.y + r / RPI) * parts;
+  int parts, g, stride;
+  size_t item0;
+  if constexpr (TOKENS) {
+    const int4 d0 = *reinterpret_cast<const int4*>(ws_tok + 8 * static_cast<size_t>(t));
+    const int4 d1 = *reinterpret_cast<const int4*>(ws_tok + 8 * static_cast<size_t>(t) + 4);
+    parts = d1.x;
+    if (d1.w == 0 || parts <= 1) return;  // not covered, or written by the first kernel
+    const int r = d0.y * group + h % group;
+    item0 = static_cast<size_t>(d0.w) + (static_cast<size_t>(h / group) * d1.y + r / RPI) * parts;
+    g = r % RPI;
+    stride = RPI;
+  } else {
+    const int L = min(max(context_lens[t], 0), cap);
+    const int P = ws_off[num_seqs + 1];
+    parts = (L + P - 1) / P;
+    if (parts <= 1) return;  // written by the first kernel
+    item0 = static_cast<size_t>(ws_off[t]) + static_cast<size_t>(h / group) * parts;
+    g = h % group;
+    stride = group;
+  }
   if (item0 + parts > static_cast<size_t>(max_items)) return;
-  const int g = r % RPI;
   const int c = lane % kC;
   const int gl = lane / kC;
   float Mx = -INFINITY, den = 0.f;
@@ -604,7 +622,7 @@ __global__ __launch_bounds__(256) void lse_merge_tokens_kernel(
     f4_t v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const size_t slot = (item0 + min(p0 + u * kG + gl, parts - 1)) * RPI + g;
+      const size_t slot = (item0 + min(p0 + u * kG + gl, parts - 1)) * stride + g;
       ml[u] = *reinterpret_cast<const f32x2*>(ws_ml + slot * 2);
       v[u] = *reinterpret_cast<const f4_t*>(ws_acc + slot * D + 4 * c);
     }
@@ -654,20 +672,23 @@ hipError_t run_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_heads / a.num_kv_heads;
   if constexpr (MQ) {  // (query token, head) rows, four per workgroup
     const int rows = a.num_tokens * a.num_heads;
-    hipLaunchKernelGGL((lse_merge_tokens_kernel<T, D, 16 * NT>), dim3((rows + 3) / 4), dim3(4 * kWave), 0, stream,
-                       static_cast<S16*>(a.out), a.ws_tok, a.ws_ml, a.ws_acc, rows, a.num_heads, group, a.max_items);
+    hipLaunchKernelGGL((lse_merge_wave_kernel<T, D, 16 * NT, true>), dim3((rows + 3) / 4), dim3(4 * kWave), 0,
+                       stream, static_cast<S16*>(a.out), a.ws_tok, nullptr, nullptr, a.ws_ml, a.ws_acc, rows,
+                       a.num_seqs, a.num_heads, group, 0, a.max_items);
     return hipGetLastError();
   }
   const int rows = a.num_seqs * a.num_heads;
   const int cap = a.max_blocks_per_seq * a.block_size;
-  if (rows < kMergeRowsFew)
-    hipLaunchKernelGGL((lse_merge_kernel<T, D, 32, 128>), dim3(rows * (D / 32)), dim3(128), 0, stream,
-                       static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
-                       a.num_heads, group, cap);
-  else
-    hipLaunchKernelGGL((lse_merge_kernel<T, D, 64, 128>), dim3(rows * (D / 64)), dim3(128), 0, stream,
-                       static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
-                       a.num_heads, group, cap);
+  if (rows >= kMergeRowsFew) {  // many rows: one wave per row
+    hipLaunchKernelGGL((lse_merge_wave_kernel<T, D, 16, false>), dim3((rows + 3) / 4), dim3(4 * kWave), 0, stream,
+                       static_cast<S16*>(a.out), nullptr, a.ws_off, a.context_lens, a.ws_ml, a.ws_acc, rows,
+                       a.num_seqs, a.num_heads, group, cap, a.max_items);
+    return hipGetLastError();
+  }
+  // few rows (long contexts: many partials per row): a workgroup per 32-element slice
+  hipLaunchKernelGGL((lse_merge_kernel<T, D, 32, 128>), dim3(rows * (D / 32)), dim3(128), 0, stream,
+                     static_cast<S16*>(a.out), a.ws_off, a.ws_ml, a.ws_acc, a.context_lens, a.num_seqs,
+                     a.num_heads, group, cap);
   return hipGetLastError();
 }
 
