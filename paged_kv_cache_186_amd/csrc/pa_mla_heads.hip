@@ -261,10 +261,13 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
           const int row = x / kMhChunks;
           const int chunk = x - row * kMhChunks;
           const bool ok = hg * kMhHeads + row < num_heads;
-          // a negative scale flips q's signs instead
-          r[i] = ok ? (load16(reinterpret_cast<const char*>(qg + static_cast<size_t>(row) * kMlaQkDim) + chunk * 16) ^
-                       q_sign)
-                    : u32x4{0u, 0u, 0u, 0u};
+          // every lane loads (a row past the last head reads the group's
+          // first row, which exists), so that the loads are issued together
+          // instead of one conditional round trip after another; a negative
+          // scale flips q's signs instead
+          const u32x4 v =
+              load16(reinterpret_cast<const char*>(qg + static_cast<size_t>(ok ? row : 0) * kMlaQkDim) + chunk * 16);
+          r[i] = ok ? (v ^ q_sign) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int i = 0; i < kMhLoads; ++i) {
