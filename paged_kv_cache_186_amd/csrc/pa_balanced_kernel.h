@@ -233,8 +233,9 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     float q_scale, int num_seqs, int num_heads, int num_kv_heads, int group, int num_blocks,
     int max_blocks) {
-  constexpr int R = Unit<KT, D, BS, GW>::kRows;
-  constexpr int kUnitsPerBlock = Unit<KT, D, BS, GW>::kPerBlock;
+  using U = Unit<KT, D, BS, GW>;
+  constexpr int R = U::kRows;
+  constexpr int kUnitsPerBlock = U::kPerBlock;
   using C = Tile<KT, D, R>;
   using St = BStage<QT, KT, D, BS, GW>;
   using QS = QSlice<QT, KT>;
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   // more state (grouped heads, or 16 elements per lane over an 8-bit cache);
   // the host's range bound assumes at most 2 units per block for it, 8 else
   constexpr int kCostRow = (GW > 1 || KT::kScaled) ? kBalancedCostRowWide : kBalancedCostRow;
-  static_assert(Unit<KT, D, BS, GW>::kPerBlock <= (kCostRow == kBalancedCostRow ? 8 : 2),
+  static_assert(U::kPerBlock <= (kCostRow == kBalancedCostRow ? 8 : 2),
                 "units per block within the host's cost bound");
   static_assert(NW * (kWave + 1) <= kBalancedMaxSeqs, "every wave's copy of the prefix sums fits");
   __shared__ int s_off[kBalancedMaxSeqs + 1];   // units of all sequences before s (per head)
@@ -270,7 +271,13 @@ __global__ __launch_bounds__(NW* kWave, GW > 1 ? 1 : (KT::kScaled ? 2 : 16 / NW)
   //    each array): no workgroup barrier between the lengths load and the
   //    first K/V loads.  Past that thread t owns sequences [t*kPer,
   //    (t+1)*kPer) and the workgroup shares one copy.
-  const bool wave_local = S <= kWaveLocalSeqs;
+  // (not for fp16 queries with four heads per load over an 8-bit cache:
+  // those instances use the whole register file, and the second prologue
+  // pushed 12 bytes per lane of the unit loop's values to scratch memory —
+  // continuous batching with 8 K/V heads over E4M3 46.4 -> 48.2 us; the bf16
+  // instances keep 24 bytes there either way and gain 0.8 us)
+  constexpr bool kWaveLocalOk = !(GW >= 4 && KT::kScaled && __is_same(QT, F16));
+  const bool wave_local = kWaveLocalOk && S <= kWaveLocalSeqs;
   const int sb = wave_local ? wave * (kWave + 1) : 0;
   int* const off_l = s_off + sb;
   int* const coff_l = s_coff + sb;
