@@ -378,12 +378,32 @@ __global__ __launch_bounds__(NW* kWave) void decode_kernel(
     __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One workgroup per CU when each streams much and there are many: with up
+// to four resident per CU the older one is served first and the rest trail;
+// reserving more than half the CU's LDS (dynamic LDS, unused) leaves room for
+// one.  Measured, one per CU against four: 512-token partitions of a 16-bit
+// D = 128 cache (256 KiB of K and V per workgroup) over 4 x 131072 tokens
+// 1507 -> 1317 us (1436 -> 1322 on another box), over 1 x 131072 367 -> 350
+// us; but with less per workgroup it loses — the same over an 8-bit cache 188
+// -> 247 us, 256-token partitions 370 -> 397 us, the layer shape with
+// 64-token partitions 27.8 -> 46.5 us — and so it does where most partitions
+// are empty (continuous batching, 512-token partitions of a 129-block table:
+// 142 -> 155 us).  Hence: at least kPartOneWgBytes of K and V per partition
+// and at least kPartOneWgMinParts partitions per row.
+constexpr size_t kPartOneWgBytes = 256 * 1024;
+constexpr int kPartOneWgMinParts = 32;
+constexpr size_t kPartOneWgLds = 96 * 1024;
+
 template <typename QT, typename KT, int D, int BS>
 hipError_t run_decode(const DecodeArgs& a, hipStream_t stream) {
   using S = typename QT::storage;
   const dim3 grid(a.num_heads, a.max_partitions, a.num_seqs);
+  // K and V bytes of one (head, partition)
+  const size_t part_bytes = static_cast<size_t>(a.partition_blocks) * BS * D * sizeof(typename KT::storage) * 2;
+  const size_t dyn_lds =
+      (a.max_partitions >= kPartOneWgMinParts && part_bytes >= kPartOneWgBytes) ? kPartOneWgLds : 0;
   hipLaunchKernelGGL((decode_kernel<QT, KT, D, BS, kWavesPerGroup, kTilesPerStage>), grid,
-                     dim3(kWavesPerGroup * kWave), 0, stream, static_cast<S*>(a.out), a.counters,
+                     dim3(kWavesPerGroup * kWave), dyn_lds, stream, static_cast<S*>(a.out), a.counters,
                      a.ws_ml, a.ws_acc, static_cast<const S*>(a.q),
                      static_cast<const char*>(a.k_pool), static_cast<const char*>(a.v_pool),
                      a.k_scales, a.v_scales, a.block_tables, a.context_lens, a.scale * kLog2e,
