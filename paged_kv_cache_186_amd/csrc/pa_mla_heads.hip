@@ -20,7 +20,19 @@
 // wave reads its operands; the workgroup's 64 query rows sit in LDS too (in
 // registers, beside the 128 accumulator registers of a wave's 16 x 512
 // outputs, they would not fit).  The next step's rows are in flight in
-// registers while a step is computed; one barrier per step.
+// registers while a step is computed; one barrier per step.  A step's 32 keys
+// lie in one table block (two of 16 tokens): their ids are read from LDS once
+// per step, not once per load (the per-load reads had put nine dependent LDS
+// round trips before the step's loads: 128 heads 138 -> 130 us).
+//
+// Up to 16 heads (SPLIT) there is one 16-row tile, and with one wave owning
+// it the other three only loaded rows: the step's arithmetic, on one wave
+// per CU, set the time.  There the four waves share the tile instead: wave w
+// scores the 32-element latent slices 4w .. 4w + 3 (and, for w < 2, rotary
+// slice 16 + w), the four partial score tiles are summed through LDS in wave
+// order (every wave then holds the same scores, softmax state and row sums),
+// and wave w accumulates values 128 w .. 128 w + 127 (16 heads, 32 sequences
+// of 1024..8192 tokens: 65 -> 54.5 us).
 //
 // Per step and wave (16 heads, 32 keys):
 //   S^T = K Q^T     18 v_mfma_f32_16x16x32 per 16-key block over the 576
@@ -52,14 +64,16 @@ namespace {
 
 typedef __attribute__((address_space(3))) s4_t lds_s4_t;
 
+// Waves per workgroup, one per SIMD.  (Up to 16 heads share one tile; eight
+// waves then, two per SIMD, were slower: every wave reads every other
+// wave's partial scores, 128 KiB of LDS per step against 32 KiB with four.)
 constexpr int kMhWaves = 4;
 constexpr int kMhHeads = kMlaHeadsGroup;             // heads per workgroup (16 per wave)
 constexpr int kMhRowB = kMlaQkDim * 2;               // bytes of one latent row
 constexpr int kMhLdsRow = kMhRowB + 16;              // padded LDS row stride
 constexpr int kMhStepKeys = 32;
 constexpr int kMhChunks = kMhRowB / 16;              // 16-byte chunks per row (72)
-constexpr int kMhLoads = kMhStepKeys * kMhChunks / (kMhWaves * kWave);  // per thread per step (9)
-static_assert(kMhLoads * kMhWaves * kWave == kMhStepKeys * kMhChunks, "whole rows per step");
+constexpr int kMhStepChunks = kMhStepKeys * kMhChunks;  // 16-byte chunks of one step's rows (2304)
 constexpr int kMhQK = kMlaQkDim / 32;                // S^T products per 16 keys (18)
 constexpr int kMhDt = kMlaVDim / 16;                 // 16-value tiles (32): rows of the P.V A operand
 constexpr int kMhMaxBlocks = kMlaHeadsMaxPart / 16;  // table entries of the longest item
@@ -67,15 +81,15 @@ constexpr int kMhMaxBlocks = kMlaHeadsMaxPart / 16;  // table entries of the lon
 // A lane's share of one head's 512 outputs: 4 consecutive values of each
 // 16-value tile (values 16 dt + 4 g4 + i in acc[dt][i]), scaled by inv,
 // rounded and stored 8 bytes a tile; row points at the lane's first value.
-template <typename T>
-__device__ __forceinline__ void store_row(typename T::storage* row, const f4_t (&acc)[kMlaVDim / 16], float inv) {
+template <typename T, int N>
+__device__ __forceinline__ void store_row(typename T::storage* row, const f4_t (&acc)[N], float inv) {
 #pragma unroll
-  for (int dt = 0; dt < kMlaVDim / 16; ++dt)
+  for (int dt = 0; dt < N; ++dt)
     *reinterpret_cast<u32x2*>(row + 16 * dt) = u32x2{Mfma<T>::pack2(acc[dt][0] * inv, acc[dt][1] * inv),
                                                      Mfma<T>::pack2(acc[dt][2] * inv, acc[dt][3] * inv)};
 }
 
-template <typename T, int BS>
+template <typename T, int BS, bool SPLIT>
 __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     typename T::storage* __restrict__ out, const typename T::storage* __restrict__ q,
     const char* __restrict__ kv_pool, const int32_t* __restrict__ block_tables,
@@ -86,18 +100,25 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
   using M = Mfma<T>;
   using PV = PvOps<T, 2>;
   using pw_t = typename PV::word_t;
-  constexpr int kThreads = kMhWaves * kWave;
+  constexpr int NW = kMhWaves;
+  constexpr int kThreads = NW * kWave;
+  constexpr int kMhLoads = (kMhStepChunks + kThreads - 1) / kThreads;  // per thread per step (9)
   constexpr int kPer = (kMlaHeadsMaxSeqs + kThreads - 1) / kThreads;
   constexpr int kCand = 8;  // partition sizes tried
   __shared__ int s_off[kMlaHeadsMaxSeqs + 1];
   __shared__ int s_len[kMlaHeadsMaxSeqs];
-  __shared__ int s_wsum[kCand][kMhWaves];
-  __shared__ int s_wtok[kMhWaves];
-  __shared__ int s_wpre[kMhWaves];
+  __shared__ int s_wsum[kCand][NW];
+  __shared__ int s_wtok[NW];
+  __shared__ int s_wpre[NW];
   __shared__ int s_tbl[kMhMaxBlocks];
-  // the workgroup's 64 query rows and two steps of latent rows (padded rows)
-  __shared__ __attribute__((aligned(16))) char s_q[kMhHeads * kMhLdsRow];
+  // the workgroup's query rows (64; SPLIT: 16) and two steps of latent rows
+  // (padded rows)
+  constexpr int kQRows = SPLIT ? 16 : kMhHeads;
+  __shared__ __attribute__((aligned(16))) char s_q[kQRows * kMhLdsRow];
   __shared__ __attribute__((aligned(16))) char s_rows[2][kMhStepKeys * kMhLdsRow];
+  // SPLIT: each wave's partial scores (its share of the 576 elements), lane l's
+  // four scores of key block kb at s_x[wave][kb][l]
+  __shared__ f4_t s_x[SPLIT ? NW : 1][2][SPLIT ? kWave : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -122,7 +143,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
   __syncthreads();
   long long tokens = 0;
 #pragma unroll
-  for (int w = 0; w < kMhWaves; ++w) tokens += s_wtok[w];
+  for (int w = 0; w < NW; ++w) tokens += s_wtok[w];
 
   // 2. the partition P, a multiple of the 32-key step: items (sequence,
   //    partition, head group) number NG * sum ceil(L / P); the smallest P
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
   for (int c = kCand - 1; c >= 0; --c) {
     long long tot = 0;
 #pragma unroll
-    for (int w = 0; w < kMhWaves; ++w) tot += s_wsum[c][w];
+    for (int w = 0; w < NW; ++w) tot += s_wsum[c][w];
     if (static_cast<long long>(NG) * tot <= slots) P = cand[c];
   }
   P = __builtin_amdgcn_readfirstlane(P);
@@ -186,7 +207,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
   int run = incl - mine;
   int total = 0;
 #pragma unroll
-  for (int w = 0; w < kMhWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     run += (w < wave) ? s_wpre[w] : 0;
     total += s_wpre[w];
   }
@@ -246,18 +267,22 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     // this wave's 16 heads; the workgroup's 64 query rows go to LDS (the B
     // operands of S^T are read from there every step: in registers they and
     // the O^T accumulators would not fit the register file)
-    const int h = hg * kMhHeads + wave * 16 + col;
+    // (SPLIT: every wave serves heads 0..15, each over its own 128 values)
+    const int h = SPLIT ? col : hg * kMhHeads + wave * 16 + col;
     const bool row_ok = h < num_heads;
-    const bool wave_rows = hg * kMhHeads + wave * 16 < num_heads;  // the wave has a head (uniform)
+    const bool wave_rows = SPLIT || hg * kMhHeads + wave * 16 < num_heads;  // the wave has a head (uniform)
     {
       const S16* qg = q + (static_cast<size_t>(s) * num_heads + hg * kMhHeads) * kMlaQkDim;
-      constexpr int kQLoads = kMhHeads * kMhChunks / kThreads;  // 18 per thread
+      constexpr int kQChunks = kQRows * kMhChunks;
+      constexpr int kQLoads = (kQChunks + kThreads - 1) / kThreads;  // 18 per thread (SPLIT: 5)
+      constexpr int kQBatch = SPLIT ? kQLoads : kMhLoads;             // issued together
+      static_assert(kQLoads % kQBatch == 0, "whole batches");
 #pragma unroll
-      for (int i0 = 0; i0 < kQLoads; i0 += kMhLoads) {
-        u32x4 r[kMhLoads];
+      for (int i0 = 0; i0 < kQLoads; i0 += kQBatch) {
+        u32x4 r[kQBatch];
 #pragma unroll
-        for (int i = 0; i < kMhLoads; ++i) {
-          const int x = tid + (i0 + i) * kThreads;
+        for (int i = 0; i < kQBatch; ++i) {
+          const int x = min(tid + (i0 + i) * kThreads, kQChunks - 1);
           const int row = x / kMhChunks;
           const int chunk = x - row * kMhChunks;
           const bool ok = hg * kMhHeads + row < num_heads;
@@ -270,40 +295,50 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
           r[i] = ok ? (v ^ q_sign) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int i = 0; i < kMhLoads; ++i) {
+        for (int i = 0; i < kQBatch; ++i) {
           const int x = tid + (i0 + i) * kThreads;
           const int row = x / kMhChunks;
           const int chunk = x - row * kMhChunks;
-          *reinterpret_cast<u32x4*>(&s_q[row * kMhLdsRow + chunk * 16]) = r[i];
+          if (x < kQChunks) *reinterpret_cast<u32x4*>(&s_q[row * kMhLdsRow + chunk * 16]) = r[i];
         }
       }
     }
+    // the wave's 16-value tiles: all 32, or (SPLIT) tiles 8 wave .. 8 wave + 7
+    constexpr int kDtW = SPLIT ? kMhDt / NW : kMhDt;
+    const int dt0 = SPLIT ? kDtW * wave : 0;
     float m = -INFINITY;
     f4_t lacc = {0.f, 0.f, 0.f, 0.f};
-    f4_t acc[kMhDt];
+    f4_t acc[kDtW];
 #pragma unroll
-    for (int dt = 0; dt < kMhDt; ++dt) acc[dt] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < kDtW; ++dt) acc[dt] = f4_t{0.f, 0.f, 0.f, 0.f};
     int bad = 0;
     __syncthreads();  // s_tbl and s_q written; the previous item's LDS rows no longer read
 
-    // cooperative load of one step's 32 rows: thread chunk x = tid + 256 i
+    // cooperative load of one step's 32 rows: thread chunk x = tid + kThreads i
     // covers row x / 72, 16-byte chunk x % 72; keys past the item's end read
     // the step's first row instead (their table entry may not exist; they
-    // are masked)
+    // are masked).  The step's keys lie in one block (two for 16-token
+    // blocks), whose ids are read once, uniformly, and selected per key.
     auto load_step = [&](u32x4 (&r)[kMhLoads], int step) __attribute__((always_inline)) {
       const int c0 = k_begin + step * kMhStepKeys;
+      const int b0 = c0 / BS - blk0;
+      int ph[2];
+      ph[0] = __builtin_amdgcn_readfirstlane(s_tbl[b0]);
+      ph[1] = (BS < kMhStepKeys && c0 + BS < k_end) ? __builtin_amdgcn_readfirstlane(s_tbl[b0 + 1]) : ph[0];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (static_cast<unsigned>(ph[j]) >= static_cast<unsigned>(num_blocks)) {
+          bad = 1;  // never dereference an id outside the pool
+          ph[j] = 0;
+        }
 #pragma unroll
       for (int i = 0; i < kMhLoads; ++i) {
-        const int x = tid + i * kThreads;
+        const int x = min(tid + i * kThreads, kMhStepChunks - 1);
         const int key = x / kMhChunks;
         const int chunk = x - key * kMhChunks;
-        const int k = (c0 + key < k_end) ? c0 + key : c0;
-        int phys = s_tbl[k / BS - blk0];
-        if (static_cast<unsigned>(phys) >= static_cast<unsigned>(num_blocks)) {
-          bad = 1;  // never dereference an id outside the pool
-          phys = 0;
-        }
-        r[i] = load16(kv_pool + (static_cast<size_t>(phys) * BS + k % BS) * kMhRowB + chunk * 16);
+        const int o = (c0 + key < k_end) ? key : 0;  // the key's offset from c0
+        const int phys = o >= BS ? ph[1] : ph[0];
+        r[i] = load16(kv_pool + (static_cast<size_t>(phys) * BS + (c0 + o) % BS) * kMhRowB + chunk * 16);
       }
     };
     auto store_step = [&](const u32x4 (&r)[kMhLoads], int buf) __attribute__((always_inline)) {
@@ -312,7 +347,8 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
         const int x = tid + i * kThreads;
         const int key = x / kMhChunks;
         const int chunk = x - key * kMhChunks;
-        *reinterpret_cast<u32x4*>(&s_rows[buf][key * kMhLdsRow + chunk * 16]) = r[i];
+        if (kMhStepChunks % kThreads == 0 || x < kMhStepChunks)
+          *reinterpret_cast<u32x4*>(&s_rows[buf][key * kMhLdsRow + chunk * 16]) = r[i];
       }
     };
 
@@ -328,6 +364,39 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
       // next chunk's loads issued before this chunk's products (scheduling
       // barriers keep the compiler from hoisting every load at once)
       f4_t sc[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
+      if constexpr (SPLIT) {
+        // this wave's share of the 576 elements: latent slices kL w ..
+        // kL w + kL - 1 and, for waves 0 and 1, rotary slice 16 + w; the NW
+        // partial score tiles are summed through LDS in wave order, so that
+        // every wave holds the same scores (and the same softmax state)
+        constexpr int kL = 16 / NW;  // latent 32-element slices per wave
+        const char* qrow = s_q + col * kMhLdsRow + 16 * g4;
+        const char* krow = rows + col * kMhLdsRow + 16 * g4;
+        u32x4 kd[kL + 1][2], qd[kL + 1];
+#pragma unroll
+        for (int j = 0; j <= kL; ++j) {
+          const int off = 64 * (j < kL ? kL * wave + j : 16 + (wave & 1));
+          qd[j] = *reinterpret_cast<const u32x4*>(qrow + off);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) kd[j][kb] = *reinterpret_cast<const u32x4*>(krow + 16 * kb * kMhLdsRow + off);
+        }
+#pragma unroll
+        for (int j = 0; j < kL; ++j)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) sc[kb] = M::qk(kd[j][kb], qd[j], sc[kb]);
+        if (wave < 2)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) sc[kb] = M::qk(kd[kL][kb], qd[kL], sc[kb]);
+        s_x[wave][0][lane] = sc[0];
+        s_x[wave][1][lane] = sc[1];
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          sc[kb] = s_x[0][kb][lane];
+#pragma unroll
+          for (int w = 1; w < NW; ++w) sc[kb] += s_x[w][kb][lane];
+        }
+      } else {
       constexpr int kQc = 2;
       constexpr int kChunksQ = kMhQK / kQc;
       u32x4 kbuf[2][2][kQc], qbuf[2][kQc];
@@ -353,6 +422,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
           for (int kb = 0; kb < 2; ++kb) sc[kb] = M::qk(kbuf[ch & 1][kb][j], qbuf[ch & 1][j], sc[kb]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      }
       const bool masked = c0 + kMhStepKeys > k_end;
       float z[2][4];
 #pragma unroll
@@ -369,7 +439,7 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
         const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
         lacc *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < kMhDt; ++dt) acc[dt] *= alpha;
+        for (int dt = 0; dt < kDtW; ++dt) acc[dt] *= alpha;
         m = mn;
       }
       const float nm = -m;
@@ -397,10 +467,10 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
         dst = u32x4{lo.x, lo.y, hi.x, hi.y};
       };
       u32x4 vbuf[2];
-      load_vt(0, vbuf[0]);
+      load_vt(dt0, vbuf[0]);
 #pragma unroll
-      for (int dt = 0; dt < kMhDt; ++dt) {
-        if (dt + 1 < kMhDt) load_vt(dt + 1, vbuf[(dt + 1) & 1]);
+      for (int dt = 0; dt < kDtW; ++dt) {
+        if (dt + 1 < kDtW) load_vt(dt0 + dt + 1, vbuf[(dt + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
         acc[dt] = PV::mma(vbuf[dt & 1], pw, acc[dt]);
         __builtin_amdgcn_sched_barrier(0);
@@ -435,16 +505,16 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
     const int any_bad = __syncthreads_or(bad);
     float lrow = lacc[0];  // the row sum (every element of the ones product holds it)
     if (any_bad) lrow = __builtin_nanf("");
-    S16* orow = out_b + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 4 * g4;
+    S16* orow = out_b + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 16 * dt0 + 4 * g4;
     if (parts == 1) {
       if (row_ok) store_row<T>(orow, acc, 1.f / lrow);
       continue;
     }
     // a split row: the item's partial, normalised and rounded to the output
     // type, and its (max, sum) in fp32, for mla_merge_kernel
-    const size_t slot = static_cast<size_t>(item) * kMhHeads + wave * 16 + col;
-    store_row<T>(part_b + slot * kMlaVDim + 4 * g4, acc, 1.f / lrow);
-    if (g4 == 0) *reinterpret_cast<f32x2*>(ml_b + slot * 2) = f32x2{m, lrow};
+    const size_t slot = static_cast<size_t>(item) * kMhHeads + (SPLIT ? 0 : wave * 16) + col;
+    store_row<T>(part_b + slot * kMlaVDim + 16 * dt0 + 4 * g4, acc, 1.f / lrow);
+    if (g4 == 0 && (!SPLIT || wave == 0)) *reinterpret_cast<f32x2*>(ml_b + slot * 2) = f32x2{m, lrow};
   }
 }
 
@@ -512,10 +582,10 @@ __global__ __launch_bounds__(kWave) void mla_merge_kernel(typename T::storage* _
   store16(out + (static_cast<size_t>(s) * num_heads + h) * kMlaVDim + 8 * lane, u32x4{w[0], w[1], w[2], w[3]});
 }
 
-template <typename T, int BS>
+template <typename T, int BS, bool SPLIT>
 hipError_t run_mla_heads(const PrefillArgs& a, hipStream_t stream) {
   using S16 = typename T::storage;
-  hipLaunchKernelGGL((mla_heads_kernel<T, BS>), dim3(a.workgroups), dim3(kMhWaves * kWave), 0, stream,
+  hipLaunchKernelGGL((mla_heads_kernel<T, BS, SPLIT>), dim3(a.workgroups), dim3(kMhWaves * kWave), 0, stream,
                      static_cast<S16*>(a.out), static_cast<const S16*>(a.q), static_cast<const char*>(a.k_pool),
                      a.block_tables, a.context_lens, a.ws_off, a.ws_ml, reinterpret_cast<S16*>(a.ws_acc),
                      fabsf(a.scale) * kLog2e, a.scale < 0.f ? 0x80008000u : 0u, a.num_seqs, a.num_heads,
@@ -528,9 +598,15 @@ hipError_t run_mla_heads(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename T, bool SPLIT>
+hipError_t run_mla_heads_bs(const PrefillArgs& a, hipStream_t stream) {
+  return a.block_size == 16 ? run_mla_heads<T, 16, SPLIT>(a, stream) : run_mla_heads<T, 32, SPLIT>(a, stream);
+}
+
+// up to 16 heads: one 16-row tile, shared by the four waves (SPLIT)
 template <typename T>
 hipError_t run_mla_heads_t(const PrefillArgs& a, hipStream_t stream) {
-  return a.block_size == 16 ? run_mla_heads<T, 16>(a, stream) : run_mla_heads<T, 32>(a, stream);
+  return a.num_heads <= 16 ? run_mla_heads_bs<T, true>(a, stream) : run_mla_heads_bs<T, false>(a, stream);
 }
 
 }  // namespace

@@ -178,3 +178,59 @@ def test_many_heads_512_sequences():
     lens[[3, 511]] = [6000, 4500]
     c = LatentCase(lens.tolist(), 64, 32, torch.float16, 214)
     assert_close(c.run(), c.oracle(), torch.float16, "512 sequences")
+
+
+# ---- up to 16 heads: one 16-row tile shared by the workgroup's four waves,
+#      each scoring a quarter of the 576 elements (partial scores summed
+#      through LDS) and accumulating its own 128 of the 512 values
+
+@pytest.mark.parametrize("H", [1, 5, 16])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_few_heads_shared_tile(H, bs, dtype):
+    """Contexts of one partition and of several (split rows merged by the
+    second kernel), empty and one-token contexts, NaN-poisoned unreferenced
+    blocks and tail slots; every value slice of every head compared."""
+    announce(f"mla few heads H={H} bs={bs} {dtype}")
+    c = LatentCase([0, 1, 700, 33, 9000, 16, 4100, 31], H, bs, dtype, 230 + H + bs)
+    out = c.run()
+    assert_close(out, c.oracle(), dtype, f"few heads H={H} bs={bs}")
+    assert not out[0].any()
+
+
+def test_few_heads_bench_shape():
+    """The latent-cache workload's shape: 32 sequences of 1024..8192 tokens,
+    16 heads, block 32, bf16; each row compared over all 512 values."""
+    announce("mla few heads 32 x [1024, 8192]")
+    rng = np.random.default_rng(240)
+    lens = rng.integers(1024, 8192, size=32, endpoint=True).tolist()
+    c = LatentCase(lens, 16, 32, torch.bfloat16, 240)
+    assert_close(c.run(), c.oracle(), torch.bfloat16, "32 sequences, 16 heads")
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_few_heads_negative_and_zero_scale(scale):
+    announce(f"mla few heads scale {scale}")
+    c = LatentCase([900, 5000], 16, 16, torch.float16, 241)
+    c.scale = scale
+    assert_close(c.run(), c.oracle(), torch.float16, f"few heads scale {scale}")
+
+
+def test_few_heads_out_of_pool_id():
+    announce("mla few heads bad id")
+    c = LatentCase([1000, 6000, 50], 16, 16, torch.bfloat16, 242)
+    bt = torch.from_numpy(c.tables).to(DEV)
+    bt[1, 100] = -3
+    out = c.run(tables=bt)
+    assert torch.isnan(out[1].float()).all()
+    ref = c.oracle()
+    assert_close(out[[0, 2]], ref[[0, 2]], torch.bfloat16, "other sequences")
+
+
+def test_few_heads_repeatable():
+    """The partial scores are summed in a fixed order: two calls agree bit for bit."""
+    announce("mla few heads repeatable")
+    c = LatentCase([3000, 700, 9000], 16, 16, torch.bfloat16, 243)
+    a = c.run()
+    b = c.run()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
