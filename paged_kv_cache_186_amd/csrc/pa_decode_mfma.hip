@@ -461,10 +461,14 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
-            p[kb][i] = (masked && z[kb][i] == -INFINITY) ? 0.f : x;
-          }
+          for (int i = 0; i < 4; ++i) p[kb][i] = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
+        if (masked) {  // a uniform branch: only steps at a limit hold masked keys
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (z[kb][i] == -INFINITY) p[kb][i] = 0.f;
+        }
         pw[t] = pw_t{M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3]), M::pack2(p[1][0], p[1][1]),
                      M::pack2(p[1][2], p[1][3])};
       }

@@ -423,13 +423,21 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
       }
+      // only an item's last step can hold keys past its end: the masking is
+      // a uniform branch, skipped by every other step
       const bool masked = c0 + kMhStepKeys > k_end;
       float z[2][4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          z[kb][i] = (!masked || c0 + 16 * kb + 4 * g4 + i < k_end) ? sc[kb][i] : -INFINITY;
+        for (int i = 0; i < 4; ++i) z[kb][i] = sc[kb][i];
+      if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (c0 + 16 * kb + 4 * g4 + i >= k_end) z[kb][i] = -INFINITY;
+      }
       float cm = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
                        fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
       cm = fold_max<16>(cm);
@@ -447,10 +455,14 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
-          p[kb][i] = (masked && z[kb][i] == -INFINITY) ? 0.f : x;
-        }
+        for (int i = 0; i < 4; ++i) p[kb][i] = fast_exp2(fmaf(z[kb][i], qk_scale, nm));
+      if (masked) {  // masked scores (-inf) weigh 0 (with a zero scale -inf * 0 would be a NaN)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (z[kb][i] == -INFINITY) p[kb][i] = 0.f;
+      }
       const pw_t pw = {M::pack2(p[0][0], p[0][1]), M::pack2(p[0][2], p[0][3]), M::pack2(p[1][0], p[1][1]),
                        M::pack2(p[1][2], p[1][3])};
       // V^T operand per 16-value tile dt by two transposing reads
