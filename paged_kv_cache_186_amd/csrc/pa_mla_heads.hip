@@ -331,14 +331,20 @@ __global__ __launch_bounds__(kMhWaves* kWave, 1) void mla_heads_kernel(
           bad = 1;  // never dereference an id outside the pool
           ph[j] = 0;
         }
+      // uniform block bases, a 32-bit offset per load (c0 is a multiple of
+      // both block sizes, so key o of the step is row o % BS of block o / BS)
+      const char* const base0 = kv_pool + static_cast<size_t>(ph[0]) * (BS * kMhRowB);
+      const char* const base1 = kv_pool + static_cast<size_t>(ph[1]) * (BS * kMhRowB);
+      const bool tail = c0 + kMhStepKeys > k_end;
 #pragma unroll
       for (int i = 0; i < kMhLoads; ++i) {
         const int x = min(tid + i * kThreads, kMhStepChunks - 1);
         const int key = x / kMhChunks;
         const int chunk = x - key * kMhChunks;
-        const int o = (c0 + key < k_end) ? key : 0;  // the key's offset from c0
-        const int phys = o >= BS ? ph[1] : ph[0];
-        r[i] = load16(kv_pool + (static_cast<size_t>(phys) * BS + (c0 + o) % BS) * kMhRowB + chunk * 16);
+        const int o = (!tail || c0 + key < k_end) ? key : 0;  // the key's offset from c0
+        const uint32_t off = static_cast<uint32_t>((o % BS) * kMhRowB + chunk * 16);
+        const char* const base = (BS >= kMhStepKeys || o < BS) ? base0 : base1;
+        r[i] = load16(base + off);
       }
     };
     auto store_step = [&](const u32x4 (&r)[kMhLoads], int buf) __attribute__((always_inline)) {
