@@ -585,7 +585,12 @@ QueriesPlan plan_queries(int32_t num_seqs, int32_t num_tokens, int32_t num_heads
     return p;
   }
   p.max_items = static_cast<int>(items);
-  p.workgroups = p.slots;
+  // one workgroup per item as far as the bound allows, as in decode: the
+  // hardware starts each on whichever CU frees first, where a grid of one
+  // workgroup per slot taking items by stride left the CUs that drew long
+  // items behind (verify with one token per sequence: main kernel 48.3 us
+  // against 43.5 us for the same rows through pa_decode_gqa)
+  p.workgroups = static_cast<int>(std::min<long long>(items, pa::kMfmaMaxWorkgroups));
   if (cap > pa::kMfmaMinPartTokens) {  // a row can span several partitions
     p.ws = pa::workspace_layout(0, static_cast<size_t>(items) * rows_per_item, head_dim);
     p.tok_offset = p.ws.total;
