@@ -174,8 +174,12 @@ constexpr int kMfmaMinPartTokens = 128;   // the smallest partition the kernel p
 #ifndef PA_GQ_MAX_PART
 #define PA_GQ_MAX_PART 2048
 #endif
+// Grid bound: the grid is one workgroup per item as far as this allows (the
+// hardware starts each on whichever CU frees first; past the bound the
+// workgroups take the remaining items by stride).  Continuous batching with
+// 8 K/V heads (~1040 items): 47.5 us with 1024, 46.9 with 2048 or 4096.
 #ifndef PA_GQ_MAX_WG
-#define PA_GQ_MAX_WG 1024
+#define PA_GQ_MAX_WG 2048
 #endif
 constexpr int kMfmaMaxPartTokens = PA_GQ_MAX_PART;  // the largest
 constexpr int kMfmaMaxWorkgroups = PA_GQ_MAX_WG;
