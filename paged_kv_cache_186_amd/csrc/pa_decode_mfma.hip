@@ -25,8 +25,9 @@
 // (adjacent waves read adjacent 8 KiB of K and V at once), each with its own
 // online softmax over NT tiles of 16 query rows; at the end of the item the
 // four states are merged through LDS.  An item that is its row's only
-// partition writes the output; otherwise it writes its (max, sum, weighted V
-// sum) per head to the workspace, and a second, small kernel merges each
+// partition writes the output; otherwise it writes per head its (max, sum)
+// in fp32 and its normalised output in the 16-bit type (the weighted V sum
+// over the sum) to the workspace, and a second, small kernel merges each
 // split row's partials (one workgroup per (sequence, query head)) — a
 // 131072-token context on one K/V head has hundreds of partials, far more
 // than one wave could merge at the end of the first kernel.
@@ -557,8 +558,13 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
         *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(qs0 + tok) * num_heads + h) * D + 4 * c4) =
             u32x2{w0, w1};
       } else {
+        // a split row's partial: o / l rounded to the 16-bit type (half the
+        // bytes of fp32 sums, written here and read by the merge) and its
+        // (max, sum) in fp32; an empty partial (l = 0) is zero
         const size_t slot = static_cast<size_t>(item) * (MQ ? kRows : G) + row;
-        *reinterpret_cast<f4_t*>(ws_acc + slot * D + 4 * c4) = o;
+        const float inv = (l == 0.f) ? 0.f : 1.f / l;
+        *reinterpret_cast<u32x2*>(reinterpret_cast<S16*>(ws_acc) + slot * D + 4 * c4) =
+            u32x2{M::pack2(o[0] * inv, o[1] * inv), M::pack2(o[2] * inv, o[3] * inv)};
         if (c4 == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{Mx, l};
       }
     }
@@ -573,7 +579,9 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
 // tokens, item offset, partitions, chunks, partition size, whether a
 // sequence covers it) places row r = i * group + h % group of K/V head
 // h / group in chunk r / RPI of the sequence's items, at slot
-// item * RPI + r % RPI of each.  Lane l holds elements 4 * (l % kC) .. + 3 of
+// item * RPI + r % RPI of each.  A partial is o_p = acc_p / l_p in the
+// 16-bit type with (m_p, l_p) in fp32, weighing l_p 2^(m_p - M).  Lane l
+// holds elements 4 * (l % kC) .. + 3 of
 // the partials l / kC, l / kC + kG, ..., kU of them in flight per round,
 // folded into a running (max, sum, sums) with the online rescaling; the kG
 // lane groups are then folded by cross-lane reads.  Slots past max_items are
@@ -628,7 +636,12 @@ __global__ __launch_bounds__(256) void lse_merge_wave_kernel(
     for (int u = 0; u < kU; ++u) {
       const size_t slot = (item0 + min(p0 + u * kG + gl, parts - 1)) * stride + g;
       ml[u] = *reinterpret_cast<const f32x2*>(ws_ml + slot * 2);
-      v[u] = *reinterpret_cast<const f4_t*>(ws_acc + slot * D + 4 * c);
+      const u32x2 w = *reinterpret_cast<const u32x2*>(
+          reinterpret_cast<const typename T::storage*>(ws_acc) + slot * D + 4 * c);
+      float f[4];
+      T::unpack_word(w.x, f);
+      T::unpack_word(w.y, f + 2);
+      v[u] = f4_t{f[0], f[1], f[2], f[3]};
     }
     float bm = -INFINITY;
 #pragma unroll
@@ -642,9 +655,10 @@ __global__ __launch_bounds__(256) void lse_merge_wave_kernel(
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const float mu = ml[u][0];
-      const float wgt = (p0 + u * kG + gl < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f;
-      den = fmaf(wgt, ml[u][1], den);
-      num += wgt * v[u];
+      // partial p holds o_p = acc_p / l_p: it weighs l_p 2^(m_p - M)
+      const float wl = ((p0 + u * kG + gl < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f) * ml[u][1];
+      den += wl;
+      num += wl * v[u];
     }
     Mx = mn;
   }

@@ -110,8 +110,10 @@ struct PvOps<BF16, 2> {
 // sequence s in partition p sits in slot (off[s] + (h / group) * parts + p)
 // * group + h % group, where off[] (S + 1 item offsets) and the partition
 // size P (off[S + 1]) are what the first kernel wrote.  A row of one
-// partition was written by the first kernel: nothing to do.  kC = SLICE / 4
-// lanes cover one partial's slice (4 sums each) and the kG lane groups take
+// partition was written by the first kernel: nothing to do.  A partial is
+// o_p = acc_p / l_p in the 16-bit type (D elements per slot) with (m_p, l_p)
+// in fp32, and weighs l_p 2^(m_p - M).  kC = SLICE / 4
+// lanes cover one partial's slice (4 values each) and the kG lane groups take
 // every kG-th partial, kU per round with all their loads issued at once;
 // each round is folded into a running (max, sum, sums) with the online
 // rescaling, and the groups are combined through LDS.
@@ -151,7 +153,12 @@ __global__ __launch_bounds__(THREADS) void lse_merge_kernel(
     for (int u = 0; u < kU; ++u) {
       const size_t slot = (item0 + min(p0 + u * kG, parts - 1)) * group + g;
       ml[u] = *reinterpret_cast<const f32x2*>(ws_ml + slot * 2);
-      v[u] = *reinterpret_cast<const f4_t*>(ws_acc + slot * D + e0);
+      const u32x2 w = *reinterpret_cast<const u32x2*>(
+          reinterpret_cast<const typename T::storage*>(ws_acc) + slot * D + e0);
+      float f[4];
+      T::unpack_word(w.x, f);
+      T::unpack_word(w.y, f + 2);
+      v[u] = f4_t{f[0], f[1], f[2], f[3]};
     }
     float bm = -INFINITY;
 #pragma unroll
@@ -165,9 +172,10 @@ __global__ __launch_bounds__(THREADS) void lse_merge_kernel(
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const float mu = ml[u][0];
-      const float wgt = (p0 + u * kG < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f;
-      den = fmaf(wgt, ml[u][1], den);
-      num += wgt * v[u];
+      // partial p holds o_p = acc_p / l_p: it weighs l_p 2^(m_p - M)
+      const float wl = ((p0 + u * kG < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f) * ml[u][1];
+      den += wl;
+      num += wl * v[u];
     }
     Mx = mn;
   }
