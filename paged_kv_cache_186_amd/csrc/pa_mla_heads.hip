@@ -32,9 +32,12 @@
 // slice 16 + w), the four partial score tiles are summed through LDS in wave
 // order (every wave then holds the same scores, softmax state and row sums),
 // and wave w accumulates values 128 w .. 128 w + 127 (16 heads, 32 sequences
-// of 1024..8192 tokens: 65 -> 54.5 us).
+// of 1024..8192 tokens: 65 -> 54.5 us; 51 us with the masking of an item's
+// last step under a uniform branch and the row loads addressed from the
+// step's uniform block base).  Per step and wave that is 5 (4) score slices
+// x 2 key blocks and 8 P.V tiles instead of 18 x 2 and 32.
 //
-// Per step and wave (16 heads, 32 keys):
+// Per step and wave (16 heads, 32 keys; without SPLIT):
 //   S^T = K Q^T     18 v_mfma_f32_16x16x32 per 16-key block over the 576
 //                   elements (A = 16 keys x 32 elements, B = the wave's 16
 //                   query rows, both from LDS);
