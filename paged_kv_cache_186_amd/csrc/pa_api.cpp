@@ -59,6 +59,7 @@ struct DecodePlan {
   size_t slots;  // partial slots (each of head_dim fp32 sums and a (max, sum) pair)
   int max_items;     // kMfma: items the workspace holds
   int mfma_slots;    // kMfma: workgroups resident at once
+  int mfma_fuse;     // kMfma: split rows merged in the kernel
   size_t off_offset; // kMfma: byte offset of the item offsets in the workspace
   pa::WorkspaceLayout ws;
 };
@@ -110,7 +111,7 @@ int group_width(int num_heads, int num_kv_heads, pa_dtype_t dtype, pa_dtype_t kv
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                        int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                        int32_t partition_size, pa_dtype_t dtype, pa_dtype_t kv_dtype) {
-  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, 1, 0, 0, 0, 0, 0, {0, 0, 0, 0}};
+  DecodePlan p{PA_OK, pa::DecodeMode::kPartitioned, 0, 0, 0, 1, 0, 0, 0, 0, 0, 0, {0, 0, 0, 0}};
   if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0 || num_kv_heads <= 0 ||
       num_heads % num_kv_heads != 0) {
     p.status = PA_ERR_INVALID_ARG;
@@ -150,6 +151,10 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     p.workgroups = static_cast<int>(grid < 1 ? 1 : (grid > pa::kMfmaMaxWorkgroups ? pa::kMfmaMaxWorkgroups : grid));
     p.rows = rows;
     if (ctx > pa::kMfmaMinPartTokens) {  // a row can span several partitions
+      p.mfma_fuse = (ctx <= pa::kMfmaFuseMaxTokens &&
+                     static_cast<long long>(num_seqs) * num_kv_heads * pa::kMfmaFuseRowsPerSlot <= p.mfma_slots)
+                        ? 1
+                        : 0;
       p.slots = static_cast<size_t>(items) * group;
       p.ws = pa::workspace_layout(rows, p.slots, head_dim);
       p.off_offset = p.ws.total;
@@ -325,6 +330,7 @@ pa_status_t decode_impl(void* out, const void* q, const void* k_pool, const void
   a.workgroups = plan.workgroups;
   a.max_items = plan.max_items;
   a.mfma_slots = plan.mfma_slots;
+  a.mfma_fuse = plan.mfma_fuse;
   if (layout.total > 0) {
     char* ws = static_cast<char*>(workspace);
     a.counters = reinterpret_cast<uint32_t*>(ws + layout.counter_offset);

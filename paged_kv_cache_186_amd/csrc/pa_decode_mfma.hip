@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
     const int32_t* __restrict__ context_lens, int* __restrict__ ws_off, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, float qk_scale, uint32_t q_sign_bits, int num_seqs, int num_heads,
     int num_kv_heads, int group, int num_blocks, int max_blocks, int max_items, int slots,
-    const int32_t* __restrict__ query_start, int num_tokens, int* __restrict__ ws_tok) {
+    const int32_t* __restrict__ query_start, int num_tokens, int* __restrict__ ws_tok,
+    uint32_t* __restrict__ counters) {
   static_assert(D % 64 == 0 && BS % 16 == 0, "MFMA slices");
   using S16 = typename T::storage;
   using M = Mfma<T>;
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
   __shared__ float s_m[kGqWaves][NT][16];
   __shared__ float s_l[kGqWaves][NT][16];
   __shared__ int s_bad[kGqWaves];
+  __shared__ uint32_t s_ticket;
   __shared__ f4_t s_o[kGqWaves][NT][16][D / 4];
 
   const int tid = threadIdx.x;
@@ -563,9 +565,75 @@ __global__ __launch_bounds__(kGqWaves* kWave, NT == 1 ? 2 : 1) void decode_mfma_
         // (max, sum) in fp32; an empty partial (l = 0) is zero
         const size_t slot = static_cast<size_t>(item) * (MQ ? kRows : G) + row;
         const float inv = (l == 0.f) ? 0.f : 1.f / l;
-        *reinterpret_cast<u32x2*>(reinterpret_cast<S16*>(ws_acc) + slot * D + 4 * c4) =
-            u32x2{M::pack2(o[0] * inv, o[1] * inv), M::pack2(o[2] * inv, o[3] * inv)};
-        if (c4 == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{Mx, l};
+        const u32x2 w = {M::pack2(o[0] * inv, o[1] * inv), M::pack2(o[2] * inv, o[3] * inv)};
+        S16* const po = reinterpret_cast<S16*>(ws_acc) + slot * D + 4 * c4;
+        if (!MQ && counters != nullptr) {  // merged in this kernel: stores other XCDs will read
+          // (the 64-bit value built from the two words, not passed as floats)
+          const uint64_t wv = static_cast<uint64_t>(w.x) | (static_cast<uint64_t>(w.y) << 32);
+          __hip_atomic_store(reinterpret_cast<uint64_t*>(po), wv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (c4 == 0) store_coherent_u64(ws_ml + slot * 2, Mx, l);
+        } else {
+          *reinterpret_cast<u32x2*>(po) = w;
+          if (c4 == 0) *reinterpret_cast<f32x2*>(ws_ml + slot * 2) = f32x2{Mx, l};
+        }
+      }
+    }
+    if constexpr (!MQ) {
+      if (counters != nullptr && parts > 1) {
+        // the split rows of (sequence, K/V head) merged by the item that
+        // arrives last: every thread's partial stores performed, then one
+        // ticket per item; the last ticket's workgroup folds the `parts`
+        // partials of each of the G heads in partition order (o_p weighs
+        // l_p 2^(m_p - M)) and clears the counter for the next call.  No
+        // workgroup waits for another.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        uint32_t* const ctr = counters + static_cast<size_t>(s) * HKV + kvh;
+        if (tid == 0) s_ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (s_ticket == static_cast<uint32_t>(parts - 1)) {
+          constexpr int kU = 8;  // partials in flight per thread
+          const size_t item0 = static_cast<size_t>(item - part);
+          for (int x = tid; x < G * (D / 4); x += kThreads) {
+            const int g = x / (D / 4);
+            const int c4 = x - g * (D / 4);
+            float Mx = -INFINITY, den = 0.f;
+            f4_t num = {0.f, 0.f, 0.f, 0.f};
+            for (int p0 = 0; p0 < parts; p0 += kU) {
+              uint64_t mlv[kU], ov[kU];
+#pragma unroll
+              for (int u = 0; u < kU; ++u) {
+                const size_t slot = (item0 + min(p0 + u, parts - 1)) * G + g;
+                mlv[u] = load_coherent_u64(ws_ml + slot * 2);
+                ov[u] = load_coherent_u64(reinterpret_cast<const float*>(reinterpret_cast<const S16*>(ws_acc) + slot * D + 4 * c4));
+              }
+              float bm = -INFINITY;
+#pragma unroll
+              for (int u = 0; u < kU; ++u)
+                if (p0 + u < parts) bm = fmaxf(bm, lo_float(mlv[u]));
+              const float mn = fmaxf(Mx, bm);
+              if (mn == -INFINITY) continue;  // only empty partials so far
+              const float a = (Mx == -INFINITY) ? 0.f : fast_exp2(Mx - mn);
+              den *= a;
+              num *= a;
+#pragma unroll
+              for (int u = 0; u < kU; ++u) {
+                const float mu = lo_float(mlv[u]);
+                const float wl = ((p0 + u < parts && mu != -INFINITY) ? fast_exp2(mu - mn) : 0.f) * hi_float(mlv[u]);
+                float f[4];
+                T::unpack_word(static_cast<uint32_t>(ov[u]), f);
+                T::unpack_word(static_cast<uint32_t>(ov[u] >> 32), f + 2);
+                den += wl;
+                num += wl * f4_t{f[0], f[1], f[2], f[3]};
+              }
+              Mx = mn;
+            }
+            const float inv = 1.f / den;
+            *reinterpret_cast<u32x2*>(out + (static_cast<size_t>(s) * num_heads + static_cast<size_t>(kvh) * G + g) * D +
+                                      4 * c4) = u32x2{M::pack2(num[0] * inv, num[1] * inv), M::pack2(num[2] * inv, num[3] * inv)};
+          }
+          if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     __syncthreads();  // the LDS state is rewritten by the next item
@@ -684,9 +752,10 @@ hipError_t run_mfma(const DecodeArgs& a, hipStream_t stream) {
                      static_cast<const char*>(a.v_pool), a.block_tables, a.context_lens, a.ws_off, a.ws_ml,
                      a.ws_acc, fabsf(a.scale) * kLog2e, a.scale < 0.f ? 0x80008000u : 0u, a.num_seqs,
                      a.num_heads, a.num_kv_heads, a.num_heads / a.num_kv_heads, a.num_blocks,
-                     a.max_blocks_per_seq, a.max_items, a.mfma_slots, a.query_start, a.num_tokens, a.ws_tok);
+                     a.max_blocks_per_seq, a.max_items, a.mfma_slots, a.query_start, a.num_tokens, a.ws_tok,
+                     (!MQ && a.mfma_fuse) ? a.counters : nullptr);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.ws_ml == nullptr) return e;
+  if (e != hipSuccess || a.ws_ml == nullptr || (!MQ && a.mfma_fuse)) return e;
   const int group = a.num_heads / a.num_kv_heads;
   if constexpr (MQ) {  // (query token, head) rows, four per workgroup
     const int rows = a.num_tokens * a.num_heads;

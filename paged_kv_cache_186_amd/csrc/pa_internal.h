@@ -74,6 +74,7 @@ struct DecodeArgs {
   int* ws_off;           // kMfma: [S + 2] item offsets and the partition size, for the merge
   int max_items;         // kMfma: items the workspace holds (slots = max_items * group)
   int mfma_slots;        // kMfma: workgroups resident on the whole GPU at once
+  int mfma_fuse;         // kMfma: split rows merged in the kernel (no merge kernel)
   // several query tokens per sequence (pa_prefill through the grouped-query
   // kernel): query_start [S + 1], num_tokens, and the per-token merge
   // descriptors [num_tokens][8]; null / 0 for decode
@@ -186,6 +187,18 @@ constexpr int kMfmaMaxWorkgroups = PA_GQ_MAX_WG;
 // Workgroups of the kernel resident on one CU: two with one 16-row tile
 // (groups of up to 16 heads), one with two (register file).
 inline int mfma_wg_per_cu(int group) { return group > 16 ? 1 : 2; }
+// Small batches whose contexts are at most this many tokens (the table
+// width; at most 64 partitions a row) and whose (sequence, K/V head) rows
+// number at most one per kMfmaFuseRowsPerSlot resident workgroups: split
+// rows are merged inside the kernel by the item that arrives last, and the
+// second kernel (whose launch costs a few microseconds whatever it does) is
+// not launched.  Longer contexts can have hundreds of partials per row, more
+// than one workgroup folds quickly; larger batches run several items per
+// workgroup, each then waiting for its stores and its ticket (layer shape
+// with 8 K/V heads 12.6 -> 12.1 us, but continuous batching with 8 / 4
+// 46.6 / 32.0 -> 48.9 / 32.5 us when fused).
+constexpr int kMfmaFuseMaxTokens = 64 * kMfmaMinPartTokens;
+constexpr int kMfmaFuseRowsPerSlot = 8;
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // the same kernel over several query tokens per sequence (pa_prefill with at
 // most kMfmaQueriesMaxSeqs sequences and few rows each): rows (query token, head of the

@@ -159,3 +159,47 @@ def test_long_context_every_head(Hkv):
     print(f"long context 32 query / {Hkv} K/V heads: max abs err {err:.2e}")
     del w
     torch.cuda.empty_cache()
+
+
+# ---- split rows merged inside the kernel (contexts of at most 8192 tokens,
+#      the table width deciding): the item that arrives last folds its
+#      (sequence, K/V head)'s partials and clears the arrival counter
+
+@pytest.mark.parametrize("H,Hkv,bs", [(32, 8, 16), (32, 4, 32), (48, 3, 16)])
+def test_in_kernel_merge_at_most_partitions(H, Hkv, bs):
+    """One 8192-token context beside seven one-token ones: 128-token
+    partitions, so the long rows have 64 partials (the most the in-kernel
+    merge takes, eight rounds of loads); every head compared, and a second
+    call bit-identical (the counters were left at zero)."""
+    announce(f"gqa mfma in-kernel merge 64 partitions H={H} Hkv={Hkv} bs={bs}")
+    w = _workload([8192] + [1] * 7, H, Hkv, 128, bs, torch.float16, 300 + H + bs)
+    assert w.table_width * bs <= 8192
+    out = _run(w)
+    assert_close(out, _oracle(w), torch.float16, f"in-kernel merge H={H} Hkv={Hkv}")
+    assert torch.equal(bits(_run(w)), bits(out)), "second call differs"
+
+
+def test_merge_kernel_just_past_the_limit():
+    """A table one block wider than 8192 tokens: the split rows go to the
+    merge kernel instead; the same contexts give the same result (to the
+    fp16 tolerance) either way."""
+    announce("gqa mfma merge kernel past 8192 tokens")
+    lens = [8192 + 16, 700, 3, 2500, 0, 1]
+    w = _workload(lens, 32, 8, 128, 16, torch.float16, 311)
+    assert w.table_width * 16 > 8192
+    assert_close(_run(w), _oracle(w), torch.float16, "merge kernel")
+
+
+def test_in_kernel_merge_alternating_with_other_calls():
+    """Calls that merge in the kernel, calls that take the merge kernel and
+    balanced-split calls (2 query heads per K/V head) on one cached workspace
+    in turn: each matches the oracle (no call sees another's counters)."""
+    announce("gqa mfma in-kernel merge alternating")
+    a = _workload([3000, 5, 7000, 900], 32, 8, 128, 16, torch.float16, 320)
+    b = _workload([9000, 40, 300], 32, 8, 128, 16, torch.float16, 321)
+    c = _workload([3000, 5, 7000, 900], 32, 16, 128, 16, torch.float16, 322)
+    ra, rb, rc = _oracle(a), _oracle(b), _oracle(c)
+    for _ in range(2):
+        assert_close(_run(a), ra, torch.float16, "in-kernel merge")
+        assert_close(_run(b), rb, torch.float16, "merge kernel")
+        assert_close(_run(c), rc, torch.float16, "balanced split")
