@@ -151,7 +151,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
     p.workgroups = static_cast<int>(grid < 1 ? 1 : (grid > pa::kMfmaMaxWorkgroups ? pa::kMfmaMaxWorkgroups : grid));
     p.rows = rows;
     if (ctx > pa::kMfmaMinPartTokens) {  // a row can span several partitions
-      p.mfma_fuse = (ctx <= pa::kMfmaFuseMaxTokens &&
+      p.mfma_fuse = (ctx <= pa::kMfmaFuseMaxTokens && group <= pa::kMfmaFuseMaxGroup &&
                      static_cast<long long>(num_seqs) * num_kv_heads * pa::kMfmaFuseRowsPerSlot <= p.mfma_slots)
                         ? 1
                         : 0;

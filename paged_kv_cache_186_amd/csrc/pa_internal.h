@@ -196,9 +196,13 @@ inline int mfma_wg_per_cu(int group) { return group > 16 ? 1 : 2; }
 // than one workgroup folds quickly; larger batches run several items per
 // workgroup, each then waiting for its stores and its ticket (layer shape
 // with 8 K/V heads 12.6 -> 12.1 us, but continuous batching with 8 / 4
-// 46.6 / 32.0 -> 48.9 / 32.5 us when fused).
+// 46.6 / 32.0 -> 48.9 / 32.5 us when fused); and groups of at most 4 heads:
+// one workgroup folds G heads' partials serially, so larger groups lengthen
+// the last item more than the second kernel costs (layer shape with 4 / 1
+// K/V heads, groups of 8 / 32: 10.1 / 12.6 -> 10.6 / 18.4 us when fused).
 constexpr int kMfmaFuseMaxTokens = 64 * kMfmaMinPartTokens;
 constexpr int kMfmaFuseRowsPerSlot = 8;
+constexpr int kMfmaFuseMaxGroup = 4;
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // the same kernel over several query tokens per sequence (pa_prefill with at
 // most kMfmaQueriesMaxSeqs sequences and few rows each): rows (query token, head of the

@@ -161,11 +161,12 @@ def test_long_context_every_head(Hkv):
     torch.cuda.empty_cache()
 
 
-# ---- split rows merged inside the kernel (contexts of at most 8192 tokens,
-#      the table width deciding): the item that arrives last folds its
-#      (sequence, K/V head)'s partials and clears the arrival counter
+# ---- split rows merged inside the kernel (groups of at most 4 heads, small
+#      batches, contexts of at most 8192 tokens, the table width deciding):
+#      the item that arrives last folds its (sequence, K/V head)'s partials
+#      and clears the arrival counter
 
-@pytest.mark.parametrize("H,Hkv,bs", [(32, 8, 16), (32, 4, 32), (48, 3, 16)])
+@pytest.mark.parametrize("H,Hkv,bs", [(32, 8, 16), (16, 4, 32), (12, 4, 16)])
 def test_in_kernel_merge_at_most_partitions(H, Hkv, bs):
     """One 8192-token context beside seven one-token ones: 128-token
     partitions, so the long rows have 64 partials (the most the in-kernel
