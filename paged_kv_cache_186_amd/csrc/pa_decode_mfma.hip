@@ -27,10 +27,13 @@
 // four states are merged through LDS.  An item that is its row's only
 // partition writes the output; otherwise it writes per head its (max, sum)
 // in fp32 and its normalised output in the 16-bit type (the weighted V sum
-// over the sum) to the workspace, and a second, small kernel merges each
-// split row's partials (one workgroup per (sequence, query head)) — a
-// 131072-token context on one K/V head has hundreds of partials, far more
-// than one wave could merge at the end of the first kernel.
+// over the sum) to the workspace.  Small batches with groups of at most 4
+// heads and contexts of at most 8192 tokens merge them in this kernel: the
+// item of a (sequence, K/V head) that arrives last (a ticket from the row's
+// arrival counter) folds the row's partials.  Otherwise a second, small
+// kernel merges each split row's partials — a 131072-token context on one
+// K/V head has hundreds of partials, far more than one workgroup could
+// merge at the end of the first kernel.
 //
 // One 32-key step of one wave (two 16-key blocks), per tile of 16 query rows:
 //   S^T = K Q^T    v_mfma_f32_16x16x32_{f16,bf16}, D/32 products per block:
